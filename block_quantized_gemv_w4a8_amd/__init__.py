@@ -1,0 +1,172 @@
+"""Python binding of libqgemv (W4A8 block-quantized GEMV for AMD MI355X / gfx950).
+
+Argument marshalling only: every function here has the name of a C-ABI entry
+point in ``include/qgemv.h``, takes torch device tensors (or raw integer
+device addresses) for its pointer arguments, passes them with the current
+torch stream (unless ``stream`` is given) to the library, and raises
+:class:`QgemvError` when the library returns a non-OK status.  All arithmetic
+happens in the library's HIP kernels.  Importing this package fails loudly if
+the library has not been built (``python -m block_quantized_gemv_w4a8_amd.build``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "_lib", "libqgemv.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"libqgemv.so is not built ({LIB_PATH}); run "
+        "`python -m block_quantized_gemv_w4a8_amd.build` (hipcc, gfx950)")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+QGEMV_OK = 0
+QGEMV_E_NULL = 1
+QGEMV_E_SHAPE = 2
+QGEMV_E_UNSUPPORTED = 3
+QGEMV_E_ALIGN = 4
+QGEMV_E_DEVICE = 5
+QGEMV_E_LAUNCH = 6
+
+QGEMV_FMT_Q4_0, QGEMV_FMT_Q4_K, QGEMV_FMT_Q6_K, QGEMV_FMT_Q8_0 = 0, 1, 2, 3
+QGEMV_VARIANT_AUTO, QGEMV_VARIANT_DOT4, QGEMV_VARIANT_MFMA = 0, 1, 2
+QGEMV_K_MAX = 32768
+QGEMV_M_MAX = 64
+
+# Every extern "C" symbol that include/qgemv.h declares.
+EXPORTS = [
+    "qgemv_abi_version", "qgemv_status_str", "qgemv_build_info", "qgemv_last_error",
+    "qgemv_quantize_act", "qgemv_q4_0", "qgemv_q4_k", "qgemv_q6_k", "qgemv_q8_0",
+    "qgemm_q4_k_small_m", "qgemv_silu_mul_quantize", "qgemv_block_dots",
+]
+
+_P, _I64, _I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+_lib.qgemv_abi_version.restype = _I
+_lib.qgemv_abi_version.argtypes = []
+_lib.qgemv_status_str.restype = ctypes.c_char_p
+_lib.qgemv_status_str.argtypes = [_I]
+_lib.qgemv_build_info.restype = ctypes.c_char_p
+_lib.qgemv_build_info.argtypes = []
+_lib.qgemv_last_error.restype = ctypes.c_char_p
+_lib.qgemv_last_error.argtypes = []
+_lib.qgemv_quantize_act.restype = _I
+_lib.qgemv_quantize_act.argtypes = [_P, _I64, _I64, _I64, _P, _P, _P, _P]
+for _n in ("qgemv_q4_0", "qgemv_q4_k", "qgemv_q6_k", "qgemv_q8_0"):
+    getattr(_lib, _n).restype = _I
+    getattr(_lib, _n).argtypes = [_P, _I64, _I64, _P, _P, _P, _P, _P]
+_lib.qgemm_q4_k_small_m.restype = _I
+_lib.qgemm_q4_k_small_m.argtypes = [_P, _I64, _I64, _I64, _P, _P, _P, _P, _I, _P]
+_lib.qgemv_silu_mul_quantize.restype = _I
+_lib.qgemv_silu_mul_quantize.argtypes = [_P, _I64, _P, _P, _P, _P, _P]
+_lib.qgemv_block_dots.restype = _I
+_lib.qgemv_block_dots.argtypes = [_I, _P, _I64, _I64, _I64, _I64, _P, _P, _P]
+
+if _lib.qgemv_abi_version() != 1:
+    raise ImportError("libqgemv ABI generation mismatch (expected 1)")
+
+
+class QgemvError(RuntimeError):
+    def __init__(self, status: int, func: str):
+        self.status = status
+        reason = qgemv_last_error()
+        super().__init__(f"{func}: {qgemv_status_str(status)} ({reason})")
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status: int, func: str) -> int:
+    if status != QGEMV_OK:
+        raise QgemvError(status, func)
+    return status
+
+
+# ---------------------------------------------------------- C-ABI names ----
+
+def qgemv_abi_version() -> int:
+    return _lib.qgemv_abi_version()
+
+
+def qgemv_status_str(status: int) -> str:
+    return _lib.qgemv_status_str(status).decode()
+
+
+def qgemv_build_info() -> str:
+    return _lib.qgemv_build_info().decode()
+
+
+def qgemv_last_error() -> str:
+    return _lib.qgemv_last_error().decode()
+
+
+def qgemv_quantize_act(x, M, K, ldx, q, d, s, stream=None):
+    return _check(_lib.qgemv_quantize_act(_ptr(x), M, K, ldx, _ptr(q), _ptr(d), _ptr(s),
+                                          _stream(stream)), "qgemv_quantize_act")
+
+
+def _gemv(name, w, N, K, q, d, s, y, stream):
+    return _check(getattr(_lib, name)(_ptr(w), N, K, _ptr(q), _ptr(d), _ptr(s), _ptr(y),
+                                      _stream(stream)), name)
+
+
+def qgemv_q4_0(w, N, K, q, d, s, y, stream=None):
+    return _gemv("qgemv_q4_0", w, N, K, q, d, s, y, stream)
+
+
+def qgemv_q4_k(w, N, K, q, d, s, y, stream=None):
+    return _gemv("qgemv_q4_k", w, N, K, q, d, s, y, stream)
+
+
+def qgemv_q6_k(w, N, K, q, d, s, y, stream=None):
+    return _gemv("qgemv_q6_k", w, N, K, q, d, s, y, stream)
+
+
+def qgemv_q8_0(w, N, K, q, d, s, y, stream=None):
+    return _gemv("qgemv_q8_0", w, N, K, q, d, s, y, stream)
+
+
+def qgemm_q4_k_small_m(w, N, K, M, q, d, s, y, variant=QGEMV_VARIANT_AUTO, stream=None):
+    return _check(_lib.qgemm_q4_k_small_m(_ptr(w), N, K, M, _ptr(q), _ptr(d), _ptr(s), _ptr(y),
+                                          variant, _stream(stream)), "qgemm_q4_k_small_m")
+
+
+def qgemv_silu_mul_quantize(gu, N, q, d, s, h=None, stream=None):
+    return _check(_lib.qgemv_silu_mul_quantize(_ptr(gu), N, _ptr(q), _ptr(d), _ptr(s), _ptr(h),
+                                               _stream(stream)), "qgemv_silu_mul_quantize")
+
+
+def qgemv_block_dots(fmt, w, N, K, row0, nrows, q, dots, stream=None):
+    return _check(_lib.qgemv_block_dots(fmt, _ptr(w), N, K, row0, nrows, _ptr(q), _ptr(dots),
+                                        _stream(stream)), "qgemv_block_dots")
+
+
+GEMV = {"q4_0": qgemv_q4_0, "q4_k": qgemv_q4_k, "q6_k": qgemv_q6_k, "q8_0": qgemv_q8_0}
+FMT_ID = {"q4_0": QGEMV_FMT_Q4_0, "q4_k": QGEMV_FMT_Q4_K, "q6_k": QGEMV_FMT_Q6_K,
+          "q8_0": QGEMV_FMT_Q8_0}
+
+
+def act_buffers(M: int, K: int, device="cuda"):
+    """Empty activation buffers (q, d, s) of the library's layout for M rows of K."""
+    import torch
+    Kp = (K + 255) // 256 * 256
+    q = torch.empty((M, Kp), dtype=torch.int8, device=device)
+    d = torch.empty((M, Kp // 32), dtype=torch.int16, device=device)
+    s = torch.empty((M, Kp // 32), dtype=torch.int32, device=device)
+    return q, d, s

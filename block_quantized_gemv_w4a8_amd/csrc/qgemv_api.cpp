@@ -1,0 +1,252 @@
+// qgemv_api.cpp -- the C ABI of libqgemv: argument gates, status codes and
+// kernel launches.  No allocation, no host synchronisation, no copies.
+//
+// Every entry point runs its gates in the same order -- NULL pointers,
+// shapes, limits of this build, alignment, device -- and returns at the first
+// failure without launching anything, so a failed call never leaves a partial
+// result (colibri GPU backends, "Eligibility gates" and "Failure invariant").
+// A refusal names its reason through qgemv_last_error() ("Backends and
+// hardware", section "CUDA": decline at open with a message naming the reason
+// rather than run a different path).
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/qgemv.h"
+#include "qgemv_launch.h"
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+qgemv_status fail(qgemv_status st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+qgemv_status ok() { return QGEMV_OK; }
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+// Per-device cache of "is this device gfx950": 0 unknown, 1 yes, 2 no.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_dev_ok[kMaxDevices];
+
+qgemv_status check_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+        (void)hipGetLastError();
+        return fail(QGEMV_E_DEVICE, "no current HIP device");
+    }
+    if (dev >= kMaxDevices) return fail(QGEMV_E_DEVICE, "device index %d out of range", dev);
+    int state = g_dev_ok[dev].load(std::memory_order_relaxed);
+    if (state == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(QGEMV_E_DEVICE, "hipGetDeviceProperties failed for device %d", dev);
+        }
+        state = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+        g_dev_ok[dev].store(state, std::memory_order_relaxed);
+        if (state == 2)
+            return fail(QGEMV_E_DEVICE, "device %d is %s, this build targets gfx950", dev,
+                        prop.gcnArchName);
+    }
+    if (state == 2) return fail(QGEMV_E_DEVICE, "device %d is not gfx950", dev);
+    return QGEMV_OK;
+}
+
+qgemv_status launched(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(QGEMV_E_LAUNCH, "%s: %s", what, hipGetErrorString(e));
+    return QGEMV_OK;
+}
+
+qgemv_status check_k(int64_t K) {
+    if (K < 32 || K % 32 != 0)
+        return fail(QGEMV_E_SHAPE, "K = %lld must be a positive multiple of 32", (long long)K);
+    return QGEMV_OK;
+}
+
+qgemv_status check_act_align(const int8_t* q, const uint16_t* d, const int32_t* s) {
+    if (!aligned(q, 16)) return fail(QGEMV_E_ALIGN, "q must be 16-byte aligned");
+    if (!aligned(d, 2)) return fail(QGEMV_E_ALIGN, "d must be 2-byte aligned");
+    if (!aligned(s, 4)) return fail(QGEMV_E_ALIGN, "s must be 4-byte aligned");
+    return QGEMV_OK;
+}
+
+const char* fmt_name(int fmt) {
+    switch (fmt) {
+    case QGEMV_FMT_Q4_0: return "qgemv_q4_0";
+    case QGEMV_FMT_Q4_K: return "qgemv_q4_k";
+    case QGEMV_FMT_Q6_K: return "qgemv_q6_k";
+    case QGEMV_FMT_Q8_0: return "qgemv_q8_0";
+    default: return "qgemv";
+    }
+}
+
+qgemv_status gemv_common(int fmt, const void* w, int64_t N, int64_t K, const int8_t* q,
+                         const uint16_t* d, const int32_t* s, float* y, qgemv_stream_t stream) {
+    const char* name = fmt_name(fmt);
+    if (N < 0) return fail(QGEMV_E_SHAPE, "%s: N = %lld is negative", name, (long long)N);
+    if (N == 0) return ok();
+    if (!w || !q || !d || !s || !y) return fail(QGEMV_E_NULL, "%s: NULL pointer argument", name);
+    qgemv_status st = check_k(K);
+    if (st != QGEMV_OK) return st;
+    if (N > INT32_MAX) return fail(QGEMV_E_SHAPE, "%s: N = %lld exceeds 2^31-1", name, (long long)N);
+    if (K > QGEMV_K_MAX)
+        return fail(QGEMV_E_UNSUPPORTED, "%s: K = %lld exceeds QGEMV_K_MAX = %d", name,
+                    (long long)K, QGEMV_K_MAX);
+    if (!aligned(w, 16)) return fail(QGEMV_E_ALIGN, "%s: w must be 16-byte aligned", name);
+    if ((st = check_act_align(q, d, s)) != QGEMV_OK) return st;
+    if (!aligned(y, 4)) return fail(QGEMV_E_ALIGN, "%s: y must be 4-byte aligned", name);
+    if ((st = check_device()) != QGEMV_OK) return st;
+    const qgemv::GemvArgs a{w, N, K, q, d, s, y};
+    return launched(qgemv::launch_gemv(fmt, a, (hipStream_t)stream), name);
+}
+
+}  // namespace
+
+extern "C" {
+
+int qgemv_abi_version(void) { return QGEMV_ABI_VERSION; }
+
+const char* qgemv_status_str(int status) {
+    switch (status) {
+    case QGEMV_OK: return "QGEMV_OK";
+    case QGEMV_E_NULL: return "QGEMV_E_NULL: a required pointer is NULL";
+    case QGEMV_E_SHAPE: return "QGEMV_E_SHAPE: invalid size or stride";
+    case QGEMV_E_UNSUPPORTED: return "QGEMV_E_UNSUPPORTED: valid but declined by this build";
+    case QGEMV_E_ALIGN: return "QGEMV_E_ALIGN: misaligned pointer";
+    case QGEMV_E_DEVICE: return "QGEMV_E_DEVICE: no usable gfx950 device";
+    case QGEMV_E_LAUNCH: return "QGEMV_E_LAUNCH: kernel launch failed";
+    default: return "QGEMV_E_UNKNOWN: unknown status code";
+    }
+}
+
+const char* qgemv_build_info(void) {
+    return "libqgemv abi=1 arch=gfx950 formats=q4_0,q4_k,q6_k,q8_0 act=int8/32+fp16+int32sum "
+           "gemv=v_dot4_i32_i8,lds-act,lanes-per-row{4,8,16,32,64} "
+           "small_m=q4_k{dot4} K_max=32768 M_max=64";
+}
+
+const char* qgemv_last_error(void) { return g_last_error; }
+
+qgemv_status qgemv_quantize_act(const float* x, int64_t M, int64_t K, int64_t ldx, int8_t* q,
+                                uint16_t* d, int32_t* s, qgemv_stream_t stream) {
+    if (M < 0) return fail(QGEMV_E_SHAPE, "qgemv_quantize_act: M = %lld is negative", (long long)M);
+    if (M == 0) return ok();
+    if (!x || !q || !d || !s) return fail(QGEMV_E_NULL, "qgemv_quantize_act: NULL pointer argument");
+    qgemv_status st = check_k(K);
+    if (st != QGEMV_OK) return st;
+    if (ldx < K)
+        return fail(QGEMV_E_SHAPE, "qgemv_quantize_act: ldx = %lld < K = %lld", (long long)ldx,
+                    (long long)K);
+    if (M > (int64_t)1 << 31 || ldx > (int64_t)1 << 40 || K > (int64_t)1 << 31)
+        return fail(QGEMV_E_UNSUPPORTED, "qgemv_quantize_act: sizes beyond this build's range");
+    const int64_t Kp = (K + 255) / 256 * 256;
+    if (M * (Kp / 32) * 8 / 256 >= ((int64_t)1 << 31))
+        return fail(QGEMV_E_UNSUPPORTED, "qgemv_quantize_act: M*K too large for one launch");
+    if (!aligned(x, 4)) return fail(QGEMV_E_ALIGN, "qgemv_quantize_act: x must be 4-byte aligned");
+    if ((st = check_act_align(q, d, s)) != QGEMV_OK) return st;
+    if ((st = check_device()) != QGEMV_OK) return st;
+    return launched(qgemv::launch_quantize_act(x, M, K, ldx, q, d, s, (hipStream_t)stream),
+                    "qgemv_quantize_act");
+}
+
+qgemv_status qgemv_q4_0(const void* w, int64_t N, int64_t K, const int8_t* q, const uint16_t* d,
+                        const int32_t* s, float* y, qgemv_stream_t stream) {
+    return gemv_common(QGEMV_FMT_Q4_0, w, N, K, q, d, s, y, stream);
+}
+
+qgemv_status qgemv_q4_k(const void* w, int64_t N, int64_t K, const int8_t* q, const uint16_t* d,
+                        const int32_t* s, float* y, qgemv_stream_t stream) {
+    return gemv_common(QGEMV_FMT_Q4_K, w, N, K, q, d, s, y, stream);
+}
+
+qgemv_status qgemv_q6_k(const void* w, int64_t N, int64_t K, const int8_t* q, const uint16_t* d,
+                        const int32_t* s, float* y, qgemv_stream_t stream) {
+    return gemv_common(QGEMV_FMT_Q6_K, w, N, K, q, d, s, y, stream);
+}
+
+qgemv_status qgemv_q8_0(const void* w, int64_t N, int64_t K, const int8_t* q, const uint16_t* d,
+                        const int32_t* s, float* y, qgemv_stream_t stream) {
+    return gemv_common(QGEMV_FMT_Q8_0, w, N, K, q, d, s, y, stream);
+}
+
+qgemv_status qgemm_q4_k_small_m(const void* w, int64_t N, int64_t K, int64_t M, const int8_t* q,
+                                const uint16_t* d, const int32_t* s, float* y, int variant,
+                                qgemv_stream_t stream) {
+    const char* name = "qgemm_q4_k_small_m";
+    if (N < 0 || M < 0) return fail(QGEMV_E_SHAPE, "%s: negative N or M", name);
+    if (N == 0 || M == 0) return ok();
+    if (!w || !q || !d || !s || !y) return fail(QGEMV_E_NULL, "%s: NULL pointer argument", name);
+    qgemv_status st = check_k(K);
+    if (st != QGEMV_OK) return st;
+    if (N > INT32_MAX) return fail(QGEMV_E_SHAPE, "%s: N exceeds 2^31-1", name);
+    if (K > QGEMV_K_MAX)
+        return fail(QGEMV_E_UNSUPPORTED, "%s: K = %lld exceeds QGEMV_K_MAX", name, (long long)K);
+    if (M > QGEMV_M_MAX)
+        return fail(QGEMV_E_UNSUPPORTED, "%s: M = %lld exceeds QGEMV_M_MAX = %d", name,
+                    (long long)M, QGEMV_M_MAX);
+    if (variant != QGEMV_VARIANT_AUTO && variant != QGEMV_VARIANT_DOT4 &&
+        variant != QGEMV_VARIANT_MFMA)
+        return fail(QGEMV_E_UNSUPPORTED, "%s: unknown variant %d", name, variant);
+    if (variant == QGEMV_VARIANT_MFMA)
+        return fail(QGEMV_E_UNSUPPORTED, "%s: the MFMA variant is not built in this library", name);
+    if (!aligned(w, 16)) return fail(QGEMV_E_ALIGN, "%s: w must be 16-byte aligned", name);
+    if ((st = check_act_align(q, d, s)) != QGEMV_OK) return st;
+    if (!aligned(y, 4)) return fail(QGEMV_E_ALIGN, "%s: y must be 4-byte aligned", name);
+    if ((st = check_device()) != QGEMV_OK) return st;
+    return launched(qgemv::launch_small_m_q4k(w, N, K, M, q, d, s, y, variant,
+                                              (hipStream_t)stream),
+                    name);
+}
+
+qgemv_status qgemv_silu_mul_quantize(const float* gu, int64_t N, int8_t* q, uint16_t* d,
+                                     int32_t* s, float* h, qgemv_stream_t stream) {
+    const char* name = "qgemv_silu_mul_quantize";
+    if (N < 0) return fail(QGEMV_E_SHAPE, "%s: N is negative", name);
+    if (N == 0) return ok();
+    if (!gu || !q || !d || !s) return fail(QGEMV_E_NULL, "%s: NULL pointer argument", name);
+    if (N % 32 != 0)
+        return fail(QGEMV_E_SHAPE, "%s: N = %lld must be a multiple of 32", name, (long long)N);
+    if (N > (int64_t)1 << 31) return fail(QGEMV_E_UNSUPPORTED, "%s: N too large", name);
+    if (!aligned(gu, 4)) return fail(QGEMV_E_ALIGN, "%s: gu must be 4-byte aligned", name);
+    qgemv_status st = check_act_align(q, d, s);
+    if (st != QGEMV_OK) return st;
+    if (h && !aligned(h, 4)) return fail(QGEMV_E_ALIGN, "%s: h must be 4-byte aligned", name);
+    if ((st = check_device()) != QGEMV_OK) return st;
+    return launched(qgemv::launch_silu_mul_quantize(gu, N, q, d, s, h, (hipStream_t)stream), name);
+}
+
+qgemv_status qgemv_block_dots(int fmt, const void* w, int64_t N, int64_t K, int64_t row0,
+                              int64_t nrows, const int8_t* q, int32_t* dots,
+                              qgemv_stream_t stream) {
+    const char* name = "qgemv_block_dots";
+    if (N < 0 || row0 < 0 || nrows < 0 || row0 > N || nrows > N - row0)
+        return fail(QGEMV_E_SHAPE, "%s: rows [%lld, %lld) outside [0, %lld)", name,
+                    (long long)row0, (long long)(row0 + nrows), (long long)N);
+    if (nrows == 0) return ok();
+    if (!w || !q || !dots) return fail(QGEMV_E_NULL, "%s: NULL pointer argument", name);
+    qgemv_status st = check_k(K);
+    if (st != QGEMV_OK) return st;
+    if (fmt < QGEMV_FMT_Q4_0 || fmt > QGEMV_FMT_Q8_0)
+        return fail(QGEMV_E_UNSUPPORTED, "%s: unknown format %d", name, fmt);
+    if (K > QGEMV_K_MAX) return fail(QGEMV_E_UNSUPPORTED, "%s: K exceeds QGEMV_K_MAX", name);
+    if (nrows * ((K + 255) / 64) / 256 >= ((int64_t)1 << 31))
+        return fail(QGEMV_E_UNSUPPORTED, "%s: too many rows for one launch", name);
+    if (!aligned(w, 16)) return fail(QGEMV_E_ALIGN, "%s: w must be 16-byte aligned", name);
+    if (!aligned(q, 16)) return fail(QGEMV_E_ALIGN, "%s: q must be 16-byte aligned", name);
+    if (!aligned(dots, 4)) return fail(QGEMV_E_ALIGN, "%s: dots must be 4-byte aligned", name);
+    if ((st = check_device()) != QGEMV_OK) return st;
+    return launched(qgemv::launch_block_dots(fmt, w, K, row0, nrows, q, dots, (hipStream_t)stream),
+                    name);
+}
+
+}  // extern "C"

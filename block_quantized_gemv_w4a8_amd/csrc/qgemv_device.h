@@ -1,0 +1,272 @@
+// qgemv_device.h -- device-side building blocks shared by every kernel of
+// libqgemv: unaligned byte loads, the 4 x int8 dot, and per-format "units".
+//
+// A unit is 64 consecutive weights of one row (the same for every format), so
+// that one lane always pairs with 64 activation codes = 16 dwords:
+//   Q4_K : unit u = chunk c (0..3) of super-block S = u/4; its 32 packed bytes
+//          hold sub-blocks 2c (low nibbles) and 2c+1 (high nibbles); the
+//          super-block header (d, dmin, 12 scale bytes) is read alongside.
+//   Q6_K : unit u = quarter (h, t) of super-block S = u/4 (h = half, t = which
+//          16 of the 32 positions l): 16 B of low nibbles for positions l,
+//          16 B for l+32, 16 B of high bit pairs; that is 4 complete groups of
+//          16 weights (elements 128h + 16t + 32j + 0..15, j = 0..3).
+//   Q4_0 / Q8_0 : unit u = blocks 2u and 2u+1 (the second may be absent when
+//          the row has an odd number of blocks).
+// The unit loaders read the packed bytes straight from global memory, and the
+// unit dot functions turn them into exact int32 block dots; the GEMV, the
+// small-M and the block-dots kernels all call these same functions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+
+namespace qgemv {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Byte-addressed loads.  memcpy lets the compiler emit one dwordx4 / dwordx2
+// load even when the address is only 2-byte aligned (Q6_K super-blocks start
+// at 210*S, Q4_0 blocks at 18*b); the HSA runtime runs in unaligned mode.
+__device__ __forceinline__ u32x4 ld16(const uint8_t* p) {
+    u32x4 v;
+    __builtin_memcpy(&v, p, 16);
+    return v;
+}
+__device__ __forceinline__ u32x2 ld8(const uint8_t* p) {
+    u32x2 v;
+    __builtin_memcpy(&v, p, 8);
+    return v;
+}
+__device__ __forceinline__ uint32_t ld2(const uint8_t* p) {
+    uint16_t v;
+    __builtin_memcpy(&v, p, 2);
+    return v;
+}
+
+__device__ __forceinline__ float h2f(uint32_t bits) {
+    return __half2float(__ushort_as_half((unsigned short)bits));
+}
+
+// Signed 4 x int8 dot with int32 accumulate (v_dot4_i32_i8).
+__device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c) {
+    return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);
+}
+
+__device__ __forceinline__ uint32_t bfe(uint32_t x, uint32_t off, uint32_t w) {
+    return __builtin_amdgcn_ubfe(x, off, w);
+}
+
+__device__ __forceinline__ int sbyte(uint32_t x, uint32_t k) {
+    return __builtin_amdgcn_sbfe((int)x, 8 * k, 8);
+}
+
+constexpr uint32_t LO4 = 0x0F0F0F0Fu;
+
+// Activation view of one unit: 16 dwords of codes (elements 64u .. 64u+63 of
+// the activation row, as laid out for the weights of the format).
+struct Act16 {
+    uint32_t a[16];
+};
+
+// ------------------------------------------------------------------ Q4_K --
+struct Q4K {
+    static constexpr int SB_BYTES = 144;
+    static constexpr int NDOT = 2;  // int32 dots per unit (sub-blocks 2c, 2c+1)
+    struct W {
+        u32x4 hdr, qa, qb;
+    };
+    __device__ static __forceinline__ void load(const uint8_t* row, int u, W& w) {
+        const uint8_t* p = row + SB_BYTES * (u >> 2);
+        const int c = u & 3;
+        w.hdr = ld16(p);
+        w.qa = ld16(p + 16 + 32 * c);
+        w.qb = ld16(p + 32 + 32 * c);
+    }
+    // Unpacked codes of a unit: lo = sub-block 2c (elements 64u + 0..31),
+    // hi = sub-block 2c+1 (elements 64u + 32..63), 4 codes per dword.
+    struct C {
+        uint32_t lo[8], hi[8];
+    };
+    __device__ static __forceinline__ void unpack(const W& w, C& c) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            c.lo[i] = w.qa[i] & LO4;
+            c.lo[4 + i] = w.qb[i] & LO4;
+            c.hi[i] = (w.qa[i] >> 4) & LO4;
+            c.hi[4 + i] = (w.qb[i] >> 4) & LO4;
+        }
+    }
+    // Activation elements of unit u start at 64u: sub-block 2c is a[0..7],
+    // sub-block 2c+1 is a[8..15].
+    __device__ static __forceinline__ void dots_c(const C& c, const Act16& x, int D[2]) {
+        int d0 = 0, d1 = 0;
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            d0 = dot4(c.lo[i], x.a[i], d0);
+            d1 = dot4(c.hi[i], x.a[8 + i], d1);
+        }
+        D[0] = d0;
+        D[1] = d1;
+    }
+    __device__ static __forceinline__ void dots(const W& w, const Act16& x, int D[2]) {
+        C c;
+        unpack(w, c);
+        dots_c(c, x, D);
+    }
+    // 6-bit scale and min of sub-block j (0..7) from the 12 header bytes
+    // b[0..11] = hdr.y, hdr.z, hdr.w:
+    //   j < 4 : scale = b[j] & 63, min = b[j+4] & 63
+    //   j >= 4: scale = (b[j+4] & 15) | (b[j-4] >> 6) << 4,
+    //           min   = (b[j+4] >> 4) | (b[j]   >> 6) << 4
+    __device__ static __forceinline__ void scale_min(const W& w, int j, int& sc, int& mn) {
+        if (j < 4) {
+            sc = (int)bfe(w.hdr.y, 8 * j, 6);
+            mn = (int)bfe(w.hdr.z, 8 * j, 6);
+        } else {
+            const uint32_t k = j - 4;
+            sc = (int)(bfe(w.hdr.w, 8 * k, 4) | (bfe(w.hdr.y, 8 * k + 6, 2) << 4));
+            mn = (int)(bfe(w.hdr.w, 8 * k + 4, 4) | (bfe(w.hdr.z, 8 * k + 6, 2) << 4));
+        }
+    }
+};
+
+// ------------------------------------------------------------------ Q6_K --
+struct Q6K {
+    static constexpr int SB_BYTES = 210;
+    static constexpr int NDOT = 4;  // int32 dots per unit (4 groups of 16)
+    struct W {
+        u32x4 qa, qb, qh;
+        u32x2 sc;
+        uint32_t d;
+    };
+    __device__ static __forceinline__ void load(const uint8_t* row, int u, W& w) {
+        const uint8_t* p = row + SB_BYTES * (u >> 2);
+        const int h = (u >> 1) & 1, t = u & 1;
+        w.qa = ld16(p + 64 * h + 16 * t);        // ql[64h + 16t ..]: positions l
+        w.qb = ld16(p + 64 * h + 32 + 16 * t);   // ql[64h + 32 + 16t ..]: l + 32
+        w.qh = ld16(p + 128 + 32 * h + 16 * t);  // qh[32h + 16t ..]
+        w.sc = ld8(p + 192 + 8 * h);             // scales of groups 8h .. 8h+7
+        w.d = ld2(p + 208);
+    }
+    // Activation of unit u = quarter (h, t): group j (elements
+    // 128h + 16t + 32j + 0..15 of the super-block) is a[4j .. 4j+3].
+    // init[j] = -32 * (sum of those 16 activation codes) folds the code offset
+    // into the dot's accumulator, so D16_j = sum (code - 32) * q exactly.
+    __device__ static __forceinline__ void dots(const W& w, const Act16& x, const int init[4],
+                                                int D[4]) {
+        int d0 = init[0], d1 = init[1], d2 = init[2], d3 = init[3];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const uint32_t qa = w.qa[i], qb = w.qb[i], qh = w.qh[i];
+            const uint32_t c0 = (qa & LO4) | ((qh << 4) & 0x30303030u);
+            const uint32_t c1 = (qb & LO4) | ((qh << 2) & 0x30303030u);
+            const uint32_t c2 = ((qa >> 4) & LO4) | (qh & 0x30303030u);
+            const uint32_t c3 = ((qb >> 4) & LO4) | ((qh >> 2) & 0x30303030u);
+            d0 = dot4(c0, x.a[i], d0);
+            d1 = dot4(c1, x.a[4 + i], d1);
+            d2 = dot4(c2, x.a[8 + i], d2);
+            d3 = dot4(c3, x.a[12 + i], d3);
+        }
+        D[0] = d0;
+        D[1] = d1;
+        D[2] = d2;
+        D[3] = d3;
+    }
+    // int8 scale of group j of this unit (group index 8h + t + 2j).
+    __device__ static __forceinline__ int scale(const W& w, int u, int j) {
+        const int t = u & 1;
+        const int k = t + 2 * j;  // byte within sc[8h .. 8h+7]
+        return k < 4 ? sbyte(w.sc.x, k) : sbyte(w.sc.y, k - 4);
+    }
+    // Activation element offset (within the row) of group j of unit u.
+    __device__ static __forceinline__ int act_offset(int u, int j) {
+        const int S = u >> 2, h = (u >> 1) & 1, t = u & 1;
+        return 256 * S + 128 * h + 16 * t + 32 * j;
+    }
+};
+
+// ------------------------------------------------------------------ Q4_0 --
+struct Q40 {
+    static constexpr int BLK_BYTES = 18;
+    static constexpr int NDOT = 2;
+    struct W {
+        u32x4 q0, q1;
+        uint32_t d0, d1;
+    };
+    // has1: whether block 2u+1 exists (row has an odd number of blocks).
+    __device__ static __forceinline__ void load(const uint8_t* row, int u, bool has1, W& w) {
+        const uint8_t* p = row + 2 * BLK_BYTES * u;
+        w.d0 = ld2(p);
+        w.q0 = ld16(p + 2);
+        if (has1) {
+            w.d1 = ld2(p + 18);
+            w.q1 = ld16(p + 20);
+        } else {
+            w.d1 = 0;
+            w.q1 = u32x4{0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u};
+        }
+    }
+    // Block 2u is a[0..7], block 2u+1 is a[8..15]; init = -8 * s_b folds the
+    // code offset into the accumulator: D = sum (code - 8) * q.
+    __device__ static __forceinline__ void dots(const W& w, const Act16& x, const int init[2],
+                                                int D[2]) {
+        int d0 = init[0], d1 = init[1];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            d0 = dot4(w.q0[i] & LO4, x.a[i], d0);
+            d0 = dot4((w.q0[i] >> 4) & LO4, x.a[4 + i], d0);
+            d1 = dot4(w.q1[i] & LO4, x.a[8 + i], d1);
+            d1 = dot4((w.q1[i] >> 4) & LO4, x.a[12 + i], d1);
+        }
+        D[0] = d0;
+        D[1] = d1;
+    }
+};
+
+// ------------------------------------------------------------------ Q8_0 --
+struct Q80 {
+    static constexpr int BLK_BYTES = 34;
+    static constexpr int NDOT = 2;
+    struct W {
+        u32x4 a0, b0, a1, b1;
+        uint32_t d0, d1;
+    };
+    __device__ static __forceinline__ void load(const uint8_t* row, int u, bool has1, W& w) {
+        const uint8_t* p = row + 2 * BLK_BYTES * u;
+        w.d0 = ld2(p);
+        w.a0 = ld16(p + 2);
+        w.b0 = ld16(p + 18);
+        if (has1) {
+            w.d1 = ld2(p + 34);
+            w.a1 = ld16(p + 36);
+            w.b1 = ld16(p + 52);
+        } else {
+            w.d1 = 0;
+            w.a1 = w.b1 = u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+    __device__ static __forceinline__ void dots(const W& w, const Act16& x, int D[2]) {
+        int d0 = 0, d1 = 0;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            d0 = dot4(w.a0[i], x.a[i], d0);
+            d0 = dot4(w.b0[i], x.a[4 + i], d0);
+            d1 = dot4(w.a1[i], x.a[8 + i], d1);
+            d1 = dot4(w.b1[i], x.a[12 + i], d1);
+        }
+        D[0] = d0;
+        D[1] = d1;
+    }
+};
+
+// Sum of 16 activation codes (4 dwords) via dot with all-ones bytes.
+__device__ __forceinline__ int sum16(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3) {
+    int s = dot4(a0, 0x01010101u, 0);
+    s = dot4(a1, 0x01010101u, s);
+    s = dot4(a2, 0x01010101u, s);
+    return dot4(a3, 0x01010101u, s);
+}
+
+}  // namespace qgemv

@@ -1,0 +1,34 @@
+// qgemv_launch.h -- internal interface between the C-ABI layer (qgemv_api.cpp)
+// and the kernel translation units.  Arguments reaching these launchers have
+// already passed every gate of the public entry points.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/qgemv.h"
+
+namespace qgemv {
+
+struct GemvArgs {
+    const void* w;
+    int64_t N, K;
+    const int8_t* q;
+    const uint16_t* d;
+    const int32_t* s;
+    float* y;
+};
+
+int gemv_smem_bytes(int fmt, int64_t K);
+hipError_t launch_gemv(int fmt, const GemvArgs& a, hipStream_t st);
+hipError_t launch_block_dots(int fmt, const void* w, int64_t K, int64_t row0, int64_t nrows,
+                             const int8_t* q, int32_t* dots, hipStream_t st);
+hipError_t launch_quantize_act(const float* x, int64_t M, int64_t K, int64_t ldx, int8_t* q,
+                               uint16_t* d, int32_t* s, hipStream_t st);
+hipError_t launch_silu_mul_quantize(const float* gu, int64_t N, int8_t* q, uint16_t* d,
+                                    int32_t* s, float* h, hipStream_t st);
+hipError_t launch_small_m_q4k(const void* w, int64_t N, int64_t K, int64_t M, const int8_t* q,
+                              const uint16_t* d, const int32_t* s, float* y, int variant,
+                              hipStream_t st);
+
+}  // namespace qgemv

@@ -1,0 +1,168 @@
+/*
+ * qgemv.h -- C ABI of libqgemv: W4A8 block-quantized GEMV for AMD MI355X (gfx950).
+ *
+ * The operation ("Backends and hardware", llamay docs, section "CPU"): the
+ * activation is quantised to int8 once per matmul, in blocks of 32 with an
+ * fp16 scale and an int32 code sum, and each weight row stays in its packed
+ * block format -- it is never expanded to float.  A row is multiplied block by
+ * block with 4 x int8 integer dot products (section "CUDA" names that dot as
+ * the W4A8 inner product), the block scales (and, for Q4_K, mins) are applied
+ * in fp32, and the row is reduced.  Accumulation across blocks is fp32
+ * ("Running an LLM on VKNN", section 7 "Precision").
+ *
+ * Generation 1.  All data pointers are DEVICE pointers (HIP global memory)
+ * unless stated otherwise; sizes are element counts.
+ *
+ * Stored weight formats (GGUF block layouts, little-endian fields), row-major,
+ * one row after another with no gap:
+ *   Q4_0  18 B per 32 weights : fp16 d | 16 B, byte j = code j (low nibble),
+ *                               code j+16 (high nibble); w = d*(code-8)
+ *   Q4_K 144 B per 256 weights: fp16 d | fp16 dmin | 12 B of 6-bit scale and
+ *                               min for 8 sub-blocks of 32 | 128 B nibbles;
+ *                               w = d*scale_j*code - dmin*min_j
+ *   Q6_K 210 B per 256 weights: 128 B low nibbles | 64 B high 2-bit pairs |
+ *                               16 int8 scales (one per 16) | fp16 d;
+ *                               w = d*scale*(code-32)
+ *   Q8_0  34 B per 32 weights : fp16 d | 32 int8 codes; w = d*code
+ * K-quant (Q4_K, Q6_K) rows hold ceil(K/256) super-blocks; the weights past K
+ * in the last one must have zero codes, scales and mins.  Q4_0 / Q8_0 rows
+ * hold exactly K/32 blocks.
+ *
+ * Activation layout (this library's, struct of arrays), Kp = K rounded up to
+ * a multiple of 256:  q int8 [M][Kp], d fp16 bits [M][Kp/32], s int32
+ * [M][Kp/32].  Blocks past K are all zero.
+ *
+ * Conventions shared by every entry point:
+ *   - Argument gates run in a fixed order, cheapest first, and the first
+ *     failure returns: NULL pointers, then shapes, then limits of this build,
+ *     then alignment, then the device (colibri GPU backends, "Eligibility
+ *     gates": every gate returns).  On any error nothing is launched and no
+ *     output is written (same page, "Failure invariant": a failure is never a
+ *     partial result).  qgemv_last_error() then names the reason.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL is the null stream)
+ *     and returns without waiting; there is no host synchronisation, no
+ *     host<->device copy and no allocation, so calls can be captured into a
+ *     HIP graph.  Faults inside a kernel surface at the caller's next
+ *     synchronisation, as usual for HIP.
+ *   - The library keeps no per-call state: concurrent calls on different
+ *     streams are safe as long as their output buffers do not overlap.
+ *     Inputs and outputs of one call must not alias.
+ *   - An empty problem (N == 0 or M == 0) returns QGEMV_OK without launching.
+ *   - Results are deterministic: the same inputs give bit-identical outputs.
+ */
+#ifndef QGEMV_H
+#define QGEMV_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QGEMV_ABI_VERSION 1
+
+/* Largest K accepted by the GEMV and small-M entry points in this build. */
+#define QGEMV_K_MAX 32768
+/* Largest M accepted by qgemm_q4_k_small_m. */
+#define QGEMV_M_MAX 64
+
+typedef void* qgemv_stream_t;
+
+typedef enum {
+    QGEMV_OK = 0,
+    QGEMV_E_NULL = 1,        /* a required pointer is NULL */
+    QGEMV_E_SHAPE = 2,       /* negative size, K not a positive multiple of 32, ldx < K, ... */
+    QGEMV_E_UNSUPPORTED = 3, /* valid but declined by this build (K > QGEMV_K_MAX, M > QGEMV_M_MAX, bad enum) */
+    QGEMV_E_ALIGN = 4,       /* w, q not 16-byte aligned; d 2-byte; x, s, y, h, gu, dots 4-byte */
+    QGEMV_E_DEVICE = 5,      /* no current HIP device, or it is not gfx950 */
+    QGEMV_E_LAUNCH = 6       /* the kernel launch itself failed */
+} qgemv_status;
+
+enum { QGEMV_FMT_Q4_0 = 0, QGEMV_FMT_Q4_K = 1, QGEMV_FMT_Q6_K = 2, QGEMV_FMT_Q8_0 = 3 };
+enum { QGEMV_VARIANT_AUTO = 0, QGEMV_VARIANT_DOT4 = 1, QGEMV_VARIANT_MFMA = 2 };
+
+/* Returns QGEMV_ABI_VERSION of the loaded library.  A caller built against a
+ * different generation must refuse the library as a whole. */
+int qgemv_abi_version(void);
+
+/* Static, never-NULL name of a status code (unknown codes included). */
+const char* qgemv_status_str(int status);
+
+/* Static string: target architecture, formats and kernel variants built in. */
+const char* qgemv_build_info(void);
+
+/* Reason for the most recent non-OK status returned to the calling thread
+ * (thread-local, overwritten by the next failing call; "" if none). */
+const char* qgemv_last_error(void);
+
+/* Activation quantisation ("Backends and hardware", section "CPU": quantised
+ * to int8 once per matmul).  x: fp32 [M][ldx] with K valid columns
+ * (K % 32 == 0, ldx >= K).  For every block of 32 values:
+ *     amax = max|x_i|;  amax == 0 -> d = 0, q_i = 0, s = 0;  otherwise
+ *     d32 = amax / 127 (IEEE fp32 division),
+ *     q_i = clamp(round_half_away(x_i / d32), -127, 127) (IEEE division),
+ *     d = fp16(d32) rounded to nearest even, s = sum q_i.
+ * Writes q [M][Kp], d [M][Kp/32], s [M][Kp/32]; blocks past K are zero. */
+qgemv_status qgemv_quantize_act(const float* x, int64_t M, int64_t K, int64_t ldx,
+                                int8_t* q, uint16_t* d, int32_t* s,
+                                qgemv_stream_t stream);
+
+/* y[n] = sum over the row's blocks of the block's integer dot with the
+ * activation codes times its scales (see the format table above):
+ *   Q4_0, Q8_0: y = sum_b f(dw_b) f(dx_b) D_b
+ *   Q4_K: y = sum_{S,j} f(d_S) sc_Sj f(dx_b) D_Sj - f(dmin_S) m_Sj f(dx_b) s_b
+ *   Q6_K: y = sum_{S,g} f(d_S) sc_Sg f(dx_b) D16_Sg   (groups of 16)
+ * with D the int32 block dot of the codes (minus the format's offset) and the
+ * activation codes.  w: N weight rows in the format; q/d/s: one activation
+ * row from qgemv_quantize_act with the same K; y: fp32 [N].
+ * The weight rows are read once, as packed bytes. */
+qgemv_status qgemv_q4_0(const void* w, int64_t N, int64_t K, const int8_t* q,
+                        const uint16_t* d, const int32_t* s, float* y,
+                        qgemv_stream_t stream);
+qgemv_status qgemv_q4_k(const void* w, int64_t N, int64_t K, const int8_t* q,
+                        const uint16_t* d, const int32_t* s, float* y,
+                        qgemv_stream_t stream);
+qgemv_status qgemv_q6_k(const void* w, int64_t N, int64_t K, const int8_t* q,
+                        const uint16_t* d, const int32_t* s, float* y,
+                        qgemv_stream_t stream);
+qgemv_status qgemv_q8_0(const void* w, int64_t N, int64_t K, const int8_t* q,
+                        const uint16_t* d, const int32_t* s, float* y,
+                        qgemv_stream_t stream);
+
+/* A few activation rows at once against Q4_K weights (the batched prefill
+ * chunk; "Backends and hardware", section "CUDA": tensor-core prefill that
+ * stages the next weight tile behind the current multiply).  Row m of y
+ * equals qgemv_q4_k on activation row m (colibri GPU backends, eligibility
+ * gates: C = A x B is row-independent).  q [M][Kp], d/s [M][Kp/32],
+ * y fp32 [M][N] row-major, 1 <= M <= QGEMV_M_MAX.
+ * variant: QGEMV_VARIANT_DOT4 (4 x int8 dots), QGEMV_VARIANT_MFMA (int8
+ * matrix cores), or QGEMV_VARIANT_AUTO (chooses by M). */
+qgemv_status qgemm_q4_k_small_m(const void* w, int64_t N, int64_t K, int64_t M,
+                                const int8_t* q, const uint16_t* d, const int32_t* s,
+                                float* y, int variant, qgemv_stream_t stream);
+
+/* SwiGLU glue between the gate|up and down products (llambda.lisp README,
+ * supported architectures; "Running an LLM on VKNN", SwiGLU):
+ * gu fp32 [2N] = [gate (N) | up (N)], N % 32 == 0.
+ *   h_i = g_i / (1 + exp(-g_i)) * u_i   (fp32)
+ * then h is quantised exactly as qgemv_quantize_act with K = N: writes
+ * q [Kp], d [Kp/32], s [Kp/32]; if h != NULL the fp32 h [N] is written too. */
+qgemv_status qgemv_silu_mul_quantize(const float* gu, int64_t N, int8_t* q,
+                                     uint16_t* d, int32_t* s, float* h,
+                                     qgemv_stream_t stream);
+
+/* Validation: the int32 block dots of weight rows [row0, row0+nrows) against
+ * one activation row q [Kp], computed by the same device code as the GEMV
+ * kernels.  dots: int32 [nrows][nblk] with nblk = K/32 (Q4_0, Q8_0),
+ * Kp/32 (Q4_K: sub-blocks of 32, codes 0..15, no min), Kp/16 (Q6_K: groups of
+ * 16, codes minus 32); Q4_0 dots include the -8 offset.  "The way to tell a
+ * SIMD bug from a block bug" ("Backends and hardware", section "CPU"). */
+qgemv_status qgemv_block_dots(int fmt, const void* w, int64_t N, int64_t K,
+                              int64_t row0, int64_t nrows, const int8_t* q,
+                              int32_t* dots, qgemv_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QGEMV_H */

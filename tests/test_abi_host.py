@@ -1,0 +1,122 @@
+"""Host-side checks of the C-ABI library: it loads, exports every symbol the
+header declares, and each argument gate returns its own status before any
+device work (no compute call is made here)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qgemv.h")
+
+
+def _lib():
+    import block_quantized_gemv_w4a8_amd as qg
+    return qg
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(qgemv_\w+|qgemm_\w+)\s*\(", text)))
+
+
+def _no_gpu():
+    import torch
+    return torch.cuda.device_count() == 0
+
+
+def test_header_declarations_match_binding():
+    qg = _lib()
+    assert _declared() == sorted(qg.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    qg = _lib()
+    lib = ctypes.CDLL(qg.LIB_PATH)
+    for name in _declared():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", qg.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r" T (\w+)$", out, re.M))
+    assert set(_declared()) <= exported
+
+
+def test_version_and_strings():
+    qg = _lib()
+    assert qg.qgemv_abi_version() == 1
+    for code in range(0, 8):
+        s = qg.qgemv_status_str(code)
+        assert s.startswith("QGEMV_")
+    assert qg.qgemv_status_str(-5).startswith("QGEMV_E_UNKNOWN")
+    info = qg.qgemv_build_info()
+    assert "gfx950" in info and "q6_k" in info
+
+
+# Fake device addresses: only ever passed where an earlier gate must refuse.
+A = 0x7F0000000000  # 256-byte aligned
+
+
+def _status(fn, *args):
+    qg = _lib()
+    return getattr(qg._lib, fn)(*args)
+
+
+def test_gates_null_shape_limits_align():
+    qg = _lib()
+    S = 0  # stream
+    # NULL pointers
+    assert _status("qgemv_q4_k", None, 10, 256, A, A, A, A, S) == qg.QGEMV_E_NULL
+    assert _status("qgemv_q6_k", A, 10, 256, A, A, A, None, S) == qg.QGEMV_E_NULL
+    assert "NULL" in qg.qgemv_last_error()
+    assert _status("qgemv_quantize_act", None, 1, 32, 32, A, A, A, S) == qg.QGEMV_E_NULL
+    assert _status("qgemv_silu_mul_quantize", A, 64, None, A, A, None, S) == qg.QGEMV_E_NULL
+    assert _status("qgemv_block_dots", 1, A, 4, 256, 0, 4, A, None, S) == qg.QGEMV_E_NULL
+    # shapes
+    for K in (0, 16, 48, -32):
+        assert _status("qgemv_q4_0", A, 10, K, A, A, A, A, S) == qg.QGEMV_E_SHAPE
+    assert _status("qgemv_q4_k", A, -1, 256, A, A, A, A, S) == qg.QGEMV_E_SHAPE
+    assert _status("qgemv_quantize_act", A, 2, 64, 32, A, A, A, S) == qg.QGEMV_E_SHAPE  # ldx < K
+    assert _status("qgemv_silu_mul_quantize", A, 48, A, A, A, None, S) == qg.QGEMV_E_SHAPE
+    assert _status("qgemv_block_dots", 1, A, 4, 256, 3, 2, A, A, S) == qg.QGEMV_E_SHAPE
+    assert _status("qgemm_q4_k_small_m", A, 8, 256, -1, A, A, A, A, 1, S) == qg.QGEMV_E_SHAPE
+    # empty problems succeed without touching anything (NULLs allowed)
+    assert _status("qgemv_q4_k", None, 0, 256, None, None, None, None, S) == qg.QGEMV_OK
+    assert _status("qgemv_quantize_act", None, 0, 256, 256, None, None, None, S) == qg.QGEMV_OK
+    assert _status("qgemm_q4_k_small_m", None, 5, 256, 0, None, None, None, None, 0, S) == qg.QGEMV_OK
+    assert _status("qgemv_block_dots", 2, None, 4, 256, 4, 0, None, None, S) == qg.QGEMV_OK
+    # limits of this build
+    assert _status("qgemv_q6_k", A, 10, 65536, A, A, A, A, S) == qg.QGEMV_E_UNSUPPORTED
+    assert _status("qgemm_q4_k_small_m", A, 8, 256, 65, A, A, A, A, 1, S) == qg.QGEMV_E_UNSUPPORTED
+    assert _status("qgemm_q4_k_small_m", A, 8, 256, 4, A, A, A, A, 9, S) == qg.QGEMV_E_UNSUPPORTED
+    assert _status("qgemv_block_dots", 7, A, 4, 256, 0, 4, A, A, S) == qg.QGEMV_E_UNSUPPORTED
+    # alignment
+    assert _status("qgemv_q4_k", A + 8, 10, 256, A, A, A, A, S) == qg.QGEMV_E_ALIGN
+    assert _status("qgemv_q4_k", A, 10, 256, A + 4, A, A, A, S) == qg.QGEMV_E_ALIGN
+    assert _status("qgemv_q4_k", A, 10, 256, A, A + 1, A, A, S) == qg.QGEMV_E_ALIGN
+    assert _status("qgemv_q4_k", A, 10, 256, A, A, A + 2, A, S) == qg.QGEMV_E_ALIGN
+    assert _status("qgemv_q4_k", A, 10, 256, A, A, A, A + 2, S) == qg.QGEMV_E_ALIGN
+    assert _status("qgemv_quantize_act", A + 2, 1, 32, 32, A, A, A, S) == qg.QGEMV_E_ALIGN
+    assert _status("qgemv_silu_mul_quantize", A, 64, A, A, A, A + 1, S) == qg.QGEMV_E_ALIGN
+    assert "aligned" in qg.qgemv_last_error()
+
+
+def test_gate_order_null_before_shape_before_align():
+    qg = _lib()
+    # a NULL pointer wins over a bad K and a misaligned pointer
+    assert _status("qgemv_q4_k", None, 10, 48, A + 1, A, A, A, 0) == qg.QGEMV_E_NULL
+    # a bad K wins over a misaligned pointer
+    assert _status("qgemv_q4_k", A + 1, 10, 48, A, A, A, A, 0) == qg.QGEMV_E_SHAPE
+    # the limits gate wins over alignment
+    assert _status("qgemv_q4_k", A + 1, 10, 65536, A, A, A, A, 0) == qg.QGEMV_E_UNSUPPORTED
+
+
+@pytest.mark.skipif(not _no_gpu(), reason="device gate refusal is only observable without a GPU")
+def test_device_gate_without_gpu():
+    qg = _lib()
+    st = _status("qgemv_q4_k", A, 10, 256, A, A, A, A, 0)
+    assert st == qg.QGEMV_E_DEVICE
+    assert qg.qgemv_last_error()
+    with pytest.raises(qg.QgemvError):
+        qg.qgemv_q6_k(A, 10, 256, A, A, A, A, stream=0)
