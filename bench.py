@@ -1,0 +1,330 @@
+#!/usr/bin/env python3
+"""Throughput of the W4A8 block-quantized GEMV path on one MI355X.
+
+One step = one batch-1 Llama-3.1-8B decode pass over the Llama-shaped
+matrices of the hot path, stream-ordered on one HIP stream with no host
+round trip:
+    quantize(x) -> gate|up  Q4_K 28672 x 4096 -> SiLU(gate)*up + requantize
+                -> down     Q6_K  4096 x 14336
+    quantize(x') -> lm_head Q6_K 128256 x 4096
+All inputs are seeded synthetic data (synth module) resident in HBM before the
+timed region; weights are rotated over --copies copies so consecutive steps do
+not read the same bytes (one copy is already 545 MB, twice the 256 MB
+Infinity Cache).
+
+Prints ONE JSON line on stdout (diagnostics go to stderr):
+  value      weight GB/s of the whole step (logical weight bytes / step time)
+  roofline   the dominant kernel (the lm_head Q6_K GEMV): algorithmic bytes
+             per launch / its average duration from HIP events recorded
+             around each of its launches inside the timed region
+  cpu_baseline  the CPU oracle timed on this host over whole steps
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+METRIC = "quantized GEMV weight GB/s and % of HBM peak at Llama-3-8B shapes, 1 GPU"
+WORKLOAD = ("llama3.1-8b decode step, batch 1: ffn gate|up q4_k 28672x4096 -> silu*up "
+            "requant -> down q6_k 4096x14336, then lm_head q6_k 128256x4096")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_q6k_lm_head.json")
+KERNEL_SOURCES = ["qgemv_device.h", "k_gemv.hip", "k_quantize.hip", "qgemv_api.cpp"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_fingerprint() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "block_quantized_gemv_w4a8_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--copies", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the per-kernel/config extras")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a plain 1 GiB device copy (for counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the "
+              "multi-GPU sharding of this path is a design note, not a measured mode.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import block_quantized_gemv_w4a8_amd as qg
+    import synth
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    t0 = time.time()
+    c2 = synth.config2()
+    c3 = synth.config3()
+    log(f"[bench] inputs generated in {time.time() - t0:.1f}s")
+    Ngu, Kgu, Nd, Kd = c2["N_gu"], c2["K_gu"], c2["N_down"], c2["K_down"]
+    Nh, Kh = c3["N"], c3["K"]
+    R = max(1, args.copies)
+    w_gu = [torch.from_numpy(c2["w_gu"]).to(dev)]
+    w_dn = [torch.from_numpy(c2["w_down"]).to(dev)]
+    w_hd = [torch.from_numpy(c3["w"]).to(dev)]
+    for _ in range(R - 1):
+        w_gu.append(w_gu[0].clone())
+        w_dn.append(w_dn[0].clone())
+        w_hd.append(w_hd[0].clone())
+    x_ffn = torch.from_numpy(c2["x"]).to(dev)
+    x_head = torch.from_numpy(c3["x"]).to(dev)
+    q1, d1, s1 = qg.act_buffers(1, Kgu, dev)
+    gu = torch.empty(Ngu, dtype=torch.float32, device=dev)
+    q2, d2, s2 = qg.act_buffers(1, Kd, dev)
+    y_ffn = torch.empty(Nd, dtype=torch.float32, device=dev)
+    q3, d3, s3 = qg.act_buffers(1, Kh, dev)
+    logits = torch.empty(Nh, dtype=torch.float32, device=dev)
+
+    wbytes = {
+        "gate_up": synth.logical_bytes("q4_k", Ngu, Kgu),
+        "down": synth.logical_bytes("q6_k", Nd, Kd),
+        "lm_head": synth.logical_bytes("q6_k", Nh, Kh),
+    }
+    step_wbytes = sum(wbytes.values())
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    def step(i, ev=None):
+        c = i % R
+        qg.qgemv_quantize_act(x_ffn, 1, Kgu, Kgu, q1, d1, s1, stream=sh)
+        qg.qgemv_q4_k(w_gu[c], Ngu, Kgu, q1, d1, s1, gu, stream=sh)
+        qg.qgemv_silu_mul_quantize(gu, Kd, q2, d2, s2, None, stream=sh)
+        qg.qgemv_q6_k(w_dn[c], Nd, Kd, q2, d2, s2, y_ffn, stream=sh)
+        qg.qgemv_quantize_act(x_head, 1, Kh, Kh, q3, d3, s3, stream=sh)
+        if ev is not None:
+            ev[0].record(stream)
+        qg.qgemv_q6_k(w_hd[c], Nh, Kh, q3, d3, s3, logits, stream=sh)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(K)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    start.record(stream)
+    for i in range(K):
+        step(i, evs[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    w1 = time.perf_counter()
+    gpu_ms = start.elapsed_time(end)
+    wall_ms = (w1 - w0) * 1e3
+    ms_per_step = max(gpu_ms, wall_ms) / K
+    value = step_wbytes / (ms_per_step * 1e-3) / 1e9
+    head_us = [a.elapsed_time(b) * 1e3 for a, b in evs]
+    head_avg_us = float(np.mean(head_us))
+    log(f"[bench] step {ms_per_step * 1e3:.1f} us (events {gpu_ms / K * 1e3:.1f}, wall "
+        f"{wall_ms / K * 1e3:.1f}); lm_head avg {head_avg_us:.2f} us")
+
+    # dominant kernel roofline: algorithmic bytes per launch of the lm_head GEMV
+    # = N rows x (row weight bytes + 4 B output) + one activation row
+    act_bytes = Kh + 2 * (Kh // 32) + 4 * (Kh // 32)
+    head_alg = Nh * (synth.row_bytes("q6_k", Kh) + 4) + act_bytes
+    achieved = head_alg / (head_avg_us * 1e-6) / 1e9
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        tr = json.load(open(TRAFFIC_FILE))
+        if tr.get("kernel_fingerprint") == kernel_fingerprint():
+            traffic = tr.get("bytes_per_launch")
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                "kernel": "qgemv_q6_k lm_head 128256x4096", "avg_us": round(head_avg_us, 2),
+                "alg_bytes_per_launch": head_alg}
+
+    extra = {}
+    if not args.no_extra:
+        extra = extras(qg, torch, np, synth, dev, R, c2, c3, args)
+
+    if args.calib_copy:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(np, synth, c2, c3, args.cpu_seconds, step_wbytes)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic (seeded; shapes and value distributions of the five workloads)",
+        "config": {"workload": WORKLOAD, "batch": 1,
+                   "weight_bytes_per_step": step_wbytes, "weight_copies_rotated": R,
+                   "steps_per_s": round(1e3 / ms_per_step, 1)},
+        "hbm_peak_frac": round(value / HBM_PEAK_GBPS, 4),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    if extra:
+        out["extra"] = extra
+    print(json.dumps(out), flush=True)
+
+
+def time_kernel(torch, fn, iters, R):
+    """Average microseconds of fn(i) over iters launches (events around the loop)."""
+    for i in range(3):
+        fn(i % R)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(iters):
+        fn(i % R)
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / iters
+
+
+def extras(qg, torch, np, synth, dev, R, c2, c3, args):
+    """Per-kernel timings of the step's GEMVs and the other workloads."""
+    ex = {}
+    Ngu, Kgu, Nd, Kd = c2["N_gu"], c2["K_gu"], c2["N_down"], c2["K_down"]
+    Nh, Kh = c3["N"], c3["K"]
+
+    def gemv_case(fmt, w_host, N, K, x, copies):
+        ws = [torch.from_numpy(w_host).to(dev)]
+        for _ in range(copies - 1):
+            ws.append(ws[0].clone())
+        q, d, s = qg.act_buffers(1, K, dev)
+        qg.qgemv_quantize_act(torch.from_numpy(x).to(dev), 1, K, K, q, d, s)
+        y = torch.empty(N, dtype=torch.float32, device=dev)
+        f = qg.GEMV[fmt]
+        us = time_kernel(torch, lambda c: f(ws[c], N, K, q, d, s, y), 100, copies)
+        wb = synth.logical_bytes(fmt, N, K)
+        del ws
+        return {"us": round(us, 2), "weight_GBps": round(wb / us / 1e3, 1),
+                "hbm_frac": round(wb / us / 1e3 / HBM_PEAK_GBPS, 4), "calls_per_s": round(1e6 / us)}
+
+    ex["gate_up_q4_k_28672x4096"] = gemv_case("q4_k", c2["w_gu"], Ngu, Kgu, c2["x"], 8)
+    hx = np.random.default_rng(0).standard_normal((1, Kd)).astype(np.float32)
+    ex["down_q6_k_4096x14336"] = gemv_case("q6_k", c2["w_down"], Nd, Kd, hx, 11)
+    ex["lm_head_q6_k_128256x4096"] = gemv_case("q6_k", c3["w"], Nh, Kh, c3["x"], 2)
+    # cache-resident (single 48 MB copy of down, read again and again)
+    one = gemv_case("q6_k", c2["w_down"], Nd, Kd, hx, 1)
+    ex["down_q6_k_cache_resident_single_copy"] = one
+
+    # quantize and glue kernels
+    q, d, s = qg.act_buffers(1, Kgu, dev)
+    x = torch.from_numpy(c2["x"]).to(dev)
+    ex["quantize_act_4096_us"] = round(time_kernel(
+        torch, lambda c: qg.qgemv_quantize_act(x, 1, Kgu, Kgu, q, d, s), 200, 1), 2)
+    gu = torch.randn(Ngu, device=dev)
+    q2, d2, s2 = qg.act_buffers(1, Kd, dev)
+    ex["silu_mul_quantize_14336_us"] = round(time_kernel(
+        torch, lambda c: qg.qgemv_silu_mul_quantize(gu, Kd, q2, d2, s2, None), 200, 1), 2)
+
+    # config 0 / config 1: launch-bound small GEMVs (weights rotated over 64 copies)
+    c0 = synth.config0()
+    ex["config0_q4_0_896x896"] = gemv_case("q4_0", c0["w"], 896, 896, c0["x"], 1200)
+    c1 = synth.config1()
+    layer_us = 0.0
+    per = {}
+    for name, m in c1["mats"].items():
+        r = gemv_case("q4_k", m["w"], m["N"], m["K"], m["x"], 64)
+        per[name] = r["us"]
+        layer_us += r["us"]
+    ex["config1_q4_k_layer"] = {"per_matrix_us": per, "sum_us": round(layer_us, 2),
+                                "weight_GBps": round(8386560 / layer_us / 1e3, 1)}
+
+    # config 4: small-M Q4_K 14336 x 4096
+    c4 = synth.config4()
+    N4, K4 = c4["N"], c4["K"]
+    w4 = [torch.from_numpy(c4["w"]).to(dev)]
+    for _ in range(15):
+        w4.append(w4[0].clone())
+    sm = {}
+    for M in (1, 2, 4, 8, 16, 32, 64):
+        xm = torch.from_numpy(np.ascontiguousarray(c4["x64"][:M])).to(dev)
+        qm, dm, smm = qg.act_buffers(M, K4, dev)
+        qg.qgemv_quantize_act(xm, M, K4, K4, qm, dm, smm)
+        ym = torch.empty((M, N4), dtype=torch.float32, device=dev)
+        for vname, v in (("dot4", qg.QGEMV_VARIANT_DOT4),):
+            us = time_kernel(torch, lambda c: qg.qgemm_q4_k_small_m(
+                w4[c], N4, K4, M, qm, dm, smm, ym, v), 50, 16)
+            sm[f"M{M}_{vname}_us"] = round(us, 2)
+    sm["weight_GBps_M8_dot4"] = round(33030144 / sm["M8_dot4_us"] / 1e3, 1)
+    ex["config4_small_m_q4_k_14336x4096"] = sm
+    del w4
+
+    # plain device copy: the achievable HBM figure beside the datasheet peak
+    a = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+    b = torch.empty_like(a)
+    us = time_kernel(torch, lambda c: b.copy_(a), 10, 1)
+    ex["device_copy_1GiB_GBps_read_plus_write"] = round(2 * (1 << 30) / us / 1e3, 1)
+    return ex
+
+
+def cpu_baseline(np, synth, c2, c3, seconds, step_wbytes):
+    """The oracle (single-threaded plain C) over whole steps of the same
+    workload, repeated until `seconds` of CPU time have passed (at least once)."""
+    import oracle
+    Ngu, Kgu, Nd, Kd = c2["N_gu"], c2["K_gu"], c2["N_down"], c2["K_down"]
+    Nh, Kh = c3["N"], c3["K"]
+    times = []
+    t_all = time.perf_counter()
+    while True:
+        t = time.perf_counter()
+        q, d, s = oracle.quantize_act(c2["x"])
+        gu, _ = oracle.gemv("q4_k", c2["w_gu"], Ngu, Kgu, q, d, s)
+        h = oracle.silu_mul(gu.astype(np.float32))
+        q2, d2, s2 = oracle.quantize_act(h.astype(np.float32)[None])
+        oracle.gemv("q6_k", c2["w_down"], Nd, Kd, q2, d2, s2)
+        q3, d3, s3 = oracle.quantize_act(c3["x"])
+        oracle.gemv("q6_k", c3["w"], Nh, Kh, q3, d3, s3)
+        times.append(time.perf_counter() - t)
+        if time.perf_counter() - t_all >= seconds:
+            break
+    per = float(np.median(times))
+    return {"value": round(step_wbytes / per / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle", "ms_per_step": round(per * 1e3, 1),
+            "sample": f"{len(times)} whole steps of the same workload, single thread, "
+                      f"median step time"}
+
+
+if __name__ == "__main__":
+    main()

@@ -20,6 +20,8 @@
 //     lock-free writes).
 //   * a workgroup (4 waves) owns a contiguous run of rows, so the cache lines
 //     shared by neighbouring rows are fetched by one XCD.
+#include <atomic>
+
 #include "qgemv_device.h"
 #include "qgemv_launch.h"
 
@@ -27,84 +29,111 @@ namespace qgemv {
 
 constexpr int WG = 256;  // 4 wavefronts of 64
 
-// LDS layout of the staged activation row (Kp codes, then per-block data).
-struct ActSmem {
-    const uint8_t* codes;  // [Kp]
-    const float* dx;       // [Kp/32] fp32 value of the block scale
-    const float* dxs;      // Q4_K: [Kp/32] dx * s (exact in fp32)
-    const int* init;       // Q4_0: [Kp/32] -8*s ; Q6_K: [Kp/16] -32*sum16
-};
-
-__host__ __device__ inline int smem_bytes(int fmt, int Kp) {
-    const int nb = Kp / 32;
-    int bytes = Kp + 4 * nb;
-    if (fmt == QGEMV_FMT_Q4_K || fmt == QGEMV_FMT_Q4_0) bytes += 4 * nb;
-    if (fmt == QGEMV_FMT_Q6_K) bytes += 8 * nb;
-    return bytes;
+// Sum over aligned groups of LPR lanes with DPP (no LDS round trip).  The
+// total of each group is valid in the group's last lane (li == LPR - 1); the
+// order of the additions is fixed, so results are deterministic.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp(float v) {
+    return __builtin_bit_cast(float,
+        __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xF, false));
+}
+template <int LPR>
+__device__ __forceinline__ float group_sum(float v) {
+    v += dpp<0xB1, 0xF>(v);                        // quad_perm [1,0,3,2]
+    v += dpp<0x4E, 0xF>(v);                        // quad_perm [2,3,0,1]
+    if constexpr (LPR >= 8) v += dpp<0x141, 0xF>(v);   // row_half_mirror
+    if constexpr (LPR >= 16) v += dpp<0x140, 0xF>(v);  // row_mirror
+    if constexpr (LPR >= 32) v += dpp<0x142, 0xA>(v);  // row_bcast:15 into rows 1, 3
+    if constexpr (LPR >= 64) v += dpp<0x143, 0xC>(v);  // row_bcast:31 into rows 2, 3
+    return v;
 }
 
+// The activation of one unit, held in registers for the whole kernel: a lane
+// always covers the same units of every row it visits.
 template <int FMT>
-__device__ __forceinline__ ActSmem stage_act(uint8_t* smem, const int8_t* __restrict__ q,
-                                             const uint16_t* __restrict__ d,
-                                             const int32_t* __restrict__ s, int Kp) {
-    const int nb = Kp / 32;
-    uint8_t* codes = smem;
-    float* dx = reinterpret_cast<float*>(smem + Kp);
-    float* aux_f = dx + nb;
-    int* aux_i = reinterpret_cast<int*>(dx + nb);
-    const int tid = threadIdx.x;
-    for (int i = tid; i < Kp / 16; i += WG)
-        reinterpret_cast<u32x4*>(codes)[i] = reinterpret_cast<const u32x4*>(q)[i];
-    for (int b = tid; b < nb; b += WG) {
-        const float f = h2f(d[b]);
-        dx[b] = f;
-        if (FMT == QGEMV_FMT_Q4_K) aux_f[b] = f * (float)s[b];
-        if (FMT == QGEMV_FMT_Q4_0) aux_i[b] = -8 * s[b];
-    }
-    if (FMT == QGEMV_FMT_Q6_K) {
-        for (int g = tid; g < 2 * nb; g += WG) {
-            const u32x4 v = reinterpret_cast<const u32x4*>(q)[g];
-            aux_i[g] = -32 * sum16(v.x, v.y, v.z, v.w);
+struct ActReg;
+
+template <>
+struct ActReg<QGEMV_FMT_Q4_K> {
+    Act16 x;
+    float dx[2], dxs[2];  // blocks 2u, 2u+1: f(dx) and f(dx) * s (exact in fp32)
+    __device__ void load(const int8_t* q, const uint16_t* d, const int32_t* s, int u) {
+        const u32x4* p = reinterpret_cast<const u32x4*>(q + 64 * u);
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            const u32x4 v = p[k];
+            x.a[4 * k] = v.x; x.a[4 * k + 1] = v.y; x.a[4 * k + 2] = v.z; x.a[4 * k + 3] = v.w;
+        }
+#pragma unroll
+        for (int jj = 0; jj < 2; jj++) {
+            dx[jj] = h2f(d[2 * u + jj]);
+            dxs[jj] = dx[jj] * (float)s[2 * u + jj];
         }
     }
-    __syncthreads();
-    return ActSmem{codes, dx, aux_f, aux_i};
-}
+};
 
-__device__ __forceinline__ void lds_act64(const uint8_t* codes, int off, Act16& x) {
-    const u32x4* p = reinterpret_cast<const u32x4*>(codes + off);
-#pragma unroll
-    for (int k = 0; k < 4; k++) {
-        const u32x4 v = p[k];
-        x.a[4 * k + 0] = v.x;
-        x.a[4 * k + 1] = v.y;
-        x.a[4 * k + 2] = v.z;
-        x.a[4 * k + 3] = v.w;
-    }
-}
-
-__device__ __forceinline__ void lds_act_q6k(const uint8_t* codes, int u, Act16& x) {
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(codes + Q6K::act_offset(u, j));
-        x.a[4 * j + 0] = v.x;
-        x.a[4 * j + 1] = v.y;
-        x.a[4 * j + 2] = v.z;
-        x.a[4 * j + 3] = v.w;
-    }
-}
-
-// fp32 contribution of one unit of a row.
-template <int FMT>
-__device__ __forceinline__ float unit_term(const uint8_t* __restrict__ rp, int u, int nbw,
-                                           const ActSmem& A) {
+template <>
+struct ActReg<QGEMV_FMT_Q6_K> {
     Act16 x;
-    if constexpr (FMT == QGEMV_FMT_Q4_K) {
-        Q4K::W w;
-        Q4K::load(rp, u, w);
-        lds_act64(A.codes, 64 * u, x);
+    float dx[4];
+    int init[4];  // -32 * (sum of the group's 16 codes)
+    __device__ void load(const int8_t* q, const uint16_t* d, const int32_t*, int u) {
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const int off = Q6K::act_offset(u, j);
+            const u32x4 v = *reinterpret_cast<const u32x4*>(q + off);
+            x.a[4 * j] = v.x; x.a[4 * j + 1] = v.y; x.a[4 * j + 2] = v.z; x.a[4 * j + 3] = v.w;
+            init[j] = -32 * sum16(v.x, v.y, v.z, v.w);
+            dx[j] = h2f(d[off >> 5]);
+        }
+    }
+};
+
+template <>
+struct ActReg<QGEMV_FMT_Q4_0> {
+    Act16 x;
+    float dx[2];
+    int init[2];  // -8 * s_b
+    __device__ void load(const int8_t* q, const uint16_t* d, const int32_t* s, int u) {
+        const u32x4* p = reinterpret_cast<const u32x4*>(q + 64 * u);
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            const u32x4 v = p[k];
+            x.a[4 * k] = v.x; x.a[4 * k + 1] = v.y; x.a[4 * k + 2] = v.z; x.a[4 * k + 3] = v.w;
+        }
+#pragma unroll
+        for (int jj = 0; jj < 2; jj++) {
+            dx[jj] = h2f(d[2 * u + jj]);
+            init[jj] = -8 * s[2 * u + jj];
+        }
+    }
+};
+
+template <>
+struct ActReg<QGEMV_FMT_Q8_0> {
+    Act16 x;
+    float dx[2];
+    __device__ void load(const int8_t* q, const uint16_t* d, const int32_t*, int u) {
+        const u32x4* p = reinterpret_cast<const u32x4*>(q + 64 * u);
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            const u32x4 v = p[k];
+            x.a[4 * k] = v.x; x.a[4 * k + 1] = v.y; x.a[4 * k + 2] = v.z; x.a[4 * k + 3] = v.w;
+        }
+        dx[0] = h2f(d[2 * u]);
+        dx[1] = h2f(d[2 * u + 1]);
+    }
+};
+
+template <int FMT>
+struct Unit;
+template <>
+struct Unit<QGEMV_FMT_Q4_K> {
+    using W = Q4K::W;
+    __device__ static void load(const uint8_t* rp, int u, bool, W& w) { Q4K::load(rp, u, w); }
+    __device__ static float term(const W& w, const ActReg<QGEMV_FMT_Q4_K>& a, int u, int) {
         int D[2];
-        Q4K::dots(w, x, D);
+        Q4K::dots(w, a.x, D);
         const float fd = h2f(w.hdr.x & 0xFFFFu), fdm = h2f(w.hdr.x >> 16);
         const int c = u & 3;
         float t = 0.0f;
@@ -112,75 +141,289 @@ __device__ __forceinline__ float unit_term(const uint8_t* __restrict__ rp, int u
         for (int jj = 0; jj < 2; jj++) {
             int sc, mn;
             Q4K::scale_min(w, 2 * c + jj, sc, mn);
-            const int b = 2 * u + jj;
-            t = fmaf((float)D[jj], fd * (float)sc * A.dx[b], t);
-            t = fmaf(-(fdm * (float)mn), A.dxs[b], t);
+            t = fmaf((float)D[jj], fd * (float)sc * a.dx[jj], t);
+            t = fmaf(-(fdm * (float)mn), a.dxs[jj], t);
         }
         return t;
-    } else if constexpr (FMT == QGEMV_FMT_Q6_K) {
-        Q6K::W w;
-        Q6K::load(rp, u, w);
-        lds_act_q6k(A.codes, u, x);
-        int init[4], D[4];
-#pragma unroll
-        for (int j = 0; j < 4; j++) init[j] = A.init[Q6K::act_offset(u, j) >> 4];
-        Q6K::dots(w, x, init, D);
+    }
+};
+template <>
+struct Unit<QGEMV_FMT_Q6_K> {
+    using W = Q6K::W;
+    __device__ static void load(const uint8_t* rp, int u, bool, W& w) { Q6K::load(rp, u, w); }
+    __device__ static float term(const W& w, const ActReg<QGEMV_FMT_Q6_K>& a, int u, int) {
+        int D[4];
+        Q6K::dots(w, a.x, a.init, D);
         const float fd = h2f(w.d);
         float t = 0.0f;
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
-            const int b = Q6K::act_offset(u, j) >> 5;
-            t = fmaf((float)D[j], fd * (float)Q6K::scale(w, u, j) * A.dx[b], t);
-        }
-        return t;
-    } else if constexpr (FMT == QGEMV_FMT_Q4_0) {
-        const bool has1 = 2 * u + 1 < nbw;
-        Q40::W w;
-        Q40::load(rp, u, has1, w);
-        lds_act64(A.codes, 64 * u, x);
-        int init[2] = {A.init[2 * u], A.init[2 * u + 1]}, D[2];
-        Q40::dots(w, x, init, D);
-        float t = (float)D[0] * (h2f(w.d0) * A.dx[2 * u]);
-        if (has1) t = fmaf((float)D[1], h2f(w.d1) * A.dx[2 * u + 1], t);
-        return t;
-    } else {
-        const bool has1 = 2 * u + 1 < nbw;
-        Q80::W w;
-        Q80::load(rp, u, has1, w);
-        lds_act64(A.codes, 64 * u, x);
-        int D[2];
-        Q80::dots(w, x, D);
-        float t = (float)D[0] * (h2f(w.d0) * A.dx[2 * u]);
-        if (has1) t = fmaf((float)D[1], h2f(w.d1) * A.dx[2 * u + 1], t);
+        for (int j = 0; j < 4; j++)
+            t = fmaf((float)D[j], fd * (float)Q6K::scale(w, u, j) * a.dx[j], t);
         return t;
     }
+};
+template <>
+struct Unit<QGEMV_FMT_Q4_0> {
+    using W = Q40::W;
+    __device__ static void load(const uint8_t* rp, int u, bool has1, W& w) {
+        Q40::load(rp, u, has1, w);
+    }
+    __device__ static float term(const W& w, const ActReg<QGEMV_FMT_Q4_0>& a, int, int) {
+        int D[2];
+        Q40::dots(w, a.x, a.init, D);
+        // a missing second block has d1 = 0, so its term is exactly zero
+        return fmaf((float)D[1], h2f(w.d1) * a.dx[1], (float)D[0] * (h2f(w.d0) * a.dx[0]));
+    }
+};
+template <>
+struct Unit<QGEMV_FMT_Q8_0> {
+    using W = Q80::W;
+    __device__ static void load(const uint8_t* rp, int u, bool has1, W& w) {
+        Q80::load(rp, u, has1, w);
+    }
+    __device__ static float term(const W& w, const ActReg<QGEMV_FMT_Q8_0>& a, int, int) {
+        int D[2];
+        Q80::dots(w, a.x, D);
+        return fmaf((float)D[1], h2f(w.d1) * a.dx[1], (float)D[0] * (h2f(w.d0) * a.dx[0]));
+    }
+};
+
+// Byte offset of unit u within a row of the format.
+template <int FMT>
+__device__ __forceinline__ int unit_byte(int u) {
+    if constexpr (FMT == QGEMV_FMT_Q4_K) return (u >> 2) * Q4K::SB_BYTES;  // u % 4 == 0
+    else if constexpr (FMT == QGEMV_FMT_Q6_K) return (u >> 2) * Q6K::SB_BYTES;
+    else if constexpr (FMT == QGEMV_FMT_Q4_0) return u * 2 * Q40::BLK_BYTES;
+    else return u * 2 * Q80::BLK_BYTES;
 }
 
-// One workgroup = 4 waves; wave-iteration it handles rows
-// base + it*4*RPW + wave*RPW + lane/LPR, for it < R.
-template <int FMT, int LPR>
-__global__ __launch_bounds__(WG) void k_gemv(const uint8_t* __restrict__ w, int N, int Kp,
-                                              int U, int nbw, int row_bytes,
+constexpr int SEGP = 64;  // passes whose split-K partial sums are buffered in LDS
+
+// Persistent GEMV.  The grid is sized to the number of workgroups that fit
+// on the chip at once.  The rows are cut into groups of RPP consecutive rows
+// (one group per workgroup pass) and the groups are dealt round-robin over the
+// workgroups, so at any moment the whole chip streams one contiguous window of
+// the weight matrix (measured faster on MI355X than giving each workgroup a
+// contiguous slab).  Inside a workgroup the 4 waves form 4/WK row groups; the
+// WK waves of a group split the row's units into WK contiguous slices
+// (split-K for long rows) whose partial sums meet in LDS.  Lane li of a wave
+// covers the units u = slice_start + li + LPR*i (i < UPL) of every row it
+// visits, so its activation lives in registers for the whole kernel.  Two row
+// buffers are used in turn: the next row's loads are in flight while the
+// current row is computed.
+template <int FMT, int LPR, int UPL, int WK>
+__global__ __launch_bounds__(WG) void k_gemv(const uint8_t* __restrict__ w, int N, int U,
+                                              int nbw, int row_bytes,
                                               const int8_t* __restrict__ q,
                                               const uint16_t* __restrict__ d,
                                               const int32_t* __restrict__ s,
-                                              float* __restrict__ y, int R) {
-    extern __shared__ __align__(16) uint8_t smem[];
-    const ActSmem A = stage_act<FMT>(smem, q, d, s, Kp);
+                                              float* __restrict__ y) {
+    static_assert(WK == 1 || LPR == 64, "split-K needs whole waves per row");
     constexpr int RPW = 64 / LPR;
+    constexpr int NRG = 4 / WK;
+    constexpr int RPP = NRG * RPW;  // rows per workgroup pass (one row group)
+    __shared__ float part[WK > 1 ? SEGP * RPP * WK : 1];
+    using UnitT = Unit<FMT>;
+    using WT = typename UnitT::W;
+
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int li = lane % LPR;
-    const int64_t base = (int64_t)blockIdx.x * R * 4 * RPW + wave * RPW + lane / LPR;
-    for (int it = 0; it < R; it++) {
-        const int64_t row = base + (int64_t)it * 4 * RPW;
-        float acc = 0.0f;
-        if (row < N) {
-            const uint8_t* rp = w + row * (int64_t)row_bytes;
-            for (int u = li; u < U; u += LPR) acc += unit_term<FMT>(rp, u, nbw, A);
-        }
+    const int kq = wave % WK, rg = wave / WK;
+    const int li = lane % LPR, sub = lane / LPR;
+    const int US = (U + WK - 1) / WK;
+    const int u_lo = kq * US;
+    const int u_hi = min(U, u_lo + US);
+
+    // Lanes past the end of their slice repeat the slice's last unit (so every
+    // load is unconditional and in bounds) and drop its contribution.
+    ActReg<FMT> A[UPL];
+    int uu[UPL];
+    bool ok[UPL];
 #pragma unroll
-        for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, LPR);
-        if (li == 0 && row < N) y[row] = acc;
+    for (int i = 0; i < UPL; i++) {
+        const int u = u_lo + li + LPR * i;
+        ok[i] = u < u_hi;
+        uu[i] = ok[i] ? u : u_hi - 1;
+        A[i].load(q, d, s, uu[i]);
+    }
+
+    const int my_off = rg * RPW + sub;  // this lane's row within a group
+    const int64_t G = gridDim.x;
+    const int64_t ngroups = ((int64_t)N + RPP - 1) / RPP;
+    // row of pass p (passes counted from this workgroup's first group)
+    auto row_of = [&](int64_t p) { return (blockIdx.x + p * G) * RPP + my_off; };
+    // Rows past N reload row N-1: loads never sit under a lane-dependent
+    // branch, so the compiler waits for exactly the loads a row needs while
+    // the next row's loads stay in flight.
+    auto load_row = [&](WT (&wv)[UPL], int64_t row) {
+        const uint8_t* rp = w + min(row, (int64_t)N - 1) * (int64_t)row_bytes;
+#pragma unroll
+        for (int i = 0; i < UPL; i++) UnitT::load(rp, uu[i], 2 * uu[i] + 1 < nbw, wv[i]);
+    };
+    // Dot one loaded row and reduce it over the row's lanes; the row sum (or
+    // this wave's split-K part of it) is valid in lane li == LPR - 1.
+    auto dot_row = [&](const WT (&wv)[UPL]) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int i = 0; i < UPL; i++) {
+            const float t = UnitT::term(wv[i], A[i], uu[i], nbw);
+            acc += ok[i] ? t : 0.0f;
+        }
+        return group_sum<LPR>(acc);
+    };
+    auto finish_row = [&](float acc, int64_t row, int pl) {
+        if (li == LPR - 1 && row < N) {
+            if constexpr (WK == 1) y[row] = acc;
+            else part[(pl * RPP + my_off) * WK + kq] = acc;
+        }
+    };
+
+    const int64_t npass_all = ngroups > (int64_t)blockIdx.x
+                                  ? (ngroups - blockIdx.x + G - 1) / G : 0;
+    for (int64_t p0 = 0; p0 < npass_all; p0 += SEGP) {
+        const int np = (int)min((int64_t)SEGP, npass_all - p0);
+        WT wa[UPL], wb[UPL];
+        load_row(wa, row_of(p0));
+        // (sched_barrier keeps the compiler from sinking a row's loads below
+        // the wait for the previous row.)
+        for (int p = 0; p < np; p += 2) {
+            load_row(wb, row_of(p0 + p + 1));
+            __builtin_amdgcn_sched_barrier(0);
+            finish_row(dot_row(wa), row_of(p0 + p), p);
+            load_row(wa, row_of(p0 + p + 2));
+            __builtin_amdgcn_sched_barrier(0);
+            if (p + 1 < np) finish_row(dot_row(wb), row_of(p0 + p + 1), p + 1);
+        }
+        if constexpr (WK > 1) {
+            __syncthreads();
+            for (int t = threadIdx.x; t < np * RPP; t += WG) {
+                const int64_t row = (blockIdx.x + (p0 + t / RPP) * G) * RPP + t % RPP;
+                if (row < N) {
+                    float v = part[t * WK];
+#pragma unroll
+                    for (int k = 1; k < WK; k++) v += part[t * WK + k];
+                    y[row] = v;
+                }
+            }
+            __syncthreads();
+        }
+    }
+}
+
+// LDS-streaming GEMV (whole waves per row, LPR = 64).  Same work split as
+// k_gemv, but a wave brings its slice of a row in with fully coalesced loads
+// -- lane i fetches 16-byte chunk i, i + 64, ... of the slice, so each wave
+// instruction reads 1 KB of consecutive bytes -- and parks it in its own LDS
+// buffer; the lanes then read their units' fields from LDS.  The last chunk
+// is shifted back to end exactly at the slice end (it overlaps its
+// neighbour; both write the same bytes), so no load leaves the row.  Two rows
+// are in flight in registers while a third is computed from LDS.
+template <int FMT, int UPL, int WK, int NL, bool NT>
+__global__ __launch_bounds__(WG) void k_gemv_lds(const uint8_t* __restrict__ w, int N, int U,
+                                                  int US, int nbw, int row_bytes, int buf_bytes,
+                                                  const int8_t* __restrict__ q,
+                                                  const uint16_t* __restrict__ d,
+                                                  const int32_t* __restrict__ s,
+                                                  float* __restrict__ y) {
+    extern __shared__ __align__(16) uint8_t lds[];
+    constexpr int LPR = 64;
+    constexpr int RPP = 4 / WK;
+    __shared__ float part[WK > 1 ? SEGP * RPP * WK : 1];
+    using UnitT = Unit<FMT>;
+    using WT = typename UnitT::W;
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int kq = wave % WK, rg = wave / WK;
+    const int u_lo = kq * US;
+    const int u_hi = min(U, u_lo + US);
+    const int sbeg = unit_byte<FMT>(u_lo);
+    const int slen = min(unit_byte<FMT>(u_hi), row_bytes) - sbeg;
+    const int nchunk = (slen + 15) >> 4;
+
+    ActReg<FMT> A[UPL];
+    int ul[UPL];
+    bool ok[UPL], has1[UPL];
+#pragma unroll
+    for (int i = 0; i < UPL; i++) {
+        const int u = u_lo + lane + LPR * i;
+        ok[i] = u < u_hi;
+        const int uc = ok[i] ? u : u_hi - 1;
+        A[i].load(q, d, s, uc);
+        ul[i] = uc - u_lo;
+        has1[i] = 2 * uc + 1 < nbw;
+    }
+    int coff[NL];  // byte offsets (within the slice) of this lane's chunks
+#pragma unroll
+    for (int k = 0; k < NL; k++) coff[k] = min(16 * min(lane + 64 * k, nchunk - 1), slen - 16);
+
+    uint8_t* buf0 = lds + (2 * wave) * buf_bytes;
+    uint8_t* buf1 = buf0 + buf_bytes;
+    const int64_t G = gridDim.x;
+    const int64_t ngroups = ((int64_t)N + RPP - 1) / RPP;
+    auto row_of = [&](int64_t p) { return (blockIdx.x + p * G) * RPP + rg; };
+    auto stage = [&](u32x4 (&R)[NL], int64_t row) {
+        const uint8_t* rp = w + min(row, (int64_t)N - 1) * (int64_t)row_bytes + sbeg;
+#pragma unroll
+        for (int k = 0; k < NL; k++) R[k] = ld16_stream<NT>(rp + coff[k]);
+    };
+    auto commit = [&](const u32x4 (&R)[NL], uint8_t* buf) {
+#pragma unroll
+        for (int k = 0; k < NL; k++) st16(buf + coff[k], R[k]);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
+    auto dot_row = [&](const uint8_t* buf) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int i = 0; i < UPL; i++) {
+            WT wv;
+            UnitT::load(buf, ul[i], has1[i], wv);
+            const float t = UnitT::term(wv, A[i], u_lo + ul[i], nbw);
+            acc += ok[i] ? t : 0.0f;
+        }
+        return group_sum<LPR>(acc);
+    };
+    auto finish_row = [&](float acc, int64_t row, int pl) {
+        if (lane == LPR - 1 && row < N) {
+            if constexpr (WK == 1) y[row] = acc;
+            else part[(pl * RPP + rg) * WK + kq] = acc;
+        }
+    };
+
+    const int64_t npass_all = ngroups > (int64_t)blockIdx.x
+                                  ? (ngroups - blockIdx.x + G - 1) / G : 0;
+    for (int64_t p0 = 0; p0 < npass_all; p0 += SEGP) {
+        const int np = (int)min((int64_t)SEGP, npass_all - p0);
+        u32x4 Ra[NL], Rb[NL];
+        stage(Ra, row_of(p0));
+        commit(Ra, buf0);
+        stage(Ra, row_of(p0 + 1));
+        __builtin_amdgcn_sched_barrier(0);
+        stage(Rb, row_of(p0 + 2));
+        __builtin_amdgcn_sched_barrier(0);
+        for (int p = 0; p < np; p += 2) {
+            finish_row(dot_row(buf0), row_of(p0 + p), p);
+            commit(Ra, buf1);
+            stage(Ra, row_of(p0 + p + 3));
+            __builtin_amdgcn_sched_barrier(0);
+            if (p + 1 < np) finish_row(dot_row(buf1), row_of(p0 + p + 1), p + 1);
+            commit(Rb, buf0);
+            stage(Rb, row_of(p0 + p + 4));
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (WK > 1) {
+            __syncthreads();
+            for (int t = threadIdx.x; t < np * RPP; t += WG) {
+                const int64_t row = (blockIdx.x + (p0 + t / RPP) * G) * RPP + t % RPP;
+                if (row < N) {
+                    float v = part[t * WK];
+#pragma unroll
+                    for (int k = 1; k < WK; k++) v += part[t * WK + k];
+                    y[row] = v;
+                }
+            }
+            __syncthreads();
+        }
     }
 }
 
@@ -271,37 +514,154 @@ static int units_of(int fmt, int64_t K) {
     return (int)((K + 63) / 64);
 }
 
-template <int FMT, int LPR>
-static hipError_t launch_gemv_lpr(const GemvArgs& a, int U, int Kp, hipStream_t st) {
-    constexpr int RPW = 64 / LPR;
-    const int64_t rows_per_pass = 4LL * RPW;
-    // Rows per wave: enough workgroups to fill the chip several times over
-    // (about 2048), more rows per wave only when N is large.
-    int64_t passes = (a.N + rows_per_pass - 1) / rows_per_pass;
-    int R = (int)(passes / 2048);
-    if (R < 1) R = 1;
-    if (R > 16) R = 16;
-    const int64_t grid = (passes + R - 1) / R;
-    const int smem = smem_bytes(FMT, Kp);
-    hipLaunchKernelGGL((k_gemv<FMT, LPR>), dim3((unsigned)grid), dim3(WG), smem, st,
-                       (const uint8_t*)a.w, (int)a.N, Kp, U, (int)(a.K / 32),
-                       row_bytes_of(FMT, a.K), a.q, a.d, a.s, a.y, R);
+// Workgroups of one kernel instantiation that fit on the device at once
+// (occupancy x compute units), cached per device.
+template <int FMT, int LPR, int UPL, int WK>
+static int resident_workgroups() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1024;
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_gemv<FMT, LPR, UPL, WK>, WG, 0) !=
+            hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        per_cu <= 0 || cus <= 0) {
+        (void)hipGetLastError();
+        return 1024;
+    }
+    v = per_cu * cus;
+    cache[dev].store(v, std::memory_order_relaxed);
+    return v;
+}
+
+template <int FMT, int LPR, int UPL, int WK>
+static hipError_t launch_gemv_cfg(const GemvArgs& a, int U, hipStream_t st) {
+    constexpr int RPP = (4 / WK) * (64 / LPR);
+    const int64_t ngroups = (a.N + RPP - 1) / RPP;
+    // as many workgroups as fit at once, then evened out so that every
+    // workgroup gets the same number of passes (to within one)
+    const int64_t resident = resident_workgroups<FMT, LPR, UPL, WK>();
+    const int64_t passes = (ngroups + resident - 1) / resident;
+    const int64_t grid = (ngroups + passes - 1) / passes;
+    hipLaunchKernelGGL((k_gemv<FMT, LPR, UPL, WK>), dim3((unsigned)grid), dim3(WG), 0, st,
+                       (const uint8_t*)a.w, (int)a.N, U, (int)(a.K / 32), row_bytes_of(FMT, a.K),
+                       a.q, a.d, a.s, a.y);
     return hipGetLastError();
+}
+
+// Selection of the LDS-streaming kernels (rows of at least 33 units) and of
+// their non-temporal weight loads.
+constexpr bool kLdsStream = true;
+constexpr bool kStreamNT = true;
+
+template <int FMT, int UPL, int WK, int NL>
+static int resident_workgroups_lds(int smem) {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1024;
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, k_gemv_lds<FMT, UPL, WK, NL, kStreamNT>, WG, smem) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        per_cu <= 0 || cus <= 0) {
+        (void)hipGetLastError();
+        return 1024;
+    }
+    v = per_cu * cus;
+    cache[dev].store(v, std::memory_order_relaxed);
+    return v;
+}
+
+template <int FMT, int UPL, int WK, int NL>
+static hipError_t launch_lds_cfg(const GemvArgs& a, int U, int US, int buf_bytes,
+                                 hipStream_t st) {
+    constexpr int RPP = 4 / WK;
+    const int smem = 8 * buf_bytes;  // 4 waves x 2 buffers
+    const int64_t ngroups = (a.N + RPP - 1) / RPP;
+    const int64_t resident = resident_workgroups_lds<FMT, UPL, WK, NL>(smem);
+    const int64_t passes = (ngroups + resident - 1) / resident;
+    const int64_t grid = (ngroups + passes - 1) / passes;
+    hipLaunchKernelGGL((k_gemv_lds<FMT, UPL, WK, NL, kStreamNT>), dim3((unsigned)grid), dim3(WG),
+                       smem, st, (const uint8_t*)a.w, (int)a.N, U, US, (int)(a.K / 32),
+                       row_bytes_of(FMT, a.K), buf_bytes, a.q, a.d, a.s, a.y);
+    return hipGetLastError();
+}
+
+// Host mirror of unit_byte<FMT>().
+static int unit_byte_host(int fmt, int u) {
+    switch (fmt) {
+    case QGEMV_FMT_Q4_K: return (u / 4) * 144;
+    case QGEMV_FMT_Q6_K: return (u / 4) * 210;
+    case QGEMV_FMT_Q4_0: return u * 36;
+    default: return u * 68;
+    }
+}
+
+template <int FMT, int UPL, int WK>
+static hipError_t launch_lds_wk(const GemvArgs& a, int U, hipStream_t st) {
+    const bool kquant = (FMT == QGEMV_FMT_Q4_K || FMT == QGEMV_FMT_Q6_K);
+    int US = (U + WK - 1) / WK;
+    if (kquant) US = (US + 3) / 4 * 4;  // slices start at super-block boundaries
+    const int rb = row_bytes_of(FMT, a.K);
+    int max_slen = 0;
+    for (int kq = 0; kq < WK; kq++) {
+        const int lo = kq * US;
+        if (lo >= U) break;
+        const int hi = lo + US < U ? lo + US : U;
+        int e = unit_byte_host(FMT, hi);
+        if (e > rb) e = rb;
+        const int len = e - unit_byte_host(FMT, lo);
+        if (len > max_slen) max_slen = len;
+    }
+    const int buf_bytes = (max_slen + 15) / 16 * 16;
+    const int nchunk = (max_slen + 15) / 16;
+    const int nl = (nchunk + 63) / 64;  // 16-byte chunks per lane
+    if (nl <= 2) return launch_lds_cfg<FMT, UPL, WK, 2>(a, U, US, buf_bytes, st);
+    if (nl <= 3) return launch_lds_cfg<FMT, UPL, WK, 3>(a, U, US, buf_bytes, st);
+    if (nl <= 4) return launch_lds_cfg<FMT, UPL, WK, 4>(a, U, US, buf_bytes, st);
+    if (nl <= 6) return launch_lds_cfg<FMT, UPL, WK, 6>(a, U, US, buf_bytes, st);
+    return launch_lds_cfg<FMT, UPL, WK, 8>(a, U, US, buf_bytes, st);
+}
+
+// Largest slice (bytes) the LDS-streaming kernels take: at most 8 chunks of
+// 16 bytes per lane, and 8 slice buffers within 64 KB of LDS.
+constexpr int kMaxLdsSlice = 8 * 64 * 16;
+
+template <int FMT, int WK>
+static bool lds_slice_fits(int64_t K, int U) {
+    const bool kquant = (FMT == QGEMV_FMT_Q4_K || FMT == QGEMV_FMT_Q6_K);
+    int US = (U + WK - 1) / WK;
+    if (kquant) US = (US + 3) / 4 * 4;
+    const int len = unit_byte_host(FMT, US < U ? US : U);
+    return len <= kMaxLdsSlice && 8 * ((len + 15) / 16 * 16) <= 65536 - 4096;
 }
 
 template <int FMT>
 static hipError_t launch_gemv_fmt(const GemvArgs& a, hipStream_t st) {
     const int U = units_of(FMT, a.K);
-    const int Kp = (int)((a.K + 255) / 256 * 256);
-    if (U > 32) return launch_gemv_lpr<FMT, 64>(a, U, Kp, st);
-    if (U > 16) return launch_gemv_lpr<FMT, 32>(a, U, Kp, st);
-    if (U > 8) return launch_gemv_lpr<FMT, 16>(a, U, Kp, st);
-    if (U > 4) return launch_gemv_lpr<FMT, 8>(a, U, Kp, st);
-    return launch_gemv_lpr<FMT, 4>(a, U, Kp, st);
-}
-
-int gemv_smem_bytes(int fmt, int64_t K) {
-    return smem_bytes(fmt, (int)((K + 255) / 256 * 256));
+    if (kLdsStream && U > 32) {
+        if (U > 256) {
+            if (lds_slice_fits<FMT, 4>(a.K, U)) return launch_lds_wk<FMT, 2, 4>(a, U, st);
+        } else if (U > 128) {
+            if (lds_slice_fits<FMT, 4>(a.K, U)) return launch_lds_wk<FMT, 1, 4>(a, U, st);
+        } else if (U > 64) {
+            if (lds_slice_fits<FMT, 2>(a.K, U)) return launch_lds_wk<FMT, 1, 2>(a, U, st);
+        } else if (lds_slice_fits<FMT, 1>(a.K, U)) {
+            return launch_lds_wk<FMT, 1, 1>(a, U, st);
+        }
+    }
+    if (U > 256) return launch_gemv_cfg<FMT, 64, 2, 4>(a, U, st);
+    if (U > 128) return launch_gemv_cfg<FMT, 64, 1, 4>(a, U, st);
+    if (U > 64) return launch_gemv_cfg<FMT, 64, 1, 2>(a, U, st);
+    if (U > 32) return launch_gemv_cfg<FMT, 64, 1, 1>(a, U, st);
+    if (U > 16) return launch_gemv_cfg<FMT, 32, 1, 1>(a, U, st);
+    if (U > 8) return launch_gemv_cfg<FMT, 16, 1, 1>(a, U, st);
+    if (U > 4) return launch_gemv_cfg<FMT, 8, 1, 1>(a, U, st);
+    return launch_gemv_cfg<FMT, 4, 1, 1>(a, U, st);
 }
 
 hipError_t launch_gemv(int fmt, const GemvArgs& a, hipStream_t st) {

@@ -15,7 +15,7 @@
 #include <cstdio>
 #include <cstring>
 
-#include "../../include/qgemv.h"
+#include "qgemv.h"
 #include "qgemv_launch.h"
 
 namespace {

@@ -26,23 +26,39 @@ namespace qgemv {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-// Byte-addressed loads.  memcpy lets the compiler emit one dwordx4 / dwordx2
-// load even when the address is only 2-byte aligned (Q6_K super-blocks start
-// at 210*S, Q4_0 blocks at 18*b); the HSA runtime runs in unaligned mode.
+// Loads of packed weight bytes.  The vector types carry 2-byte alignment so
+// that one dwordx4 / dwordx2 load is emitted even where the address is only
+// 2-byte aligned (Q6_K super-blocks start at 210*S, Q4_0 blocks at 18*b); the
+// HSA runtime runs the memory system in unaligned mode.  These are ordinary
+// (temporal) loads on purpose: one wave instruction covers only part of each
+// cache line and sibling instructions read the rest, so the line has to stay
+// in cache until they do (a non-temporal hint made the lines re-fetch).
+typedef uint32_t u32x4_a2 __attribute__((ext_vector_type(4), aligned(2)));
+typedef uint32_t u32x2_a2 __attribute__((ext_vector_type(2), aligned(2)));
+
 __device__ __forceinline__ u32x4 ld16(const uint8_t* p) {
-    u32x4 v;
-    __builtin_memcpy(&v, p, 16);
-    return v;
+    const u32x4_a2 v = *reinterpret_cast<const u32x4_a2*>(p);
+    return u32x4{v.x, v.y, v.z, v.w};
 }
 __device__ __forceinline__ u32x2 ld8(const uint8_t* p) {
-    u32x2 v;
-    __builtin_memcpy(&v, p, 8);
-    return v;
+    const u32x2_a2 v = *reinterpret_cast<const u32x2_a2*>(p);
+    return u32x2{v.x, v.y};
 }
 __device__ __forceinline__ uint32_t ld2(const uint8_t* p) {
-    uint16_t v;
-    __builtin_memcpy(&v, p, 2);
-    return v;
+    return *reinterpret_cast<const uint16_t*>(p);
+}
+
+// A 16-byte chunk of a weight row for the LDS-staged kernels: one wave
+// instruction covers 1 KB of consecutive bytes, so whole cache lines are
+// consumed by one instruction and the non-temporal hint is safe there.
+template <bool NT>
+__device__ __forceinline__ u32x4 ld16_stream(const uint8_t* p) {
+    const u32x4_a2 v = NT ? __builtin_nontemporal_load(reinterpret_cast<const u32x4_a2*>(p))
+                          : *reinterpret_cast<const u32x4_a2*>(p);
+    return u32x4{v.x, v.y, v.z, v.w};
+}
+__device__ __forceinline__ void st16(uint8_t* p, u32x4 v) {
+    *reinterpret_cast<u32x4_a2*>(p) = u32x4_a2{v.x, v.y, v.z, v.w};
 }
 
 __device__ __forceinline__ float h2f(uint32_t bits) {
@@ -195,18 +211,17 @@ struct Q40 {
         u32x4 q0, q1;
         uint32_t d0, d1;
     };
-    // has1: whether block 2u+1 exists (row has an odd number of blocks).
+    // has1: whether block 2u+1 exists (the row may hold an odd number of
+    // blocks).  A missing block re-reads block 2u (always in bounds, no
+    // branch around the load) and gets d1 = 0, so its term is exactly zero.
     __device__ static __forceinline__ void load(const uint8_t* row, int u, bool has1, W& w) {
         const uint8_t* p = row + 2 * BLK_BYTES * u;
+        const uint8_t* p1 = has1 ? p + BLK_BYTES : p;
         w.d0 = ld2(p);
         w.q0 = ld16(p + 2);
-        if (has1) {
-            w.d1 = ld2(p + 18);
-            w.q1 = ld16(p + 20);
-        } else {
-            w.d1 = 0;
-            w.q1 = u32x4{0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u};
-        }
+        const uint32_t d1 = ld2(p1);
+        w.d1 = has1 ? d1 : 0u;
+        w.q1 = ld16(p1 + 2);
     }
     // Block 2u is a[0..7], block 2u+1 is a[8..15]; init = -8 * s_b folds the
     // code offset into the accumulator: D = sum (code - 8) * q.
@@ -233,19 +248,17 @@ struct Q80 {
         u32x4 a0, b0, a1, b1;
         uint32_t d0, d1;
     };
+    // A missing second block re-reads block 2u and gets d1 = 0 (see Q40).
     __device__ static __forceinline__ void load(const uint8_t* row, int u, bool has1, W& w) {
         const uint8_t* p = row + 2 * BLK_BYTES * u;
+        const uint8_t* p1 = has1 ? p + BLK_BYTES : p;
         w.d0 = ld2(p);
         w.a0 = ld16(p + 2);
         w.b0 = ld16(p + 18);
-        if (has1) {
-            w.d1 = ld2(p + 34);
-            w.a1 = ld16(p + 36);
-            w.b1 = ld16(p + 52);
-        } else {
-            w.d1 = 0;
-            w.a1 = w.b1 = u32x4{0u, 0u, 0u, 0u};
-        }
+        const uint32_t d1 = ld2(p1);
+        w.d1 = has1 ? d1 : 0u;
+        w.a1 = ld16(p1 + 2);
+        w.b1 = ld16(p1 + 18);
     }
     __device__ static __forceinline__ void dots(const W& w, const Act16& x, int D[2]) {
         int d0 = 0, d1 = 0;

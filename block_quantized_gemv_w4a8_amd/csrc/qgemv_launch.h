@@ -6,7 +6,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "../../include/qgemv.h"
+#include "qgemv.h"
 
 namespace qgemv {
 
@@ -19,7 +19,6 @@ struct GemvArgs {
     float* y;
 };
 
-int gemv_smem_bytes(int fmt, int64_t K);
 hipError_t launch_gemv(int fmt, const GemvArgs& a, hipStream_t st);
 hipError_t launch_block_dots(int fmt, const void* w, int64_t K, int64_t row0, int64_t nrows,
                              const int8_t* q, int32_t* dots, hipStream_t st);
