@@ -188,15 +188,6 @@ struct Unit<QGEMV_FMT_Q8_0> {
     }
 };
 
-// Byte offset of unit u within a row of the format.
-template <int FMT>
-__device__ __forceinline__ int unit_byte(int u) {
-    if constexpr (FMT == QGEMV_FMT_Q4_K) return (u >> 2) * Q4K::SB_BYTES;  // u % 4 == 0
-    else if constexpr (FMT == QGEMV_FMT_Q6_K) return (u >> 2) * Q6K::SB_BYTES;
-    else if constexpr (FMT == QGEMV_FMT_Q4_0) return u * 2 * Q40::BLK_BYTES;
-    else return u * 2 * Q80::BLK_BYTES;
-}
-
 constexpr int SEGP = 64;  // passes whose split-K partial sums are buffered in LDS
 
 // Persistent GEMV.  The grid is sized to the number of workgroups that fit
@@ -309,14 +300,116 @@ __global__ __launch_bounds__(WG) void k_gemv(const uint8_t* __restrict__ w, int 
     }
 }
 
+// Unit loaders for the LDS-streaming kernel.  The slice of a row sits in LDS
+// in its original byte order, starting `off0` bytes into the buffer (the
+// chunk grid is aligned to 16-byte global addresses, see k_gemv_lds).  Q4_K
+// fields are 16-byte aligned there; Q6_K, Q4_0 and Q8_0 blocks start every
+// 210, 18 or 34 bytes, so their fields can sit 2 bytes off a 4-byte boundary.
+// Those are read as aligned dwords and shifted into place with v_alignbyte:
+// unaligned LDS accesses stall the LDS pipeline on this chip, aligned dword
+// reads do not.
+__device__ __forceinline__ u32x4 lds16(const uint8_t* base, int off) {
+    return *reinterpret_cast<const u32x4*>(base + off);
+}
+__device__ __forceinline__ uint32_t lds2(const uint8_t* base, int off) {
+    return *reinterpret_cast<const uint16_t*>(base + off);
+}
+__device__ __forceinline__ uint32_t abyte(uint32_t hi, uint32_t lo, uint32_t sh) {
+    return __builtin_amdgcn_alignbyte(hi, lo, sh);
+}
+// 16 bytes at any even LDS offset (reads up to 4 bytes past the field).
+__device__ __forceinline__ u32x4 lds16_a2(const uint8_t* base, int off) {
+    const uint32_t* d = reinterpret_cast<const uint32_t*>(base + (off & ~3));
+    const uint32_t sh = off & 3;
+    const uint32_t w0 = d[0], w1 = d[1], w2 = d[2], w3 = d[3], w4 = d[4];
+    return u32x4{abyte(w1, w0, sh), abyte(w2, w1, sh), abyte(w3, w2, sh), abyte(w4, w3, sh)};
+}
+// 8 bytes at any even LDS offset.
+__device__ __forceinline__ u32x2 lds8_a2(const uint8_t* base, int off) {
+    const uint32_t* d = reinterpret_cast<const uint32_t*>(base + (off & ~3));
+    const uint32_t sh = off & 3;
+    const uint32_t w0 = d[0], w1 = d[1], w2 = d[2];
+    return u32x2{abyte(w1, w0, sh), abyte(w2, w1, sh)};
+}
+
+template <int FMT>
+struct UnitLds;
+template <>
+struct UnitLds<QGEMV_FMT_Q4_K> {
+    static constexpr int UNITS_PER_BLK = 4, BLK_BYTES = 144;
+    // (super-blocks are 144 = 9 x 16 bytes: the slice always starts aligned)
+    __device__ static void load(const uint8_t* b, int off0, int ul, bool, Q4K::W& w) {
+        const int p = off0 + 144 * (ul >> 2);
+        const int c = ul & 3;
+        w.hdr = lds16(b, p);
+        w.qa = lds16(b, p + 16 + 32 * c);
+        w.qb = lds16(b, p + 32 + 32 * c);
+    }
+};
+template <>
+struct UnitLds<QGEMV_FMT_Q6_K> {
+    static constexpr int UNITS_PER_BLK = 4, BLK_BYTES = 210;
+    __device__ static void load(const uint8_t* b, int off0, int ul, bool, Q6K::W& w) {
+        const int p = off0 + 210 * (ul >> 2);
+        const int h = (ul >> 1) & 1, t = ul & 1;
+        w.qa = lds16_a2(b, p + 64 * h + 16 * t);
+        w.qb = lds16_a2(b, p + 64 * h + 32 + 16 * t);
+        w.qh = lds16_a2(b, p + 128 + 32 * h + 16 * t);
+        w.sc = lds8_a2(b, p + 192 + 8 * h);
+        w.d = lds2(b, p + 208);
+    }
+};
+template <>
+struct UnitLds<QGEMV_FMT_Q4_0> {
+    static constexpr int UNITS_PER_BLK = 0, BLK_BYTES = 18;
+    // a missing second block re-reads the first one and gets d1 = 0
+    __device__ static void load(const uint8_t* b, int off0, int ul, bool has1, Q40::W& w) {
+        const int p0 = off0 + 36 * ul;
+        const int p1 = has1 ? p0 + 18 : p0;
+        w.d0 = lds2(b, p0);
+        w.q0 = lds16_a2(b, p0 + 2);
+        const uint32_t d1 = lds2(b, p1);
+        w.d1 = has1 ? d1 : 0u;
+        w.q1 = lds16_a2(b, p1 + 2);
+    }
+};
+template <>
+struct UnitLds<QGEMV_FMT_Q8_0> {
+    static constexpr int UNITS_PER_BLK = 0, BLK_BYTES = 34;
+    __device__ static void load(const uint8_t* b, int off0, int ul, bool has1, Q80::W& w) {
+        const int p0 = off0 + 68 * ul;
+        const int p1 = has1 ? p0 + 34 : p0;
+        w.d0 = lds2(b, p0);
+        w.a0 = lds16_a2(b, p0 + 2);
+        w.b0 = lds16_a2(b, p0 + 18);
+        const uint32_t d1 = lds2(b, p1);
+        w.d1 = has1 ? d1 : 0u;
+        w.a1 = lds16_a2(b, p1 + 2);
+        w.b1 = lds16_a2(b, p1 + 18);
+    }
+};
+
+// Byte offset of unit u within a row, and the first block of unit u.
+template <int FMT>
+__host__ __device__ inline int unit_byte(int u) {
+    if (FMT == QGEMV_FMT_Q4_K) return (u / 4) * 144;
+    if (FMT == QGEMV_FMT_Q6_K) return (u / 4) * 210;
+    if (FMT == QGEMV_FMT_Q4_0) return u * 36;
+    return u * 68;
+}
+
 // LDS-streaming GEMV (whole waves per row, LPR = 64).  Same work split as
 // k_gemv, but a wave brings its slice of a row in with fully coalesced loads
-// -- lane i fetches 16-byte chunk i, i + 64, ... of the slice, so each wave
-// instruction reads 1 KB of consecutive bytes -- and parks it in its own LDS
-// buffer; the lanes then read their units' fields from LDS.  The last chunk
-// is shifted back to end exactly at the slice end (it overlaps its
-// neighbour; both write the same bytes), so no load leaves the row.  Two rows
-// are in flight in registers while a third is computed from LDS.
+// -- lane i fetches the 16-byte chunk i, i + 64, ... of the slice, on a chunk
+// grid aligned to 16-byte global addresses, so each wave instruction reads
+// 1 KB of consecutive, aligned bytes (with the non-temporal hint, which is
+// safe because whole cache lines are consumed by one instruction) -- and
+// parks it in its own LDS buffer in the original byte order; the lanes then
+// read their units' fields from LDS.  The last chunk is shifted back to end
+// exactly at the slice end (it overlaps its neighbour; both write the same
+// bytes), so no load leaves the row.  Two rows are in flight in registers
+// while a third is computed from LDS.  Row results are parked in LDS and
+// written out together (one lane per row would issue a store per row).
 template <int FMT, int UPL, int WK, int NL, bool NT>
 __global__ __launch_bounds__(WG) void k_gemv_lds(const uint8_t* __restrict__ w, int N, int U,
                                                   int US, int nbw, int row_bytes, int buf_bytes,
@@ -327,9 +420,10 @@ __global__ __launch_bounds__(WG) void k_gemv_lds(const uint8_t* __restrict__ w, 
     extern __shared__ __align__(16) uint8_t lds[];
     constexpr int LPR = 64;
     constexpr int RPP = 4 / WK;
-    __shared__ float part[WK > 1 ? SEGP * RPP * WK : 1];
+    __shared__ float part[SEGP * RPP * WK];
     using UnitT = Unit<FMT>;
     using WT = typename UnitT::W;
+    using UL = UnitLds<FMT>;
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int kq = wave % WK, rg = wave / WK;
@@ -337,7 +431,6 @@ __global__ __launch_bounds__(WG) void k_gemv_lds(const uint8_t* __restrict__ w, 
     const int u_hi = min(U, u_lo + US);
     const int sbeg = unit_byte<FMT>(u_lo);
     const int slen = min(unit_byte<FMT>(u_hi), row_bytes) - sbeg;
-    const int nchunk = (slen + 15) >> 4;
 
     ActReg<FMT> A[UPL];
     int ul[UPL];
@@ -351,43 +444,44 @@ __global__ __launch_bounds__(WG) void k_gemv_lds(const uint8_t* __restrict__ w, 
         ul[i] = uc - u_lo;
         has1[i] = 2 * uc + 1 < nbw;
     }
-    int coff[NL];  // byte offsets (within the slice) of this lane's chunks
-#pragma unroll
-    for (int k = 0; k < NL; k++) coff[k] = min(16 * min(lane + 64 * k, nchunk - 1), slen - 16);
 
     uint8_t* buf0 = lds + (2 * wave) * buf_bytes;
     uint8_t* buf1 = buf0 + buf_bytes;
     const int64_t G = gridDim.x;
     const int64_t ngroups = ((int64_t)N + RPP - 1) / RPP;
     auto row_of = [&](int64_t p) { return (blockIdx.x + p * G) * RPP + rg; };
+    // offset (from the aligned chunk base) of this lane's k-th chunk
+    auto chunk_off = [&](int k, int delta) { return min(16 * (lane + 64 * k), delta + slen - 16); };
+    // Issue the loads of a row's slice; returns the slice's offset from the
+    // 16-byte-aligned address below it.
     auto stage = [&](u32x4 (&R)[NL], int64_t row) {
-        const uint8_t* rp = w + min(row, (int64_t)N - 1) * (int64_t)row_bytes + sbeg;
+        const uint8_t* a = w + min(row, (int64_t)N - 1) * (int64_t)row_bytes + sbeg;
+        const int delta = (int)((uintptr_t)a & 15);
+        const uint8_t* ab = a - delta;
 #pragma unroll
-        for (int k = 0; k < NL; k++) R[k] = ld16_stream<NT>(rp + coff[k]);
+        for (int k = 0; k < NL; k++) R[k] = ld16_stream<NT>(ab + chunk_off(k, delta));
+        return delta;
     };
-    auto commit = [&](const u32x4 (&R)[NL], uint8_t* buf) {
+    auto commit = [&](const u32x4 (&R)[NL], int delta, uint8_t* buf) {
 #pragma unroll
-        for (int k = 0; k < NL; k++) st16(buf + coff[k], R[k]);
+        for (int k = 0; k < NL; k++) st16(buf + chunk_off(k, delta), R[k]);
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     };
-    auto dot_row = [&](const uint8_t* buf) {
+    auto dot_row = [&](const uint8_t* buf, int delta) {
         float acc = 0.0f;
 #pragma unroll
         for (int i = 0; i < UPL; i++) {
             WT wv;
-            UnitT::load(buf, ul[i], has1[i], wv);
+            UL::load(buf, delta, ul[i], has1[i], wv);
             const float t = UnitT::term(wv, A[i], u_lo + ul[i], nbw);
             acc += ok[i] ? t : 0.0f;
         }
         return group_sum<LPR>(acc);
     };
-    auto finish_row = [&](float acc, int64_t row, int pl) {
-        if (lane == LPR - 1 && row < N) {
-            if constexpr (WK == 1) y[row] = acc;
-            else part[(pl * RPP + rg) * WK + kq] = acc;
-        }
+    auto finish_row = [&](float acc, int pl) {
+        if (lane == LPR - 1) part[(pl * RPP + rg) * WK + kq] = acc;
     };
 
     const int64_t npass_all = ngroups > (int64_t)blockIdx.x
@@ -395,35 +489,36 @@ __global__ __launch_bounds__(WG) void k_gemv_lds(const uint8_t* __restrict__ w, 
     for (int64_t p0 = 0; p0 < npass_all; p0 += SEGP) {
         const int np = (int)min((int64_t)SEGP, npass_all - p0);
         u32x4 Ra[NL], Rb[NL];
-        stage(Ra, row_of(p0));
-        commit(Ra, buf0);
-        stage(Ra, row_of(p0 + 1));
+        int da = stage(Ra, row_of(p0));
+        commit(Ra, da, buf0);
+        int d0 = da, d1;
+        da = stage(Ra, row_of(p0 + 1));
         __builtin_amdgcn_sched_barrier(0);
-        stage(Rb, row_of(p0 + 2));
+        int db = stage(Rb, row_of(p0 + 2));
         __builtin_amdgcn_sched_barrier(0);
         for (int p = 0; p < np; p += 2) {
-            finish_row(dot_row(buf0), row_of(p0 + p), p);
-            commit(Ra, buf1);
-            stage(Ra, row_of(p0 + p + 3));
+            finish_row(dot_row(buf0, d0), p);
+            commit(Ra, da, buf1);
+            d1 = da;
+            da = stage(Ra, row_of(p0 + p + 3));
             __builtin_amdgcn_sched_barrier(0);
-            if (p + 1 < np) finish_row(dot_row(buf1), row_of(p0 + p + 1), p + 1);
-            commit(Rb, buf0);
-            stage(Rb, row_of(p0 + p + 4));
+            if (p + 1 < np) finish_row(dot_row(buf1, d1), p + 1);
+            commit(Rb, db, buf0);
+            d0 = db;
+            db = stage(Rb, row_of(p0 + p + 4));
             __builtin_amdgcn_sched_barrier(0);
         }
-        if constexpr (WK > 1) {
-            __syncthreads();
-            for (int t = threadIdx.x; t < np * RPP; t += WG) {
-                const int64_t row = (blockIdx.x + (p0 + t / RPP) * G) * RPP + t % RPP;
-                if (row < N) {
-                    float v = part[t * WK];
+        __syncthreads();
+        for (int t = threadIdx.x; t < np * RPP; t += WG) {
+            const int64_t row = (blockIdx.x + (p0 + t / RPP) * G) * RPP + t % RPP;
+            if (row < N) {
+                float v = part[t * WK];
 #pragma unroll
-                    for (int k = 1; k < WK; k++) v += part[t * WK + k];
-                    y[row] = v;
-                }
+                for (int k = 1; k < WK; k++) v += part[t * WK + k];
+                y[row] = v;
             }
-            __syncthreads();
         }
+        __syncthreads();
     }
 }
 
@@ -576,13 +671,23 @@ static int resident_workgroups_lds(int smem) {
     return v;
 }
 
+// Workgroups per compute unit for the LDS-streaming kernels.  Measured on
+// MI355X: two workgroups (8 waves) per CU stream the Llama-shaped matrices
+// fastest; more waves add in-flight requests without adding bandwidth.
+constexpr int kLdsWgPerCu = 2;
+
 template <int FMT, int UPL, int WK, int NL>
 static hipError_t launch_lds_cfg(const GemvArgs& a, int U, int US, int buf_bytes,
                                  hipStream_t st) {
     constexpr int RPP = 4 / WK;
     const int smem = 8 * buf_bytes;  // 4 waves x 2 buffers
     const int64_t ngroups = (a.N + RPP - 1) / RPP;
-    const int64_t resident = resident_workgroups_lds<FMT, UPL, WK, NL>(smem);
+    int64_t resident = resident_workgroups_lds<FMT, UPL, WK, NL>(smem);
+    int cus = 0, dev = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        cus > 0 && resident > (int64_t)kLdsWgPerCu * cus)
+        resident = (int64_t)kLdsWgPerCu * cus;
     const int64_t passes = (ngroups + resident - 1) / resident;
     const int64_t grid = (ngroups + passes - 1) / passes;
     hipLaunchKernelGGL((k_gemv_lds<FMT, UPL, WK, NL, kStreamNT>), dim3((unsigned)grid), dim3(WG),
@@ -591,67 +696,63 @@ static hipError_t launch_lds_cfg(const GemvArgs& a, int U, int US, int buf_bytes
     return hipGetLastError();
 }
 
-// Host mirror of unit_byte<FMT>().
-static int unit_byte_host(int fmt, int u) {
-    switch (fmt) {
-    case QGEMV_FMT_Q4_K: return (u / 4) * 144;
-    case QGEMV_FMT_Q6_K: return (u / 4) * 210;
-    case QGEMV_FMT_Q4_0: return u * 36;
-    default: return u * 68;
+// Host view of the row slices of the LDS-streaming kernel.
+struct SliceGeom {
+    int US;       // units per slice
+    int nchunk;   // most 16-byte chunks a slice (plus its misalignment) spans
+};
+
+template <int FMT>
+static SliceGeom slice_geom(int64_t K, int U, int WK) {
+    const bool kq = (FMT == QGEMV_FMT_Q4_K || FMT == QGEMV_FMT_Q6_K);
+    const int rb = row_bytes_of(FMT, K);
+    SliceGeom g;
+    g.US = (U + WK - 1) / WK;
+    if (kq) g.US = (g.US + 3) / 4 * 4;  // slices start at super-block boundaries
+    g.nchunk = 0;
+    for (int k = 0; k < WK; k++) {
+        const int lo = k * g.US;
+        if (lo >= U) break;
+        const int hi = lo + g.US < U ? lo + g.US : U;
+        int e = unit_byte<FMT>(hi);
+        if (e > rb) e = rb;
+        const int len = e - unit_byte<FMT>(lo);
+        const int nc = (len + 15 + 15) / 16;  // up to 15 bytes of misalignment
+        if (nc > g.nchunk) g.nchunk = nc;
     }
+    return g;
+}
+
+// The LDS-streaming kernels take at most 8 chunks per lane and 8 slice
+// buffers (each with 16 bytes of slack for the aligned-dword field reads)
+// within 64 KB of LDS minus the parked row results.
+template <int FMT>
+static bool lds_slice_fits(const SliceGeom& g) {
+    return (g.nchunk + 63) / 64 <= 8 && 8 * (16 * g.nchunk + 16) <= 65536 - 8192;
 }
 
 template <int FMT, int UPL, int WK>
-static hipError_t launch_lds_wk(const GemvArgs& a, int U, hipStream_t st) {
-    const bool kquant = (FMT == QGEMV_FMT_Q4_K || FMT == QGEMV_FMT_Q6_K);
-    int US = (U + WK - 1) / WK;
-    if (kquant) US = (US + 3) / 4 * 4;  // slices start at super-block boundaries
-    const int rb = row_bytes_of(FMT, a.K);
-    int max_slen = 0;
-    for (int kq = 0; kq < WK; kq++) {
-        const int lo = kq * US;
-        if (lo >= U) break;
-        const int hi = lo + US < U ? lo + US : U;
-        int e = unit_byte_host(FMT, hi);
-        if (e > rb) e = rb;
-        const int len = e - unit_byte_host(FMT, lo);
-        if (len > max_slen) max_slen = len;
-    }
-    const int buf_bytes = (max_slen + 15) / 16 * 16;
-    const int nchunk = (max_slen + 15) / 16;
-    const int nl = (nchunk + 63) / 64;  // 16-byte chunks per lane
-    if (nl <= 2) return launch_lds_cfg<FMT, UPL, WK, 2>(a, U, US, buf_bytes, st);
-    if (nl <= 3) return launch_lds_cfg<FMT, UPL, WK, 3>(a, U, US, buf_bytes, st);
-    if (nl <= 4) return launch_lds_cfg<FMT, UPL, WK, 4>(a, U, US, buf_bytes, st);
-    if (nl <= 6) return launch_lds_cfg<FMT, UPL, WK, 6>(a, U, US, buf_bytes, st);
-    return launch_lds_cfg<FMT, UPL, WK, 8>(a, U, US, buf_bytes, st);
-}
-
-// Largest slice (bytes) the LDS-streaming kernels take: at most 8 chunks of
-// 16 bytes per lane, and 8 slice buffers within 64 KB of LDS.
-constexpr int kMaxLdsSlice = 8 * 64 * 16;
-
-template <int FMT, int WK>
-static bool lds_slice_fits(int64_t K, int U) {
-    const bool kquant = (FMT == QGEMV_FMT_Q4_K || FMT == QGEMV_FMT_Q6_K);
-    int US = (U + WK - 1) / WK;
-    if (kquant) US = (US + 3) / 4 * 4;
-    const int len = unit_byte_host(FMT, US < U ? US : U);
-    return len <= kMaxLdsSlice && 8 * ((len + 15) / 16 * 16) <= 65536 - 4096;
+static hipError_t launch_lds_wk(const GemvArgs& a, int U, const SliceGeom& g, hipStream_t st) {
+    const int buf_bytes = 16 * g.nchunk + 16;
+    const int nl = (g.nchunk + 63) / 64;  // 16-byte chunks per lane
+    if (nl <= 2) return launch_lds_cfg<FMT, UPL, WK, 2>(a, U, g.US, buf_bytes, st);
+    if (nl <= 3) return launch_lds_cfg<FMT, UPL, WK, 3>(a, U, g.US, buf_bytes, st);
+    if (nl <= 4) return launch_lds_cfg<FMT, UPL, WK, 4>(a, U, g.US, buf_bytes, st);
+    if (nl <= 6) return launch_lds_cfg<FMT, UPL, WK, 6>(a, U, g.US, buf_bytes, st);
+    return launch_lds_cfg<FMT, UPL, WK, 8>(a, U, g.US, buf_bytes, st);
 }
 
 template <int FMT>
 static hipError_t launch_gemv_fmt(const GemvArgs& a, hipStream_t st) {
     const int U = units_of(FMT, a.K);
     if (kLdsStream && U > 32) {
-        if (U > 256) {
-            if (lds_slice_fits<FMT, 4>(a.K, U)) return launch_lds_wk<FMT, 2, 4>(a, U, st);
-        } else if (U > 128) {
-            if (lds_slice_fits<FMT, 4>(a.K, U)) return launch_lds_wk<FMT, 1, 4>(a, U, st);
-        } else if (U > 64) {
-            if (lds_slice_fits<FMT, 2>(a.K, U)) return launch_lds_wk<FMT, 1, 2>(a, U, st);
-        } else if (lds_slice_fits<FMT, 1>(a.K, U)) {
-            return launch_lds_wk<FMT, 1, 1>(a, U, st);
+        const int WK = U > 128 ? 4 : (U > 64 ? 2 : 1);
+        const SliceGeom g = slice_geom<FMT>(a.K, U, WK);
+        if (lds_slice_fits<FMT>(g)) {
+            if (U > 256) return launch_lds_wk<FMT, 2, 4>(a, U, g, st);
+            if (U > 128) return launch_lds_wk<FMT, 1, 4>(a, U, g, st);
+            if (U > 64) return launch_lds_wk<FMT, 1, 2>(a, U, g, st);
+            return launch_lds_wk<FMT, 1, 1>(a, U, g, st);
         }
     }
     if (U > 256) return launch_gemv_cfg<FMT, 64, 2, 4>(a, U, st);
