@@ -283,11 +283,17 @@ def extras(qg, torch, np, synth, dev, R, c2, c3, args):
         qm, dm, smm = qg.act_buffers(M, K4, dev)
         qg.qgemv_quantize_act(xm, M, K4, K4, qm, dm, smm)
         ym = torch.empty((M, N4), dtype=torch.float32, device=dev)
-        for vname, v in (("dot4", qg.QGEMV_VARIANT_DOT4),):
+        for vname, v in (("dot4", qg.QGEMV_VARIANT_DOT4), ("mfma", qg.QGEMV_VARIANT_MFMA)):
             us = time_kernel(torch, lambda c: qg.qgemm_q4_k_small_m(
                 w4[c], N4, K4, M, qm, dm, smm, ym, v), 50, 16)
             sm[f"M{M}_{vname}_us"] = round(us, 2)
-    sm["weight_GBps_M8_dot4"] = round(33030144 / sm["M8_dot4_us"] / 1e3, 1)
+    for M in (8, 64):
+        best = min(sm[f"M{M}_dot4_us"], sm[f"M{M}_mfma_us"])
+        sm[f"M{M}_weight_GBps"] = round(33030144 / best / 1e3, 1)
+        # int8 MACs of the product over the measured time, against the dense int8 peak
+        sm[f"M{M}_mfma_int8_TOPS"] = round(2 * M * N4 * K4 / sm[f"M{M}_mfma_us"] / 1e6, 1)
+    sm["crossover_M_mfma_faster_from"] = next(
+        (M for M in (1, 2, 4, 8, 16, 32, 64) if sm[f"M{M}_mfma_us"] < sm[f"M{M}_dot4_us"]), None)
     ex["config4_small_m_q4_k_14336x4096"] = sm
     del w4
 

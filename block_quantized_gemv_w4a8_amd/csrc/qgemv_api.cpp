@@ -131,8 +131,8 @@ const char* qgemv_status_str(int status) {
 
 const char* qgemv_build_info(void) {
     return "libqgemv abi=1 arch=gfx950 formats=q4_0,q4_k,q6_k,q8_0 act=int8/32+fp16+int32sum "
-           "gemv=v_dot4_i32_i8,lds-act,lanes-per-row{4,8,16,32,64} "
-           "small_m=q4_k{dot4} K_max=32768 M_max=64";
+           "gemv=v_dot4_i32_i8,lds-row-stream,lanes-per-row{4,8,16,32,64} "
+           "small_m=q4_k{dot4,mfma_i8_16x16x32} K_max=32768 M_max=64";
 }
 
 const char* qgemv_last_error(void) { return g_last_error; }
@@ -197,8 +197,6 @@ qgemv_status qgemm_q4_k_small_m(const void* w, int64_t N, int64_t K, int64_t M, 
     if (variant != QGEMV_VARIANT_AUTO && variant != QGEMV_VARIANT_DOT4 &&
         variant != QGEMV_VARIANT_MFMA)
         return fail(QGEMV_E_UNSUPPORTED, "%s: unknown variant %d", name, variant);
-    if (variant == QGEMV_VARIANT_MFMA)
-        return fail(QGEMV_E_UNSUPPORTED, "%s: the MFMA variant is not built in this library", name);
     if (!aligned(w, 16)) return fail(QGEMV_E_ALIGN, "%s: w must be 16-byte aligned", name);
     if ((st = check_act_align(q, d, s)) != QGEMV_OK) return st;
     if (!aligned(y, 4)) return fail(QGEMV_E_ALIGN, "%s: y must be 4-byte aligned", name);

