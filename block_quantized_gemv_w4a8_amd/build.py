@@ -30,6 +30,9 @@ FLAGS = [
     "-fno-fast-math", "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
+    # MFMA results straight into VGPRs: the small-M epilogue reads every
+    # result with vector instructions, and AGPR results need a copy each
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", os.path.join(ROOT, "include"),
 ]
 
