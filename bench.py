@@ -33,10 +33,11 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
 METRIC = "quantized GEMV weight GB/s and % of HBM peak at Llama-3-8B shapes, 1 GPU"
-WORKLOAD = ("llama3.1-8b decode step, batch 1: ffn gate|up q4_k 28672x4096 -> silu*up "
-            "requant -> down q6_k 4096x14336, then lm_head q6_k 128256x4096")
+WORKLOAD = ("llama3.1-8b decode step, batch 1: ffn gate|up q4_k 28672x4096 with fused "
+            "silu*up requant -> down q6_k 4096x14336, then lm_head q6_k 128256x4096")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_q6k_lm_head.json")
-KERNEL_SOURCES = ["qgemv_device.h", "k_gemv.hip", "k_quantize.hip", "qgemv_api.cpp"]
+KERNEL_SOURCES = ["qgemv_device.h", "qgemv_quant.h", "k_gemv.hip", "k_quantize.hip",
+                  "qgemv_api.cpp"]
 
 
 def log(*a):
@@ -60,6 +61,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the per-kernel/config extras")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--unfused", action="store_true",
+                    help="gate|up GEMV and SiLU*up requant as two launches (comparison)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (for counter calibration)")
     args = ap.parse_args()
@@ -113,8 +116,12 @@ def main():
     def step(i, ev=None):
         c = i % R
         qg.qgemv_quantize_act(x_ffn, 1, Kgu, Kgu, q1, d1, s1, stream=sh)
-        qg.qgemv_q4_k(w_gu[c], Ngu, Kgu, q1, d1, s1, gu, stream=sh)
-        qg.qgemv_silu_mul_quantize(gu, Kd, q2, d2, s2, None, stream=sh)
+        if args.unfused:
+            qg.qgemv_q4_k(w_gu[c], Ngu, Kgu, q1, d1, s1, gu, stream=sh)
+            qg.qgemv_silu_mul_quantize(gu, Kd, q2, d2, s2, None, stream=sh)
+        else:
+            qg.qgemv_q4_k_swiglu_quantize(w_gu[c], Kd, Kgu, q1, d1, s1, q2, d2, s2, None, None,
+                                          stream=sh)
         qg.qgemv_q6_k(w_dn[c], Nd, Kd, q2, d2, s2, y_ffn, stream=sh)
         qg.qgemv_quantize_act(x_head, 1, Kh, Kh, q3, d3, s3, stream=sh)
         if ev is not None:
@@ -193,7 +200,8 @@ def main():
         "vs_baseline": None,
         "dtype": "int8",
         "data": "synthetic (seeded; shapes and value distributions of the five workloads)",
-        "config": {"workload": WORKLOAD, "batch": 1,
+        "config": {"workload": WORKLOAD if not args.unfused else
+                   WORKLOAD.replace("with fused", "then a separate"), "batch": 1,
                    "weight_bytes_per_step": step_wbytes, "weight_copies_rotated": R,
                    "steps_per_s": round(1e3 / ms_per_step, 1)},
         "hbm_peak_frac": round(value / HBM_PEAK_GBPS, 4),
@@ -220,6 +228,100 @@ def time_kernel(torch, fn, iters, R):
     return a.elapsed_time(b) * 1e3 / iters
 
 
+def graph_time(torch, calls, reps=20):
+    """Capture `calls` (each launches on the current stream) into one graph;
+    returns microseconds per replay."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for f in calls:
+            f()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for f in calls:
+            f()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return g, a.elapsed_time(b) * 1e3 / reps
+
+
+def graph_config0(qg, torch, np, dev, c0, copies):
+    """Config 0 (Q4_0 896x896) as one graph of `copies` GEMVs over rotated
+    weight copies; a replay's output must equal the eager call's bit for bit."""
+    ws = [torch.from_numpy(c0["w"]).to(dev)]
+    for _ in range(copies - 1):
+        ws.append(ws[0].clone())
+    q, d, s = qg.act_buffers(1, 896, dev)
+    qg.qgemv_quantize_act(torch.from_numpy(c0["x"]).to(dev), 1, 896, 896, q, d, s)
+    ys = torch.empty((copies, 896), dtype=torch.float32, device=dev)
+    calls = [lambda c=c: qg.qgemv_q4_0(ws[c], 896, 896, q, d, s, ys[c]) for c in range(copies)]
+    eager = torch.empty(896, dtype=torch.float32, device=dev)
+    qg.qgemv_q4_0(ws[0], 896, 896, q, d, s, eager)
+    g, us = graph_time(torch, calls)
+    ys.fill_(float("nan"))
+    g.replay()
+    torch.cuda.synchronize()
+    same = bool(torch.equal(ys[0].view(torch.int32), eager.view(torch.int32)) and
+                torch.equal(ys[-1].view(torch.int32), eager.view(torch.int32)))
+    per = us / copies
+    del ws, g
+    return {"us_per_gemv": round(per, 3), "weight_GBps": round(451584 / per / 1e3, 1),
+            "calls_per_s": round(1e6 / per), "replay_equals_eager": same}
+
+
+def graph_config1(qg, torch, np, dev, c1, layers):
+    """One config-1 layer (3 activation quantisations + 7 Q4_K GEMVs) per
+    rotated weight copy, `layers` layers in one graph."""
+    mats = c1["mats"]
+    wl = {n: [torch.from_numpy(m["w"]).to(dev)] for n, m in mats.items()}
+    for n in wl:
+        for _ in range(layers - 1):
+            wl[n].append(wl[n][0].clone())
+    # activations: q/k/v/gate/up share one 896-vector, o and down have their own
+    xs = {}
+    for n, m in mats.items():
+        key = m["x"].tobytes()
+        if key not in xs:
+            xs[key] = (torch.from_numpy(m["x"]).to(dev), m["K"], qg.act_buffers(1, m["K"], dev))
+    ys = {n: torch.empty(m["N"], dtype=torch.float32, device=dev) for n, m in mats.items()}
+
+    def layer(c):
+        calls = [lambda x=x, K=K, a=a: qg.qgemv_quantize_act(x, 1, K, K, *a)
+                 for x, K, a in xs.values()]
+        for n, m in mats.items():
+            a = xs[m["x"].tobytes()][2]
+            calls.append(lambda n=n, m=m, a=a: qg.qgemv_q4_k(wl[n][c], m["N"], m["K"], *a, ys[n]))
+        return calls
+
+    calls = []
+    for c in range(layers):
+        calls += layer(c)
+    for f in layer(0):
+        f()
+    torch.cuda.synchronize()
+    eager = {n: y.clone() for n, y in ys.items()}
+    g, us = graph_time(torch, calls)
+    for y in ys.values():
+        y.fill_(float("nan"))
+    g.replay()
+    torch.cuda.synchronize()
+    same = all(torch.equal(ys[n].view(torch.int32), eager[n].view(torch.int32)) for n in ys)
+    per = us / layers
+    del wl, g
+    return {"us_per_layer": round(per, 2), "weight_GBps": round(8386560 / per / 1e3, 1),
+            "layers_per_s": round(1e6 / per), "replay_equals_eager": same}
+
+
 def extras(qg, torch, np, synth, dev, R, c2, c3, args):
     """Per-kernel timings of the step's GEMVs and the other workloads."""
     ex = {}
@@ -241,6 +343,20 @@ def extras(qg, torch, np, synth, dev, R, c2, c3, args):
                 "hbm_frac": round(wb / us / 1e3 / HBM_PEAK_GBPS, 4), "calls_per_s": round(1e6 / us)}
 
     ex["gate_up_q4_k_28672x4096"] = gemv_case("q4_k", c2["w_gu"], Ngu, Kgu, c2["x"], 8)
+    # the same product with SiLU*up and the requantisation fused in (one launch)
+    wsw = [torch.from_numpy(c2["w_gu"]).to(dev)]
+    for _ in range(7):
+        wsw.append(wsw[0].clone())
+    qa, da, sa = qg.act_buffers(1, Kgu, dev)
+    qg.qgemv_quantize_act(torch.from_numpy(c2["x"]).to(dev), 1, Kgu, Kgu, qa, da, sa)
+    qo, do, so = qg.act_buffers(1, Kd, dev)
+    us = time_kernel(torch, lambda c: qg.qgemv_q4_k_swiglu_quantize(
+        wsw[c], Kd, Kgu, qa, da, sa, qo, do, so, None, None), 100, 8)
+    wb = synth.logical_bytes("q4_k", Ngu, Kgu)
+    ex["gate_up_swiglu_fused_q4_k_28672x4096"] = {
+        "us": round(us, 2), "weight_GBps": round(wb / us / 1e3, 1),
+        "hbm_frac": round(wb / us / 1e3 / HBM_PEAK_GBPS, 4), "calls_per_s": round(1e6 / us)}
+    del wsw
     hx = np.random.default_rng(0).standard_normal((1, Kd)).astype(np.float32)
     ex["down_q6_k_4096x14336"] = gemv_case("q6_k", c2["w_down"], Nd, Kd, hx, 11)
     ex["lm_head_q6_k_128256x4096"] = gemv_case("q6_k", c3["w"], Nh, Kh, c3["x"], 2)
@@ -258,9 +374,11 @@ def extras(qg, torch, np, synth, dev, R, c2, c3, args):
     ex["silu_mul_quantize_14336_us"] = round(time_kernel(
         torch, lambda c: qg.qgemv_silu_mul_quantize(gu, Kd, q2, d2, s2, None), 200, 1), 2)
 
-    # config 0 / config 1: launch-bound small GEMVs (weights rotated over 64 copies)
+    # config 0 / config 1: launch-bound small GEMVs (weights rotated over 1200
+    # and 64 copies), launched one by one and as one captured graph
     c0 = synth.config0()
     ex["config0_q4_0_896x896"] = gemv_case("q4_0", c0["w"], 896, 896, c0["x"], 1200)
+    ex["config0_q4_0_896x896"]["graph"] = graph_config0(qg, torch, np, dev, c0, 1200)
     c1 = synth.config1()
     layer_us = 0.0
     per = {}
@@ -269,7 +387,8 @@ def extras(qg, torch, np, synth, dev, R, c2, c3, args):
         per[name] = r["us"]
         layer_us += r["us"]
     ex["config1_q4_k_layer"] = {"per_matrix_us": per, "sum_us": round(layer_us, 2),
-                                "weight_GBps": round(8386560 / layer_us / 1e3, 1)}
+                                "weight_GBps": round(8386560 / layer_us / 1e3, 1),
+                                "graph": graph_config1(qg, torch, np, dev, c1, 64)}
 
     # config 4: small-M Q4_K 14336 x 4096
     c4 = synth.config4()

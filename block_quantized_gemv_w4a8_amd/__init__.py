@@ -40,7 +40,8 @@ QGEMV_M_MAX = 64
 EXPORTS = [
     "qgemv_abi_version", "qgemv_status_str", "qgemv_build_info", "qgemv_last_error",
     "qgemv_quantize_act", "qgemv_q4_0", "qgemv_q4_k", "qgemv_q6_k", "qgemv_q8_0",
-    "qgemm_q4_k_small_m", "qgemv_silu_mul_quantize", "qgemv_block_dots",
+    "qgemm_q4_k_small_m", "qgemv_silu_mul_quantize", "qgemv_q4_k_swiglu_quantize",
+    "qgemv_block_dots",
 ]
 
 _P, _I64, _I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
@@ -61,6 +62,8 @@ _lib.qgemm_q4_k_small_m.restype = _I
 _lib.qgemm_q4_k_small_m.argtypes = [_P, _I64, _I64, _I64, _P, _P, _P, _P, _I, _P]
 _lib.qgemv_silu_mul_quantize.restype = _I
 _lib.qgemv_silu_mul_quantize.argtypes = [_P, _I64, _P, _P, _P, _P, _P]
+_lib.qgemv_q4_k_swiglu_quantize.restype = _I
+_lib.qgemv_q4_k_swiglu_quantize.argtypes = [_P, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P]
 _lib.qgemv_block_dots.restype = _I
 _lib.qgemv_block_dots.argtypes = [_I, _P, _I64, _I64, _I64, _I64, _P, _P, _P]
 
@@ -150,6 +153,14 @@ def qgemm_q4_k_small_m(w, N, K, M, q, d, s, y, variant=QGEMV_VARIANT_AUTO, strea
 def qgemv_silu_mul_quantize(gu, N, q, d, s, h=None, stream=None):
     return _check(_lib.qgemv_silu_mul_quantize(_ptr(gu), N, _ptr(q), _ptr(d), _ptr(s), _ptr(h),
                                                _stream(stream)), "qgemv_silu_mul_quantize")
+
+
+def qgemv_q4_k_swiglu_quantize(w, N, K, q, d, s, q_out, d_out, s_out, gu=None, h=None,
+                               stream=None):
+    return _check(_lib.qgemv_q4_k_swiglu_quantize(_ptr(w), N, K, _ptr(q), _ptr(d), _ptr(s),
+                                                  _ptr(q_out), _ptr(d_out), _ptr(s_out), _ptr(gu),
+                                                  _ptr(h), _stream(stream)),
+                  "qgemv_q4_k_swiglu_quantize")
 
 
 def qgemv_block_dots(fmt, w, N, K, row0, nrows, q, dots, stream=None):

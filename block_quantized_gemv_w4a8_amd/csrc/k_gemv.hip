@@ -24,6 +24,7 @@
 
 #include "qgemv_device.h"
 #include "qgemv_launch.h"
+#include "qgemv_quant.h"
 
 namespace qgemv {
 
@@ -410,13 +411,23 @@ __host__ __device__ inline int unit_byte(int u) {
 // bytes), so no load leaves the row.  Two rows are in flight in registers
 // while a third is computed from LDS.  Row results are parked in LDS and
 // written out together (one lane per row would issue a store per row).
-template <int FMT, int UPL, int WK, int NL, bool NT>
+//
+// SW (the fused gate|up product of a SwiGLU block): the weights are gate rows
+// 0 .. nh-1 then up rows nh .. 2nh-1 (N = 2nh).  A workgroup walks whole
+// output blocks of 32: block b is gate rows 32b .. 32b+31 and up rows
+// nh+32b .. nh+32b+31, so the 64 row results of a block end up parked in the
+// workgroup's LDS together.  At the end of a segment, 8 lanes per block form
+// h = silu(g) * u and quantise it as the next product's activation block b
+// (the same device functions as k_silu_mul_quantize); the [gate | up] and h
+// values are stored only where asked for.  Workgroup 0 also zeroes the
+// activation blocks between nh and the next multiple of 256.
+template <int FMT, int UPL, int WK, int NL, bool NT, bool SW>
 __global__ __launch_bounds__(WG) void k_gemv_lds(const uint8_t* __restrict__ w, int N, int U,
                                                   int US, int nbw, int row_bytes, int buf_bytes,
                                                   const int8_t* __restrict__ q,
                                                   const uint16_t* __restrict__ d,
                                                   const int32_t* __restrict__ s,
-                                                  float* __restrict__ y) {
+                                                  float* __restrict__ y, const SwigluOut so) {
     extern __shared__ __align__(16) uint8_t lds[];
     constexpr int LPR = 64;
     constexpr int RPP = 4 / WK;
@@ -449,7 +460,26 @@ __global__ __launch_bounds__(WG) void k_gemv_lds(const uint8_t* __restrict__ w, 
     uint8_t* buf1 = buf0 + buf_bytes;
     const int64_t G = gridDim.x;
     const int64_t ngroups = ((int64_t)N + RPP - 1) / RPP;
-    auto row_of = [&](int64_t p) { return (blockIdx.x + p * G) * RPP + rg; };
+    constexpr int GPB = 64 / RPP;   // SW: row groups (passes) per output block
+    const int64_t nhb = SW ? so.nh / 32 : 0;
+    auto row_of = [&](int64_t p) -> int64_t {
+        if (!SW) return (blockIdx.x + p * G) * RPP + rg;
+        const int64_t hb = blockIdx.x + (p / GPB) * G;
+        const int l = (int)(p % GPB) * RPP + rg;   // 0..31 gate, 32..63 up
+        return l < 32 ? 32 * hb + l : so.nh + 32 * hb + (l - 32);
+    };
+    if (SW && blockIdx.x == 0) {
+        // activation blocks past nh, up to the next multiple of 256: zero
+        const int64_t nbo = (so.nh + 255) / 256 * 8;
+        for (int64_t t = threadIdx.x; t < (nbo - nhb) * 8; t += WG) {
+            const int64_t b = nhb + t / 8;
+            *reinterpret_cast<uint32_t*>(so.q + 32 * b + 4 * (t % 8)) = 0u;
+            if (t % 8 == 0) {
+                so.d[b] = 0;
+                so.s[b] = 0;
+            }
+        }
+    }
     // offset (from the aligned chunk base) of this lane's k-th chunk
     auto chunk_off = [&](int k, int delta) { return min(16 * (lane + 64 * k), delta + slen - 16); };
     // Issue the loads of a row's slice; returns the slice's offset from the
@@ -484,8 +514,10 @@ __global__ __launch_bounds__(WG) void k_gemv_lds(const uint8_t* __restrict__ w, 
         if (lane == LPR - 1) part[(pl * RPP + rg) * WK + kq] = acc;
     };
 
-    const int64_t npass_all = ngroups > (int64_t)blockIdx.x
-                                  ? (ngroups - blockIdx.x + G - 1) / G : 0;
+    const int64_t npass_all =
+        SW ? (nhb > (int64_t)blockIdx.x ? (nhb - blockIdx.x + G - 1) / G : 0) * GPB
+           : (ngroups > (int64_t)blockIdx.x ? (ngroups - blockIdx.x + G - 1) / G : 0);
+    static_assert(SEGP % GPB == 0, "a segment holds whole output blocks");
     for (int64_t p0 = 0; p0 < npass_all; p0 += SEGP) {
         const int np = (int)min((int64_t)SEGP, npass_all - p0);
         u32x4 Ra[NL], Rb[NL];
@@ -509,13 +541,46 @@ __global__ __launch_bounds__(WG) void k_gemv_lds(const uint8_t* __restrict__ w, 
             __builtin_amdgcn_sched_barrier(0);
         }
         __syncthreads();
-        for (int t = threadIdx.x; t < np * RPP; t += WG) {
-            const int64_t row = (blockIdx.x + (p0 + t / RPP) * G) * RPP + t % RPP;
-            if (row < N) {
-                float v = part[t * WK];
+        if (!SW) {
+            for (int t = threadIdx.x; t < np * RPP; t += WG) {
+                const int64_t row = (blockIdx.x + (p0 + t / RPP) * G) * RPP + t % RPP;
+                if (row < N) {
+                    float v = part[t * WK];
 #pragma unroll
-                for (int k = 1; k < WK; k++) v += part[t * WK + k];
-                y[row] = v;
+                    for (int k = 1; k < WK; k++) v += part[t * WK + k];
+                    y[row] = v;
+                }
+            }
+        } else {
+            // row l of the segment's output block j is part[(64 j + l) * WK + kq]
+            const int nblk = np / GPB;
+            const int t = threadIdx.x;
+            if (t < 8 * nblk) {
+                const int j = t >> 3, sub = t & 7;
+                const int64_t hb = blockIdx.x + (p0 / GPB + j) * G;
+                float v[4];
+#pragma unroll
+                for (int k = 0; k < 4; k++) {
+                    const int i = 4 * sub + k;
+                    float g = part[(64 * j + i) * WK], u = part[(64 * j + 32 + i) * WK];
+#pragma unroll
+                    for (int kk = 1; kk < WK; kk++) {
+                        g += part[(64 * j + i) * WK + kk];
+                        u += part[(64 * j + 32 + i) * WK + kk];
+                    }
+                    v[k] = silu_mul(g, u);
+                    if (so.gu) {
+                        so.gu[32 * hb + i] = g;
+                        so.gu[so.nh + 32 * hb + i] = u;
+                    }
+                    if (so.h) so.h[32 * hb + i] = v[k];
+                }
+                const QBlock r = quantize_block8(v);
+                *reinterpret_cast<uint32_t*>(so.q + 32 * hb + 4 * sub) = r.packed;
+                if (sub == 0) {
+                    so.d[hb] = (uint16_t)r.dbits;
+                    so.s[hb] = r.sum;
+                }
             }
         }
         __syncthreads();
@@ -651,7 +716,7 @@ static hipError_t launch_gemv_cfg(const GemvArgs& a, int U, hipStream_t st) {
 constexpr bool kLdsStream = true;
 constexpr bool kStreamNT = true;
 
-template <int FMT, int UPL, int WK, int NL>
+template <int FMT, int UPL, int WK, int NL, bool SW>
 static int resident_workgroups_lds(int smem) {
     static std::atomic<int> cache[64];
     int dev = 0;
@@ -660,7 +725,7 @@ static int resident_workgroups_lds(int smem) {
     if (v > 0) return v;
     int per_cu = 0, cus = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, k_gemv_lds<FMT, UPL, WK, NL, kStreamNT>, WG, smem) != hipSuccess ||
+            &per_cu, k_gemv_lds<FMT, UPL, WK, NL, kStreamNT, SW>, WG, smem) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         per_cu <= 0 || cus <= 0) {
         (void)hipGetLastError();
@@ -676,23 +741,24 @@ static int resident_workgroups_lds(int smem) {
 // fastest; more waves add in-flight requests without adding bandwidth.
 constexpr int kLdsWgPerCu = 2;
 
-template <int FMT, int UPL, int WK, int NL>
-static hipError_t launch_lds_cfg(const GemvArgs& a, int U, int US, int buf_bytes,
-                                 hipStream_t st) {
+template <int FMT, int UPL, int WK, int NL, bool SW>
+static hipError_t launch_lds_cfg(const GemvArgs& a, const SwigluOut& so, int U, int US,
+                                 int buf_bytes, hipStream_t st) {
     constexpr int RPP = 4 / WK;
     const int smem = 8 * buf_bytes;  // 4 waves x 2 buffers
-    const int64_t ngroups = (a.N + RPP - 1) / RPP;
-    int64_t resident = resident_workgroups_lds<FMT, UPL, WK, NL>(smem);
+    // work items: row groups, or (SW) output blocks of 32
+    const int64_t items = SW ? so.nh / 32 : (a.N + RPP - 1) / RPP;
+    int64_t resident = resident_workgroups_lds<FMT, UPL, WK, NL, SW>(smem);
     int cus = 0, dev = 0;
     if (hipGetDevice(&dev) == hipSuccess &&
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
         cus > 0 && resident > (int64_t)kLdsWgPerCu * cus)
         resident = (int64_t)kLdsWgPerCu * cus;
-    const int64_t passes = (ngroups + resident - 1) / resident;
-    const int64_t grid = (ngroups + passes - 1) / passes;
-    hipLaunchKernelGGL((k_gemv_lds<FMT, UPL, WK, NL, kStreamNT>), dim3((unsigned)grid), dim3(WG),
-                       smem, st, (const uint8_t*)a.w, (int)a.N, U, US, (int)(a.K / 32),
-                       row_bytes_of(FMT, a.K), buf_bytes, a.q, a.d, a.s, a.y);
+    const int64_t passes = (items + resident - 1) / resident;
+    const int64_t grid = (items + passes - 1) / passes;
+    hipLaunchKernelGGL((k_gemv_lds<FMT, UPL, WK, NL, kStreamNT, SW>), dim3((unsigned)grid),
+                       dim3(WG), smem, st, (const uint8_t*)a.w, (int)a.N, U, US, (int)(a.K / 32),
+                       row_bytes_of(FMT, a.K), buf_bytes, a.q, a.d, a.s, a.y, so);
     return hipGetLastError();
 }
 
@@ -731,15 +797,16 @@ static bool lds_slice_fits(const SliceGeom& g) {
     return (g.nchunk + 63) / 64 <= 8 && 8 * (16 * g.nchunk + 16) <= 65536 - 8192;
 }
 
-template <int FMT, int UPL, int WK>
-static hipError_t launch_lds_wk(const GemvArgs& a, int U, const SliceGeom& g, hipStream_t st) {
+template <int FMT, int UPL, int WK, bool SW = false>
+static hipError_t launch_lds_wk(const GemvArgs& a, int U, const SliceGeom& g, hipStream_t st,
+                                const SwigluOut& so = SwigluOut{}) {
     const int buf_bytes = 16 * g.nchunk + 16;
     const int nl = (g.nchunk + 63) / 64;  // 16-byte chunks per lane
-    if (nl <= 2) return launch_lds_cfg<FMT, UPL, WK, 2>(a, U, g.US, buf_bytes, st);
-    if (nl <= 3) return launch_lds_cfg<FMT, UPL, WK, 3>(a, U, g.US, buf_bytes, st);
-    if (nl <= 4) return launch_lds_cfg<FMT, UPL, WK, 4>(a, U, g.US, buf_bytes, st);
-    if (nl <= 6) return launch_lds_cfg<FMT, UPL, WK, 6>(a, U, g.US, buf_bytes, st);
-    return launch_lds_cfg<FMT, UPL, WK, 8>(a, U, g.US, buf_bytes, st);
+    if (nl <= 2) return launch_lds_cfg<FMT, UPL, WK, 2, SW>(a, so, U, g.US, buf_bytes, st);
+    if (nl <= 3) return launch_lds_cfg<FMT, UPL, WK, 3, SW>(a, so, U, g.US, buf_bytes, st);
+    if (nl <= 4) return launch_lds_cfg<FMT, UPL, WK, 4, SW>(a, so, U, g.US, buf_bytes, st);
+    if (nl <= 6) return launch_lds_cfg<FMT, UPL, WK, 6, SW>(a, so, U, g.US, buf_bytes, st);
+    return launch_lds_cfg<FMT, UPL, WK, 8, SW>(a, so, U, g.US, buf_bytes, st);
 }
 
 template <int FMT>
@@ -763,6 +830,21 @@ static hipError_t launch_gemv_fmt(const GemvArgs& a, hipStream_t st) {
     if (U > 8) return launch_gemv_cfg<FMT, 16, 1, 1>(a, U, st);
     if (U > 4) return launch_gemv_cfg<FMT, 8, 1, 1>(a, U, st);
     return launch_gemv_cfg<FMT, 4, 1, 1>(a, U, st);
+}
+
+// The fused gate|up product always takes the LDS-streaming kernel (with the
+// split-K of launch_gemv_fmt); every Q4_K row up to QGEMV_K_MAX fits its
+// slice buffers.
+hipError_t launch_q4k_swiglu(const GemvArgs& a, const SwigluOut& so, hipStream_t st) {
+    constexpr int FMT = QGEMV_FMT_Q4_K;
+    const int U = units_of(FMT, a.K);
+    const int WK = U > 128 ? 4 : (U > 64 ? 2 : 1);
+    const SliceGeom g = slice_geom<FMT>(a.K, U, WK);
+    if (!lds_slice_fits<FMT>(g)) return hipErrorInvalidValue;
+    if (U > 256) return launch_lds_wk<FMT, 2, 4, true>(a, U, g, st, so);
+    if (U > 128) return launch_lds_wk<FMT, 1, 4, true>(a, U, g, st, so);
+    if (U > 64) return launch_lds_wk<FMT, 1, 2, true>(a, U, g, st, so);
+    return launch_lds_wk<FMT, 1, 1, true>(a, U, g, st, so);
 }
 
 hipError_t launch_gemv(int fmt, const GemvArgs& a, hipStream_t st) {

@@ -132,7 +132,7 @@ const char* qgemv_status_str(int status) {
 const char* qgemv_build_info(void) {
     return "libqgemv abi=1 arch=gfx950 formats=q4_0,q4_k,q6_k,q8_0 act=int8/32+fp16+int32sum "
            "gemv=v_dot4_i32_i8,lds-row-stream,lanes-per-row{4,8,16,32,64} "
-           "small_m=q4_k{dot4,mfma_i8_16x16x32} K_max=32768 M_max=64";
+           "small_m=q4_k{dot4,mfma_i8_16x16x32} fused=q4_k_swiglu_quantize K_max=32768 M_max=64";
 }
 
 const char* qgemv_last_error(void) { return g_last_error; }
@@ -221,6 +221,35 @@ qgemv_status qgemv_silu_mul_quantize(const float* gu, int64_t N, int8_t* q, uint
     if (h && !aligned(h, 4)) return fail(QGEMV_E_ALIGN, "%s: h must be 4-byte aligned", name);
     if ((st = check_device()) != QGEMV_OK) return st;
     return launched(qgemv::launch_silu_mul_quantize(gu, N, q, d, s, h, (hipStream_t)stream), name);
+}
+
+qgemv_status qgemv_q4_k_swiglu_quantize(const void* w, int64_t N, int64_t K, const int8_t* q,
+                                        const uint16_t* d, const int32_t* s, int8_t* q_out,
+                                        uint16_t* d_out, int32_t* s_out, float* gu, float* h,
+                                        qgemv_stream_t stream) {
+    const char* name = "qgemv_q4_k_swiglu_quantize";
+    if (N < 0) return fail(QGEMV_E_SHAPE, "%s: N = %lld is negative", name, (long long)N);
+    if (N == 0) return ok();
+    if (!w || !q || !d || !s || !q_out || !d_out || !s_out)
+        return fail(QGEMV_E_NULL, "%s: NULL pointer argument", name);
+    qgemv_status st = check_k(K);
+    if (st != QGEMV_OK) return st;
+    if (N % 32 != 0)
+        return fail(QGEMV_E_SHAPE, "%s: N = %lld must be a multiple of 32", name, (long long)N);
+    if (2 * N > INT32_MAX)
+        return fail(QGEMV_E_SHAPE, "%s: 2N = %lld exceeds 2^31-1", name, (long long)(2 * N));
+    if (K > QGEMV_K_MAX)
+        return fail(QGEMV_E_UNSUPPORTED, "%s: K = %lld exceeds QGEMV_K_MAX = %d", name,
+                    (long long)K, QGEMV_K_MAX);
+    if (!aligned(w, 16)) return fail(QGEMV_E_ALIGN, "%s: w must be 16-byte aligned", name);
+    if ((st = check_act_align(q, d, s)) != QGEMV_OK) return st;
+    if ((st = check_act_align(q_out, d_out, s_out)) != QGEMV_OK) return st;
+    if (gu && !aligned(gu, 4)) return fail(QGEMV_E_ALIGN, "%s: gu must be 4-byte aligned", name);
+    if (h && !aligned(h, 4)) return fail(QGEMV_E_ALIGN, "%s: h must be 4-byte aligned", name);
+    if ((st = check_device()) != QGEMV_OK) return st;
+    const qgemv::GemvArgs a{w, 2 * N, K, q, d, s, nullptr};
+    const qgemv::SwigluOut so{N, q_out, d_out, s_out, gu, h};
+    return launched(qgemv::launch_q4k_swiglu(a, so, (hipStream_t)stream), name);
 }
 
 qgemv_status qgemv_block_dots(int fmt, const void* w, int64_t N, int64_t K, int64_t row0,

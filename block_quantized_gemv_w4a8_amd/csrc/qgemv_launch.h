@@ -19,7 +19,20 @@ struct GemvArgs {
     float* y;
 };
 
+// Outputs of the fused gate|up -> SwiGLU -> quantise product: the activation
+// of the next product (nh values, padded to whole super-blocks of 256) and,
+// where not NULL, the fp32 [gate | up] products and h.
+struct SwigluOut {
+    int64_t nh;
+    int8_t* q;
+    uint16_t* d;
+    int32_t* s;
+    float* gu;
+    float* h;
+};
+
 hipError_t launch_gemv(int fmt, const GemvArgs& a, hipStream_t st);
+hipError_t launch_q4k_swiglu(const GemvArgs& a, const SwigluOut& so, hipStream_t st);
 hipError_t launch_block_dots(int fmt, const void* w, int64_t K, int64_t row0, int64_t nrows,
                              const int8_t* q, int32_t* dots, hipStream_t st);
 hipError_t launch_quantize_act(const float* x, int64_t M, int64_t K, int64_t ldx, int8_t* q,

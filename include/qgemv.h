@@ -151,6 +151,26 @@ qgemv_status qgemv_silu_mul_quantize(const float* gu, int64_t N, int8_t* q,
                                      uint16_t* d, int32_t* s, float* h,
                                      qgemv_stream_t stream);
 
+/* The gate|up product, SwiGLU and the quantisation of its result in one
+ * launch ("Running an LLM on VKNN", Performance: the decode step is almost
+ * all matmul, and the few other ops each cost a launch; SwiGLU as in the
+ * same page's model description).  Equal, bit for bit, to qgemv_q4_k on
+ * the 2N rows followed by qgemv_silu_mul_quantize on its output.
+ * w: Q4_K weights of 2N rows x K (gate rows 0..N-1, then up rows N..2N-1),
+ *    row stride Kp/256*144 bytes, 16-byte aligned.
+ * q, d, s: the activation of the gate|up product (qgemv_quantize_act, K).
+ * q_out [Np], d_out [Np/32], s_out [Np/32], Np = N rounded up to 256: the
+ *    activation of the next product (K = N), blocks past N written as zero;
+ *    same alignment rules as q, d, s.
+ * gu: NULL, or fp32 [2N] receiving [gate | up]; h: NULL, or fp32 [N].
+ * N % 32 == 0, K as for qgemv_q4_k.  The caller owns every buffer; nothing
+ * is allocated; gates and errors as for qgemv_q4_k. */
+qgemv_status qgemv_q4_k_swiglu_quantize(const void* w, int64_t N, int64_t K,
+                                        const int8_t* q, const uint16_t* d,
+                                        const int32_t* s, int8_t* q_out,
+                                        uint16_t* d_out, int32_t* s_out, float* gu,
+                                        float* h, qgemv_stream_t stream);
+
 /* Validation: the int32 block dots of weight rows [row0, row0+nrows) against
  * one activation row q [Kp], computed by the same device code as the GEMV
  * kernels.  dots: int32 [nrows][nblk] with nblk = K/32 (Q4_0, Q8_0),

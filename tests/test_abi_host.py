@@ -73,6 +73,9 @@ def test_gates_null_shape_limits_align():
     assert _status("qgemv_quantize_act", None, 1, 32, 32, A, A, A, S) == qg.QGEMV_E_NULL
     assert _status("qgemv_silu_mul_quantize", A, 64, None, A, A, None, S) == qg.QGEMV_E_NULL
     assert _status("qgemv_block_dots", 1, A, 4, 256, 0, 4, A, None, S) == qg.QGEMV_E_NULL
+    SW = "qgemv_q4_k_swiglu_quantize"   # w, N, K, q, d, s, q_out, d_out, s_out, gu, h, stream
+    assert _status(SW, A, 64, 256, A, A, A, None, A, A, None, None, S) == qg.QGEMV_E_NULL
+    assert _status(SW, None, 64, 256, A, A, A, A, A, A, None, None, S) == qg.QGEMV_E_NULL
     # shapes
     for K in (0, 16, 48, -32):
         assert _status("qgemv_q4_0", A, 10, K, A, A, A, A, S) == qg.QGEMV_E_SHAPE
@@ -81,16 +84,21 @@ def test_gates_null_shape_limits_align():
     assert _status("qgemv_silu_mul_quantize", A, 48, A, A, A, None, S) == qg.QGEMV_E_SHAPE
     assert _status("qgemv_block_dots", 1, A, 4, 256, 3, 2, A, A, S) == qg.QGEMV_E_SHAPE
     assert _status("qgemm_q4_k_small_m", A, 8, 256, -1, A, A, A, A, 1, S) == qg.QGEMV_E_SHAPE
+    assert _status(SW, A, 48, 256, A, A, A, A, A, A, None, None, S) == qg.QGEMV_E_SHAPE
+    assert _status(SW, A, 64, 48, A, A, A, A, A, A, None, None, S) == qg.QGEMV_E_SHAPE
+    assert _status(SW, A, 1 << 30, 256, A, A, A, A, A, A, None, None, S) == qg.QGEMV_E_SHAPE
     # empty problems succeed without touching anything (NULLs allowed)
     assert _status("qgemv_q4_k", None, 0, 256, None, None, None, None, S) == qg.QGEMV_OK
     assert _status("qgemv_quantize_act", None, 0, 256, 256, None, None, None, S) == qg.QGEMV_OK
     assert _status("qgemm_q4_k_small_m", None, 5, 256, 0, None, None, None, None, 0, S) == qg.QGEMV_OK
     assert _status("qgemv_block_dots", 2, None, 4, 256, 4, 0, None, None, S) == qg.QGEMV_OK
+    assert _status(SW, None, 0, 256, None, None, None, None, None, None, None, None, S) == qg.QGEMV_OK
     # limits of this build
     assert _status("qgemv_q6_k", A, 10, 65536, A, A, A, A, S) == qg.QGEMV_E_UNSUPPORTED
     assert _status("qgemm_q4_k_small_m", A, 8, 256, 65, A, A, A, A, 1, S) == qg.QGEMV_E_UNSUPPORTED
     assert _status("qgemm_q4_k_small_m", A, 8, 256, 4, A, A, A, A, 9, S) == qg.QGEMV_E_UNSUPPORTED
     assert _status("qgemv_block_dots", 7, A, 4, 256, 0, 4, A, A, S) == qg.QGEMV_E_UNSUPPORTED
+    assert _status(SW, A, 64, 65536, A, A, A, A, A, A, None, None, S) == qg.QGEMV_E_UNSUPPORTED
     # alignment
     assert _status("qgemv_q4_k", A + 8, 10, 256, A, A, A, A, S) == qg.QGEMV_E_ALIGN
     assert _status("qgemv_q4_k", A, 10, 256, A + 4, A, A, A, S) == qg.QGEMV_E_ALIGN
@@ -99,6 +107,12 @@ def test_gates_null_shape_limits_align():
     assert _status("qgemv_q4_k", A, 10, 256, A, A, A, A + 2, S) == qg.QGEMV_E_ALIGN
     assert _status("qgemv_quantize_act", A + 2, 1, 32, 32, A, A, A, S) == qg.QGEMV_E_ALIGN
     assert _status("qgemv_silu_mul_quantize", A, 64, A, A, A, A + 1, S) == qg.QGEMV_E_ALIGN
+    assert _status(SW, A + 8, 64, 256, A, A, A, A, A, A, None, None, S) == qg.QGEMV_E_ALIGN
+    assert _status(SW, A, 64, 256, A, A, A, A + 4, A, A, None, None, S) == qg.QGEMV_E_ALIGN
+    assert _status(SW, A, 64, 256, A, A, A, A, A + 1, A, None, None, S) == qg.QGEMV_E_ALIGN
+    assert _status(SW, A, 64, 256, A, A, A, A, A, A + 2, None, None, S) == qg.QGEMV_E_ALIGN
+    assert _status(SW, A, 64, 256, A, A, A, A, A, A, A + 2, None, S) == qg.QGEMV_E_ALIGN
+    assert _status(SW, A, 64, 256, A, A, A, A, A, A, None, A + 1, S) == qg.QGEMV_E_ALIGN
     assert "aligned" in qg.qgemv_last_error()
 
 
