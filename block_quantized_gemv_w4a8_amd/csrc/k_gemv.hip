@@ -462,8 +462,14 @@ __global__ __launch_bounds__(WG) void k_gemv_lds(const uint8_t* __restrict__ w, 
     const int64_t ngroups = ((int64_t)N + RPP - 1) / RPP;
     constexpr int GPB = 64 / RPP;   // SW: row groups (passes) per output block
     const int64_t nhb = SW ? so.nh / 32 : 0;
+    const int64_t npass_all =
+        SW ? (nhb > (int64_t)blockIdx.x ? (nhb - blockIdx.x + G - 1) / G : 0) * GPB
+           : (ngroups > (int64_t)blockIdx.x ? (ngroups - blockIdx.x + G - 1) / G : 0);
     auto row_of = [&](int64_t p) -> int64_t {
         if (!SW) return (blockIdx.x + p * G) * RPP + rg;
+        // the prefetch runs up to two passes past the last one: keep it on
+        // this workgroup's last rows (cached) rather than other blocks' rows
+        p = min(p, npass_all - 1);
         const int64_t hb = blockIdx.x + (p / GPB) * G;
         const int l = (int)(p % GPB) * RPP + rg;   // 0..31 gate, 32..63 up
         return l < 32 ? 32 * hb + l : so.nh + 32 * hb + (l - 32);
@@ -514,9 +520,6 @@ __global__ __launch_bounds__(WG) void k_gemv_lds(const uint8_t* __restrict__ w, 
         if (lane == LPR - 1) part[(pl * RPP + rg) * WK + kq] = acc;
     };
 
-    const int64_t npass_all =
-        SW ? (nhb > (int64_t)blockIdx.x ? (nhb - blockIdx.x + G - 1) / G : 0) * GPB
-           : (ngroups > (int64_t)blockIdx.x ? (ngroups - blockIdx.x + G - 1) / G : 0);
     static_assert(SEGP % GPB == 0, "a segment holds whole output blocks");
     for (int64_t p0 = 0; p0 < npass_all; p0 += SEGP) {
         const int np = (int)min((int64_t)SEGP, npass_all - p0);
