@@ -461,6 +461,34 @@ def extras(qg, torch, np, synth, dev, R, c2, c3, args):
     ex["config4_small_m_q4_k_14336x4096"] = sm
     del w4
 
+    # the prefill chunk through the down projection: Q6_K 4096 x 14336
+    g6 = np.random.default_rng(11)
+    N6, K6 = 4096, 14336
+    w6h = synth.q6_k_weights(g6, N6, K6)
+    w6 = [torch.from_numpy(w6h).to(dev)]
+    for _ in range(10):
+        w6.append(w6[0].clone())
+    x6, _ = synth.activation(g6, 64, K6)
+    sm6 = {}
+    for M in (1, 2, 4, 8, 16, 32, 64):
+        xm = torch.from_numpy(np.ascontiguousarray(x6[:M])).to(dev)
+        qm, dm, smm = qg.act_buffers(M, K6, dev)
+        qg.qgemv_quantize_act(xm, M, K6, K6, qm, dm, smm)
+        ym = torch.empty((M, N6), dtype=torch.float32, device=dev)
+        for vname, v in (("gemv_rows", qg.QGEMV_VARIANT_DOT4), ("mfma", qg.QGEMV_VARIANT_MFMA)):
+            us = time_kernel(torch, lambda c: qg.qgemm_q6_k_small_m(
+                w6[c], N6, K6, M, qm, dm, smm, ym, v), 50, 11)
+            sm6[f"M{M}_{vname}_us"] = round(us, 2)
+    wb6 = synth.logical_bytes("q6_k", N6, K6)
+    for M in (8, 64):
+        sm6[f"M{M}_mfma_weight_GBps"] = round(wb6 / sm6[f"M{M}_mfma_us"] / 1e3, 1)
+        sm6[f"M{M}_mfma_int8_TOPS"] = round(2 * M * N6 * K6 / sm6[f"M{M}_mfma_us"] / 1e6, 1)
+    sm6["crossover_M_mfma_faster_from"] = next(
+        (M for M in (1, 2, 4, 8, 16, 32, 64) if sm6[f"M{M}_mfma_us"] < sm6[f"M{M}_gemv_rows_us"]),
+        None)
+    ex["small_m_q6_k_4096x14336"] = sm6
+    del w6
+
     # plain device copy: the achievable HBM figure beside the datasheet peak
     a = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
     b = torch.empty_like(a)

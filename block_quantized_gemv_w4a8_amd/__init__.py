@@ -40,7 +40,8 @@ QGEMV_M_MAX = 64
 EXPORTS = [
     "qgemv_abi_version", "qgemv_status_str", "qgemv_build_info", "qgemv_last_error",
     "qgemv_quantize_act", "qgemv_q4_0", "qgemv_q4_k", "qgemv_q6_k", "qgemv_q8_0",
-    "qgemm_q4_k_small_m", "qgemv_silu_mul_quantize", "qgemv_q4_k_swiglu_quantize",
+    "qgemm_q4_k_small_m", "qgemm_q6_k_small_m", "qgemm_q4_0_small_m",
+    "qgemv_silu_mul_quantize", "qgemv_q4_k_swiglu_quantize",
     "qgemv_block_dots",
 ]
 
@@ -58,8 +59,9 @@ _lib.qgemv_quantize_act.argtypes = [_P, _I64, _I64, _I64, _P, _P, _P, _P]
 for _n in ("qgemv_q4_0", "qgemv_q4_k", "qgemv_q6_k", "qgemv_q8_0"):
     getattr(_lib, _n).restype = _I
     getattr(_lib, _n).argtypes = [_P, _I64, _I64, _P, _P, _P, _P, _P]
-_lib.qgemm_q4_k_small_m.restype = _I
-_lib.qgemm_q4_k_small_m.argtypes = [_P, _I64, _I64, _I64, _P, _P, _P, _P, _I, _P]
+for _n in ("qgemm_q4_k_small_m", "qgemm_q6_k_small_m", "qgemm_q4_0_small_m"):
+    getattr(_lib, _n).restype = _I
+    getattr(_lib, _n).argtypes = [_P, _I64, _I64, _I64, _P, _P, _P, _P, _I, _P]
 _lib.qgemv_silu_mul_quantize.restype = _I
 _lib.qgemv_silu_mul_quantize.argtypes = [_P, _I64, _P, _P, _P, _P, _P]
 _lib.qgemv_q4_k_swiglu_quantize.restype = _I
@@ -148,6 +150,20 @@ def qgemv_q8_0(w, N, K, q, d, s, y, stream=None):
 def qgemm_q4_k_small_m(w, N, K, M, q, d, s, y, variant=QGEMV_VARIANT_AUTO, stream=None):
     return _check(_lib.qgemm_q4_k_small_m(_ptr(w), N, K, M, _ptr(q), _ptr(d), _ptr(s), _ptr(y),
                                           variant, _stream(stream)), "qgemm_q4_k_small_m")
+
+
+def qgemm_q6_k_small_m(w, N, K, M, q, d, s, y, variant=QGEMV_VARIANT_AUTO, stream=None):
+    return _check(_lib.qgemm_q6_k_small_m(_ptr(w), N, K, M, _ptr(q), _ptr(d), _ptr(s), _ptr(y),
+                                          variant, _stream(stream)), "qgemm_q6_k_small_m")
+
+
+def qgemm_q4_0_small_m(w, N, K, M, q, d, s, y, variant=QGEMV_VARIANT_AUTO, stream=None):
+    return _check(_lib.qgemm_q4_0_small_m(_ptr(w), N, K, M, _ptr(q), _ptr(d), _ptr(s), _ptr(y),
+                                          variant, _stream(stream)), "qgemm_q4_0_small_m")
+
+
+SMALL_M = {"q4_k": qgemm_q4_k_small_m, "q6_k": qgemm_q6_k_small_m,
+           "q4_0": qgemm_q4_0_small_m}
 
 
 def qgemv_silu_mul_quantize(gu, N, q, d, s, h=None, stream=None):

@@ -306,33 +306,8 @@ __global__ __launch_bounds__(WG) void k_gemv(const uint8_t* __restrict__ w, int 
 // chunk grid is aligned to 16-byte global addresses, see k_gemv_lds).  Q4_K
 // fields are 16-byte aligned there; Q6_K, Q4_0 and Q8_0 blocks start every
 // 210, 18 or 34 bytes, so their fields can sit 2 bytes off a 4-byte boundary.
-// Those are read as aligned dwords and shifted into place with v_alignbyte:
-// unaligned LDS accesses stall the LDS pipeline on this chip, aligned dword
-// reads do not.
-__device__ __forceinline__ u32x4 lds16(const uint8_t* base, int off) {
-    return *reinterpret_cast<const u32x4*>(base + off);
-}
-__device__ __forceinline__ uint32_t lds2(const uint8_t* base, int off) {
-    return *reinterpret_cast<const uint16_t*>(base + off);
-}
-__device__ __forceinline__ uint32_t abyte(uint32_t hi, uint32_t lo, uint32_t sh) {
-    return __builtin_amdgcn_alignbyte(hi, lo, sh);
-}
-// 16 bytes at any even LDS offset (reads up to 4 bytes past the field).
-__device__ __forceinline__ u32x4 lds16_a2(const uint8_t* base, int off) {
-    const uint32_t* d = reinterpret_cast<const uint32_t*>(base + (off & ~3));
-    const uint32_t sh = off & 3;
-    const uint32_t w0 = d[0], w1 = d[1], w2 = d[2], w3 = d[3], w4 = d[4];
-    return u32x4{abyte(w1, w0, sh), abyte(w2, w1, sh), abyte(w3, w2, sh), abyte(w4, w3, sh)};
-}
-// 8 bytes at any even LDS offset.
-__device__ __forceinline__ u32x2 lds8_a2(const uint8_t* base, int off) {
-    const uint32_t* d = reinterpret_cast<const uint32_t*>(base + (off & ~3));
-    const uint32_t sh = off & 3;
-    const uint32_t w0 = d[0], w1 = d[1], w2 = d[2];
-    return u32x2{abyte(w1, w0, sh), abyte(w2, w1, sh)};
-}
-
+// Those are read as aligned dwords and shifted into place with v_alignbyte
+// (lds16_a2, lds8_a2 in qgemv_device.h).
 template <int FMT>
 struct UnitLds;
 template <>

@@ -122,31 +122,73 @@ __global__ __launch_bounds__(SWG) void k_small_m_dot4(const uint8_t* __restrict_
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// Weight units of the MFMA variant: 256 consecutive weights of a row, which
+// is a super-block of Q4_K (144 B) and Q6_K (210 B) and 8 blocks of Q4_0
+// (8 x 18 = 144 B).  Q4_K units always start on 16-byte boundaries; Q6_K and
+// Q4_0 units and rows only on 2-byte ones.
+template <int FMT>
+struct SmUnit;
+template <>
+struct SmUnit<QGEMV_FMT_Q4_K> {
+    static constexpr int UB = 144;
+    static constexpr bool ALIGNED = true;
+    static constexpr bool S16 = false;   // per-16 activation sums needed
+};
+template <>
+struct SmUnit<QGEMV_FMT_Q6_K> {
+    static constexpr int UB = 210;
+    static constexpr bool ALIGNED = false;
+    static constexpr bool S16 = true;
+};
+template <>
+struct SmUnit<QGEMV_FMT_Q4_0> {
+    static constexpr int UB = 144;
+    static constexpr bool ALIGNED = false;
+    static constexpr bool S16 = false;
+};
+
+// LDS stride (bytes) of at least `need` whose dword count is 4 mod 8: the 16
+// rows a wave reads at once then start on 16 different 4-bank groups.
+constexpr int odd_quad_stride(int need) {
+    int dw = (need + 3) / 4;
+    while (dw % 8 != 4) dw++;
+    return 4 * dw;
+}
+
 // Geometry of the MFMA variant.  A workgroup owns ROWS = 16*RT weight rows
-// and all MP = 16*MT activation rows, and walks K in steps of G super-blocks.
-// One step of its weights and activation sits in LDS (double-buffered):
-//   weights:    ROWS rows x (G*144 bytes + 16 pad), the row's G super-blocks
-//               as they lie in HBM
-//   activation: G x { codes [MP][256 + 16 pad], fp32 dx [8][MP], dx*s [8][MP] }
-// The pads put the 16 rows a wave reads at once on different LDS banks.
-template <int MT, int RT, int G>
+// and all MP = 16*MT activation rows, and walks K in steps of G units.  One
+// step of its weights and activation sits in LDS (double-buffered):
+//   weights:    ROWS rows x WSTRIDE; a row holds the step's SPAN = G*UB bytes
+//               as they lie in HBM (for unaligned formats starting at FRONT
+//               + delta, delta = the span's offset from the 16-byte boundary
+//               below it; the front pad takes a last chunk that was shifted
+//               back to end at the row end)
+//   activation: G x { codes [MP][256 + 16 pad], fp32 dx [8][MP], dx*s [8][MP]
+//               (, int32 sums of each 16 codes [16][MP] for Q6_K) }
+template <int FMT, int MT, int RT, int G>
 struct MfmaGeom {
+    using U = SmUnit<FMT>;
     static constexpr int MP = 16 * MT;
     static constexpr int ROWS = 16 * RT;
-    static constexpr int WSTRIDE = 144 * G + 16;
+    static constexpr int SPAN = U::UB * G;
+    static constexpr int NCH = U::ALIGNED ? SPAN / 16 : (SPAN + 14 + 15) / 16;
+    static constexpr int FRONT = U::ALIGNED ? 0 : 16;
+    static constexpr int WSTRIDE = U::ALIGNED ? SPAN + 16 : odd_quad_stride(FRONT + 16 * NCH + 16);
     static constexpr int WBYTES = ROWS * WSTRIDE;
     static constexpr int ASTRIDE = 272;
     static constexpr int ACODES = MP * ASTRIDE;
-    static constexpr int ASTAGE = ACODES + 2 * 8 * MP * 4;
+    static constexpr int ASCALE = 2 * 8 * MP * 4;
+    static constexpr int ASTAGE = ACODES + ASCALE + (U::S16 ? 16 * MP * 4 : 0);
     static constexpr int BUF = WBYTES + G * ASTAGE;
 };
 
-// Wave (rt, part) of the workgroup computes weight tile rt (rows 16*rt ..
-// 16*rt + 15) over sub-blocks part*BPW .. part*BPW + BPW-1 of every
-// super-block (BPW = 8/KS); the KS partial sums of a tile are added in LDS
-// at the end, always in part order.  Lane l: weight row 16*rt + l%16, K part
-// 8*(l/16) of each 32-block (the i8 MFMA operand layout); its outputs are
-// rows 16t + 4*(l/16) + i of that weight row.
+// Wave (rt, kq, ks) of the workgroup computes weight tile rt (rows 16*rt ..
+// 16*rt + 15) over units kq, kq + KP, ... of every step and, within each,
+// over 32-blocks ks*BPW .. ks*BPW + BPW-1 (BPW = 8/KS); the KS*KP partial
+// sums of a tile are added in LDS at the end, always in the same order.  KP
+// splits K between waves where the matrix has too few rows to fill the chip.  Lane l: weight row 16*rt + l%16, K part 8*(l/16) of
+// each 32-block (the i8 MFMA operand layout); its outputs are rows
+// 16t + 4*(l/16) + i of that weight row.
 //
 // The weights are read from HBM the way the GEMV reads them: each lane loads
 // 16 consecutive bytes and a wave instruction covers about 1 KB of
@@ -154,87 +196,121 @@ struct MfmaGeom {
 // (Loading the MFMA operand layout straight from HBM -- 16 rows x 8 bytes per
 // instruction -- costs several cache-line requests per 144-byte super-block
 // and leaves the kernel waiting on them.)
-template <int MT, int RT, int KS, int G, int R>
-__global__ __launch_bounds__(64 * RT * KS) void k_small_m_mfma(const uint8_t* __restrict__ w,
-                                                               int N, int Kp, int M,
+//
+// Per format, with D the 16 x 16 int32 tile of one 32-block (Q6_K: of one
+// 16-group, the other half of the K lanes zeroed) and unsigned codes:
+//   Q4_K  y += d*sc_j*dx*D  - (dmin*m_j)(dx*s)
+//   Q4_0  y += dw*dx*D      - (8*dw)(dx*s)          (w = dw*(code - 8))
+//   Q6_K  y += d*sc_g*dx*D  - (32*d*sc_g)(dx*sum16) (w = d*sc*(code - 32))
+// The second product of each line is a small dense product over the blocks
+// (groups) of a unit and goes to the fp32 MFMA.
+template <int FMT, int MT, int RT, int KS, int KP, int G, int R>
+__global__ __launch_bounds__(64 * RT * KS * KP) void k_small_m_mfma(const uint8_t* __restrict__ w,
+                                                               int N, int K, int Kp, int M,
                                                                const int8_t* __restrict__ q,
                                                                const uint16_t* __restrict__ d,
                                                                const int32_t* __restrict__ s,
                                                                float* __restrict__ y) {
-    static_assert(KS == 1 || KS == 2 || KS == 4, "sub-blocks split over 1, 2 or 4 waves");
-    using GM = MfmaGeom<MT, RT, G>;
-    constexpr int MP = GM::MP, ROWS = GM::ROWS;
-    constexpr int NT = 64 * RT * KS;                         // threads
-    constexpr int BPW = 8 / KS;                              // sub-blocks per wave and super-block
-    constexpr int WCH = ROWS * 9 * G;                        // 16-byte weight chunks per step
+    static_assert(KS == 1 || KS == 2 || KS == 4, "32-blocks split over 1, 2 or 4 waves");
+    static_assert(G % KP == 0 && (KP > 1 || G <= 2), "units of a step split evenly over KP");
+    using GM = MfmaGeom<FMT, MT, RT, G>;
+    using U = SmUnit<FMT>;
+    constexpr int MP = GM::MP, ROWS = GM::ROWS, NCH = GM::NCH;
+    constexpr int NT = 64 * RT * KS * KP;                    // threads
+    constexpr int BPW = 8 / KS;                              // 32-blocks per wave and unit
+    constexpr int WCH = ROWS * NCH;                          // 16-byte weight chunks per step
     constexpr int WPT = (WCH + NT - 1) / NT;
     constexpr int ACH = G * MP * 16;                         // 16-byte code chunks per step
     constexpr int APT = (ACH + NT - 1) / NT;
     constexpr int SCH = G * 8 * MP;                          // scale entries per step
     constexpr int SPT = (SCH + NT - 1) / NT;
-    constexpr int PART_BYTES = (KS - 1) * RT * MT * 4 * 64 * 4;
+    constexpr int NPART = KS * KP;                           // partial sums per tile
+    constexpr int PART_BYTES = (NPART - 1) * RT * MT * 4 * 64 * 4;
     constexpr int SMEM = 2 * GM::BUF > PART_BYTES ? 2 * GM::BUF : PART_BYTES;
     __shared__ __align__(16) uint8_t smem[SMEM];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int rt = wave % RT, part = wave / RT;
+    const int rt = wave % RT, part = wave / RT;               // part = ks + KS * kq
+    const int ks = part % KS, kq = part / KS;
     const int nl = lane & 15, kp = lane >> 4;
     const int row0 = blockIdx.x * ROWS;
     const int n = row0 + 16 * rt + nl;
-    const int nsb = Kp / 256, nb = Kp / 32;
-    const int nsteps = (nsb + G - 1) / G;
-    const int64_t row_bytes = (int64_t)nsb * Q4K::SB_BYTES;
+    const int nunits = Kp / 256, nb = Kp / 32;
+    const int nbw = K / 32;                                  // weight blocks of a Q4_0 row
+    const int nsteps = (nunits + G - 1) / G;
+    const int64_t row_bytes = FMT == QGEMV_FMT_Q4_0 ? (int64_t)nbw * 18 : (int64_t)nunits * U::UB;
+    const uint8_t* my_row = w + (int64_t)min(n, N - 1) * row_bytes;
+
+    // 16-byte-aligned start of row r's span in step st, and the span's offset from it
+    auto span_base = [&](const uint8_t* rowp, int st, int& delta) {
+        const uint8_t* a = rowp + (int64_t)GM::SPAN * st;
+        delta = (int)((uintptr_t)a & 15);
+        return a - delta;
+    };
 
     // One step's global data in registers between load and LDS store.  Every
     // load is issued unconditionally with its address clamped into the
-    // buffers (rows past N re-read row N-1, super-blocks past K re-read the
-    // last one, activation rows past M re-read row M-1; none of those reach
-    // a stored output): a load behind a branch makes the compiler drain all
-    // outstanding loads.
+    // buffers (rows past N re-read row N-1, units past K re-read the last
+    // one or the row's last 16 bytes, activation rows past M re-read row
+    // M-1; none of those reach a stored output): a load behind a branch makes
+    // the compiler drain all outstanding loads.
     struct Regs {
         u32x4 wc[WPT];
         u32x4 ac[APT];
         uint32_t dh[SPT];
         int32_t sv[SPT];
     };
+    auto chunk_ptr = [&](int st, int c, int& lds_off) {
+        const int row = c / NCH, k = c - row * NCH;
+        const uint8_t* rowp = w + (int64_t)min(row0 + row, N - 1) * row_bytes;
+        if (U::ALIGNED) {
+            const int unit = min(G * st + k / 9, nunits - 1);
+            lds_off = row * GM::WSTRIDE + 16 * k;
+            return rowp + U::UB * unit + 16 * (k % 9);
+        }
+        int delta;
+        const uint8_t* a0 = span_base(rowp, st, delta);
+        const uint8_t* p = a0 + 16 * k;
+        const uint8_t* last = rowp + row_bytes - 16;
+        if (p > last) p = last;
+        lds_off = row * GM::WSTRIDE + GM::FRONT + (int)(p - a0);
+        return p;
+    };
     auto load_step = [&](int st, Regs& r) {
 #pragma unroll
         for (int k = 0; k < WPT; k++) {
-            const int c = min(tid + NT * k, WCH - 1);
-            const int row = c / (9 * G), off = c - row * (9 * G);
-            const int sb = min(G * st + off / 9, nsb - 1);
-            const uint8_t* p = w + (int64_t)min(row0 + row, N - 1) * row_bytes +
-                               Q4K::SB_BYTES * sb + 16 * (off % 9);
-            r.wc[k] = *reinterpret_cast<const u32x4*>(p);
+            int lo;
+            r.wc[k] = ld16(chunk_ptr(st, min(tid + NT * k, WCH - 1), lo));
         }
 #pragma unroll
         for (int k = 0; k < APT; k++) {
             const int c = min(tid + NT * k, ACH - 1);
             const int g = c / (MP * 16), rem = c - g * (MP * 16);
             const int m = min(rem >> 4, M - 1), cc = rem & 15;
-            const int sb = min(G * st + g, nsb - 1);
-            r.ac[k] = *reinterpret_cast<const u32x4*>(q + (int64_t)m * Kp + 256 * sb + 16 * cc);
+            const int u = min(G * st + g, nunits - 1);
+            r.ac[k] = *reinterpret_cast<const u32x4*>(q + (int64_t)m * Kp + 256 * u + 16 * cc);
         }
 #pragma unroll
         for (int k = 0; k < SPT; k++) {
             const int c = min(tid + NT * k, SCH - 1);
             const int g = c / (8 * MP), rem = c - g * (8 * MP);
             const int j = rem / MP, m = min(rem - j * MP, M - 1);
-            const int sb = min(G * st + g, nsb - 1);
-            const int64_t b = (int64_t)m * nb + 8 * sb + j;
+            const int u = min(G * st + g, nunits - 1);
+            const int64_t b = (int64_t)m * nb + 8 * u + j;
             r.dh[k] = d[b];
             r.sv[k] = s[b];
         }
     };
-    auto store_step = [&](const Regs& r, int buf) {
+    auto store_step = [&](const Regs& r, int buf, int st) {
         uint8_t* base = smem + buf * GM::BUF;
 #pragma unroll
         for (int k = 0; k < WPT; k++) {
             const int c = tid + NT * k;
             if (c < WCH) {
-                const int row = c / (9 * G), off = c - row * (9 * G);
-                *reinterpret_cast<u32x4*>(base + row * GM::WSTRIDE + 16 * off) = r.wc[k];
+                int lo;
+                (void)chunk_ptr(st, c, lo);
+                *reinterpret_cast<u32x4*>(base + lo) = r.wc[k];
             }
         }
         uint8_t* act = base + GM::WBYTES;
@@ -245,6 +321,15 @@ __global__ __launch_bounds__(64 * RT * KS) void k_small_m_mfma(const uint8_t* __
                 const int g = c / (MP * 16), rem = c - g * (MP * 16);
                 *reinterpret_cast<u32x4*>(act + g * GM::ASTAGE + (rem >> 4) * GM::ASTRIDE +
                                           16 * (rem & 15)) = r.ac[k];
+                if (U::S16) {
+                    // sum of these 16 codes (the 16-group rem & 15 of row rem >> 4)
+                    int t = dot4(r.ac[k].x, 0x01010101u, 0);
+                    t = dot4(r.ac[k].y, 0x01010101u, t);
+                    t = dot4(r.ac[k].z, 0x01010101u, t);
+                    t = dot4(r.ac[k].w, 0x01010101u, t);
+                    int* s16 = reinterpret_cast<int*>(act + g * GM::ASTAGE + GM::ACODES + GM::ASCALE);
+                    s16[(rem & 15) * MP + (rem >> 4)] = t;
+                }
             }
         }
 #pragma unroll
@@ -260,9 +345,11 @@ __global__ __launch_bounds__(64 * RT * KS) void k_small_m_mfma(const uint8_t* __
         }
     };
 
-    // one accumulator set per super-block of a step (G independent chains),
-    // or a single set where MT is large and registers are short
-    constexpr int AG = MT >= 3 ? 1 : G;
+    // one accumulator set per unit of a step (G independent chains), or a
+    // single set, with the block order pinned, where MT is large and
+    // registers are short (Q6_K and Q4_0 need more registers per block)
+    constexpr bool BIG = FMT == QGEMV_FMT_Q4_K ? MT >= 3 : MT >= 2;
+    constexpr int AG = (BIG || KP > 1) ? 1 : G;
     f32x4 acc[AG][MT], acc2[AG][MT];
 #pragma unroll
     for (int g = 0; g < AG; g++)
@@ -272,64 +359,127 @@ __global__ __launch_bounds__(64 * RT * KS) void k_small_m_mfma(const uint8_t* __
             acc2[g][t] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
     const i32x4 zero = {0, 0, 0, 0};
+    constexpr int ND = FMT == QGEMV_FMT_Q6_K ? 2 : 1;   // MFMAs (16-groups) per 32-block
 
-    // Super-block g of the step in LDS buffer buf, for part P of the
-    // sub-blocks (P is the wave's part as a compile-time constant, so the
-    // scale bytes and LDS offsets of its sub-blocks are constants too).
-    // With PIN set (large MT) empty volatile asm statements make the MFMAs of
-    // sub-block jj+1 go out before the scaling of jj and keep every other
-    // sub-block in order; without them the compiler issues all the MFMAs
-    // first and holds all their results in registers.  At small MT it may.
-    // A super-block past the end of K (the tail of the last step) holds a
-    // copy of the last one; its scales are taken as zero, so it adds exact
-    // zeros.
-    auto compute_sb = [&](auto Pc, auto Gc, int buf, bool valid) {
+    // Unit g of the step in LDS buffer buf, for part P of the 32-blocks (P is
+    // the wave's part as a compile-time constant, so field offsets within
+    // the unit are constants too).  With PIN set (large MT) empty volatile
+    // asm statements make the MFMAs of block jj+1 go out before the scaling
+    // of jj and keep every other block in order; without them the compiler
+    // issues all the MFMAs first and holds all their results in registers.
+    // A unit past the end of K (the tail of the last step) holds stale bytes;
+    // its scales are taken as zero, so it adds exact zeros (Q4_0 does the
+    // same per block for the blocks of a partial last unit).
+    auto compute_sb = [&](auto Pc, auto GAc, int g, int buf, int st, bool valid) {
         constexpr int P = decltype(Pc)::value;
-        constexpr int g = decltype(Gc)::value;
-        constexpr int ga = g < AG ? g : AG - 1;   // accumulator set
-        constexpr bool PIN = MT >= 3;
-        const int ow = buf * GM::BUF + (16 * rt + nl) * GM::WSTRIDE + Q4K::SB_BYTES * g;
-        const u32x4 hdr = *reinterpret_cast<const u32x4*>(smem + ow);
-        const float fd = valid ? h2f(hdr.x & 0xFFFFu) : 0.0f;
-        const float fdm = valid ? h2f(hdr.x >> 16) : 0.0f;
-        // 6-bit scales of sub-blocks 0..3 (bytes of hdr.y) and 4..7 (low
-        // nibbles of hdr.w, high bits from the top of hdr.y), four per dword
-        const uint32_t slo = hdr.y & 0x3F3F3F3Fu;
-        const uint32_t shi = (hdr.w & LO4) | ((hdr.y >> 2) & 0x30303030u);
+        constexpr int ga = decltype(GAc)::value;   // accumulator set
+        constexpr bool PIN = BIG;
+        int delta = 0;
+        if (!U::ALIGNED) (void)span_base(my_row, st, delta);
+        const int ow = buf * GM::BUF + (16 * rt + nl) * GM::WSTRIDE + GM::FRONT + delta + U::UB * g;
         const int oa = buf * GM::BUF + GM::WBYTES + g * GM::ASTAGE;
-        auto mfma_block = [&](int jj, i32x4 (&D)[MT]) {
+        const int blk0 = 8 * (G * st + g);        // first 32-block of the unit
+        const float* dxs = reinterpret_cast<const float*>(smem + oa + GM::ACODES + 4 * 8 * MP);
+
+        // format fields of this lane's row
+        float fd = 0.0f, fdm = 0.0f;
+        uint32_t slo = 0, shi = 0, mlo = 0, mhi = 0;
+        if constexpr (FMT == QGEMV_FMT_Q4_K) {
+            const u32x4 hdr = *reinterpret_cast<const u32x4*>(smem + ow);
+            fd = valid ? h2f(hdr.x & 0xFFFFu) : 0.0f;
+            fdm = valid ? h2f(hdr.x >> 16) : 0.0f;
+            // 6-bit scales of sub-blocks 0..3 (bytes of hdr.y) and 4..7 (low
+            // nibbles of hdr.w, high bits from the top of hdr.y); the mins:
+            // bytes of hdr.z, or high nibbles of hdr.w with bits from hdr.z
+            slo = hdr.y & 0x3F3F3F3Fu;
+            shi = (hdr.w & LO4) | ((hdr.y >> 2) & 0x30303030u);
+            mlo = hdr.z & 0x3F3F3F3Fu;
+            mhi = ((hdr.w >> 4) & LO4) | ((hdr.z >> 2) & 0x30303030u);
+        } else if constexpr (FMT == QGEMV_FMT_Q6_K) {
+            fd = valid ? h2f(lds2(smem, ow + 208)) : 0.0f;
+        }
+        // Q4_0: the scale of block j of the unit (zero past the row's blocks)
+        auto q40_scale = [&](int j) {
+            return blk0 + j < nbw ? h2f(lds2(smem, ow + 18 * j)) : 0.0f;
+        };
+
+        auto mfma_block = [&](int jj, i32x4 (&D)[ND][MT]) {
             const int j = P * BPW + jj;
-            int o = ow + 16 + 32 * (j >> 1) + 8 * kp;
             int o2 = oa + 32 * j;
-            if (PIN) asm volatile("" : "+v"(o), "+s"(o2));
-            const u32x2 v = *reinterpret_cast<const u32x2*>(smem + o);
-            const int sh = 4 * (j & 1);
-            const long B = (long)(((uint64_t)((v.y >> sh) & LO4) << 32) | ((v.x >> sh) & LO4));
+            long B[ND];
+            if constexpr (FMT == QGEMV_FMT_Q4_K) {
+                int o = ow + 16 + 32 * (j >> 1) + 8 * kp;
+                if (PIN) asm volatile("" : "+v"(o), "+s"(o2));
+                const u32x2 v = *reinterpret_cast<const u32x2*>(smem + o);
+                const int sh = 4 * (j & 1);
+                B[0] = (long)(((uint64_t)((v.y >> sh) & LO4) << 32) | ((v.x >> sh) & LO4));
+            } else if constexpr (FMT == QGEMV_FMT_Q4_0) {
+                // block j: element i < 16 = low nibble of byte i, i + 16 = high
+                int o = ow + 18 * j + 2 + 8 * (kp & 1);
+                if (PIN) asm volatile("" : "+v"(o), "+s"(o2));
+                const u32x2 v = lds8_a2(smem, o);
+                const int sh = 4 * (kp >> 1);
+                B[0] = (long)(((uint64_t)((v.y >> sh) & LO4) << 32) | ((v.x >> sh) & LO4));
+            } else {
+                // block j = 4h + t: element l of it = low (t < 2) or high
+                // (t >= 2) nibble of ql[64h + 32(t&1) + l], plus bits 2t..2t+1
+                // of qh[32h + l] as bits 4..5
+                const int h = j >> 2, t = j & 3;
+                int o = ow + 64 * h + 32 * (t & 1) + 8 * kp;
+                int oh = ow + 128 + 32 * h + 8 * kp;
+                if (PIN) asm volatile("" : "+v"(o), "+v"(oh), "+s"(o2));
+                const u32x2 ql = lds8_a2(smem, o);
+                const u32x2 qh = lds8_a2(smem, oh);
+                const int s1 = 4 * (t >> 1), s2 = 2 * t;
+                const uint32_t c0 = ((ql.x >> s1) & LO4) | (((qh.x >> s2) & 0x03030303u) << 4);
+                const uint32_t c1 = ((ql.y >> s1) & LO4) | (((qh.y >> s2) & 0x03030303u) << 4);
+                const long Bc = (long)(((uint64_t)c1 << 32) | c0);
+                // 16-group 2j is K lanes kp < 2, group 2j+1 kp >= 2
+                B[0] = kp < 2 ? Bc : 0;
+                B[1] = kp < 2 ? 0 : Bc;
+            }
 #pragma unroll
             for (int t = 0; t < MT; t++) {
                 const long A = *reinterpret_cast<const long*>(
                     smem + o2 + (16 * t + nl) * GM::ASTRIDE + 8 * kp);
-                D[t] = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, B, zero, 0, 0, 0);
+#pragma unroll
+                for (int e = 0; e < ND; e++)
+                    D[e][t] = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, B[e], zero, 0, 0, 0);
             }
         };
-        auto scale_block = [&](int jj, const i32x4 (&D)[MT]) {
+        auto scale_block = [&](int jj, const i32x4 (&D)[ND][MT]) {
             const int j = P * BPW + jj;
-            const float wsj = fd * (float)(((j >= 4 ? shi : slo) >> (8 * (j & 3))) & 0xFFu);
+            float ws0, ws1 = 0.0f;
+            if constexpr (FMT == QGEMV_FMT_Q4_K) {
+                ws0 = fd * (float)(((j >= 4 ? shi : slo) >> (8 * (j & 3))) & 0xFFu);
+            } else if constexpr (FMT == QGEMV_FMT_Q4_0) {
+                ws0 = q40_scale(j);
+            } else {
+                const uint32_t sc = lds2(smem, ow + 192 + 2 * j);   // int8 scales of 2j, 2j+1
+                ws0 = fd * (float)sbyte(sc, 0);
+                ws1 = fd * (float)sbyte(sc, 1);
+            }
             int o = oa + GM::ACODES + 4 * j * MP;
             if (PIN) asm volatile("" : "+s"(o));
 #pragma unroll
             for (int t = 0; t < MT; t++) {
                 const f32x4 x4 = *reinterpret_cast<const f32x4*>(smem + o + 4 * (16 * t + 4 * kp));
 #pragma unroll
-                for (int i = 0; i < 4; i++)
-                    acc[ga][t][i] = fmaf((float)D[t][i], wsj * x4[i], acc[ga][t][i]);
+                for (int i = 0; i < 4; i++) {
+                    if constexpr (ND == 1) {
+                        acc[ga][t][i] = fmaf((float)D[0][t][i], ws0 * x4[i], acc[ga][t][i]);
+                    } else {
+                        const float v = fmaf((float)D[1][t][i], ws1, (float)D[0][t][i] * ws0);
+                        acc[ga][t][i] = fmaf(v, x4[i], acc[ga][t][i]);
+                    }
+                }
             }
             if (PIN) {
 #pragma unroll
                 for (int t = 0; t < MT; t++) asm volatile("" : "+v"(acc[ga][t]));
             }
         };
-        i32x4 D2[2][MT];
+        i32x4 D2[2][ND][MT];
         mfma_block(0, D2[0]);
 #pragma unroll
         for (int jj = 1; jj < BPW; jj++) {
@@ -337,41 +487,65 @@ __global__ __launch_bounds__(64 * RT * KS) void k_small_m_mfma(const uint8_t* __
             scale_block(jj - 1, D2[(jj - 1) & 1]);
         }
         scale_block(BPW - 1, D2[(BPW - 1) & 1]);
-        // min term: rows m x sub-blocks j (dx*s) times sub-blocks j x this
-        // lane's row (dmin*m_j); MFMA K lane kp carries sub-block 4*kk + kp,
-        // and lanes whose sub-block belongs to another wave contribute zero.
-        // The 6-bit mins: bytes of hdr.z (sub-blocks 0..3), or high nibbles
-        // of hdr.w with high bits from the top of hdr.z (4..7).
-        const uint32_t mlo = hdr.z & 0x3F3F3F3Fu;
-        const uint32_t mhi = ((hdr.w >> 4) & LO4) | ((hdr.z >> 2) & 0x30303030u);
-        const float* dxs = reinterpret_cast<const float*>(smem + oa + GM::ACODES + 4 * 8 * MP);
+
+        // the second products: K lane kp of an fp32 MFMA carries one block
+        // (Q4_K, Q4_0: block 4*kk + kp of the unit, lanes whose block belongs
+        // to another wave contribute zero) or one 16-group (Q6_K)
+        if constexpr (FMT == QGEMV_FMT_Q6_K) {
+            const int* s16 = reinterpret_cast<const int*>(smem + oa + GM::ACODES + GM::ASCALE);
+            const float* dx = reinterpret_cast<const float*>(smem + oa + GM::ACODES);
 #pragma unroll
-        for (int kk = 0; kk < (BPW == 8 ? 2 : 1); kk++) {
-            constexpr int JB = BPW == 8 ? 0 : (P * BPW) & ~3;   // first sub-block of the group
-            const int jg = BPW == 8 ? 4 * kk : JB;
-            const bool mine = BPW >= 4 || (kp >> 1) == (P & 1);
-            const uint32_t mb = jg >= 4 ? mhi : mlo;
-            const float b = mine ? fdm * (float)bfe(mb, 8 * kp, 8) : 0.0f;
+            for (int kk = 0; kk < BPW / 2; kk++) {
+                const int gi = 2 * P * BPW + 4 * kk + kp;   // this lane's 16-group
+                const uint32_t sc = lds2(smem, ow + 192 + (gi & ~1));
+                const float b = 32.0f * fd * (float)sbyte(sc, gi & 1);
 #pragma unroll
-            for (int t = 0; t < MT; t++) {
-                const float a = dxs[(jg + kp) * MP + 16 * t + nl];
-                acc2[ga][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc2[ga][t], 0, 0, 0);
+                for (int t = 0; t < MT; t++) {
+                    const int m = 16 * t + nl;
+                    const float a = dx[(gi >> 1) * MP + m] * (float)s16[gi * MP + m];
+                    acc2[ga][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc2[ga][t], 0, 0, 0);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int kk = 0; kk < (BPW == 8 ? 2 : 1); kk++) {
+                constexpr int JB = BPW == 8 ? 0 : (P * BPW) & ~3;   // first block of the group
+                const int jg = BPW == 8 ? 4 * kk : JB;
+                const bool mine = BPW >= 4 || (kp >> 1) == (P & 1);
+                float b;
+                if constexpr (FMT == QGEMV_FMT_Q4_K) {
+                    const uint32_t mb = jg >= 4 ? mhi : mlo;
+                    b = mine ? fdm * (float)bfe(mb, 8 * kp, 8) : 0.0f;
+                } else {
+                    b = mine ? 8.0f * q40_scale(jg + kp) : 0.0f;
+                }
+#pragma unroll
+                for (int t = 0; t < MT; t++) {
+                    const float a = dxs[(jg + kp) * MP + 16 * t + nl];
+                    acc2[ga][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc2[ga][t], 0, 0, 0);
+                }
             }
         }
     };
     auto compute_part = [&](auto Pc, int buf, int st) {
-        compute_sb(Pc, std::integral_constant<int, 0>{}, buf, true);
-        if (G > 1) compute_sb(Pc, std::integral_constant<int, (G > 1 ? 1 : 0)>{}, buf, G * st + 1 < nsb);
-        static_assert(G <= 2, "one or two super-blocks per step");
+        if (KP == 1) {
+            compute_sb(Pc, std::integral_constant<int, 0>{}, 0, buf, st, true);
+            if (G > 1)
+                compute_sb(Pc, std::integral_constant<int, (AG > 1 ? 1 : 0)>{}, 1, buf, st,
+                           G * st + 1 < nunits);
+        } else {
+            for (int g = kq; g < G; g += KP)
+                compute_sb(Pc, std::integral_constant<int, 0>{}, g, buf, st, G * st + g < nunits);
+        }
     };
     auto compute_step = [&](int buf, int st) {
         if (KS == 1) {
             compute_part(std::integral_constant<int, 0>{}, buf, st);
         } else if (KS == 2) {
-            if (part == 0) compute_part(std::integral_constant<int, 0>{}, buf, st);
+            if (ks == 0) compute_part(std::integral_constant<int, 0>{}, buf, st);
             else compute_part(std::integral_constant<int, 1>{}, buf, st);
         } else {
-            switch (part) {
+            switch (ks) {
             case 0: compute_part(std::integral_constant<int, 0>{}, buf, st); break;
             case 1: compute_part(std::integral_constant<int, 1>{}, buf, st); break;
             case 2: compute_part(std::integral_constant<int, 2>{}, buf, st); break;
@@ -393,7 +567,7 @@ __global__ __launch_bounds__(64 * RT * KS) void k_small_m_mfma(const uint8_t* __
             load_step(min(st + R, nsteps - 1), rg[r]);
             __builtin_amdgcn_sched_barrier(0);
             if (st >= 0 && st < nsteps) compute_step(st & 1, st);
-            if (st + 1 >= 0 && st + 1 < nsteps) store_step(rg[(r + 1) % R], (st + 1) & 1);
+            if (st + 1 >= 0 && st + 1 < nsteps) store_step(rg[(r + 1) % R], (st + 1) & 1, st + 1);
             __syncthreads();
         }
     }
@@ -410,13 +584,13 @@ __global__ __launch_bounds__(64 * RT * KS) void k_small_m_mfma(const uint8_t* __
     auto pidx = [&](int p, int t, int i) {
         return (((p - 1) * RT + rt) * MT * 4 + 4 * t + i) * 64 + lane;
     };
-    if (KS > 1 && part > 0) {
+    if (NPART > 1 && part > 0) {
 #pragma unroll
         for (int t = 0; t < MT; t++)
 #pragma unroll
             for (int i = 0; i < 4; i++) pbuf[pidx(part, t, i)] = partial(t, i);
     }
-    if (KS > 1) __syncthreads();
+    if (NPART > 1) __syncthreads();
     if (part == 0 && n < N) {
 #pragma unroll
         for (int t = 0; t < MT; t++)
@@ -424,41 +598,54 @@ __global__ __launch_bounds__(64 * RT * KS) void k_small_m_mfma(const uint8_t* __
             for (int i = 0; i < 4; i++) {
                 float v = partial(t, i);
 #pragma unroll
-                for (int p = 1; p < KS; p++) v += pbuf[pidx(p, t, i)];
+                for (int p = 1; p < NPART; p++) v += pbuf[pidx(p, t, i)];
                 const int m = 16 * t + 4 * kp + i;
                 if (m < M) y[(int64_t)m * N + n] = v;
             }
     }
 }
 
-// Waves sharing one weight tile's sub-blocks.  Fixed for every M, so row m of
-// a product does not depend on the other rows in the batch.
-constexpr int kMfmaSplit = 2;
-// Super-blocks per step.
-constexpr int kMfmaStep = 2;
-
 // RT: weight tiles per workgroup (the activation staged by a workgroup is
-// shared by 16*RT weight rows); R: steps of global loads in flight.
-template <int MT, int RT, int R>
-static hipError_t launch_mfma_mt(const void* w, int64_t N, int64_t K, int64_t M,
-                                 const int8_t* q, const uint16_t* d, const int32_t* s, float* y,
-                                 hipStream_t st) {
+// shared by 16*RT weight rows); KS, KP: waves sharing a tile's 32-blocks and
+// units; G: units per step; R: steps of global loads in flight.
+template <int FMT, int MT, int RT, int KS, int KP, int G, int R>
+static hipError_t launch_mfma_cfg(const void* w, int64_t N, int64_t K, int64_t M,
+                                  const int8_t* q, const uint16_t* d, const int32_t* s, float* y,
+                                  hipStream_t st) {
     const int Kp = (int)((K + 255) / 256 * 256);
     const int64_t grid = (N + 16 * RT - 1) / (16 * RT);
-    hipLaunchKernelGGL((k_small_m_mfma<MT, RT, kMfmaSplit, kMfmaStep, R>), dim3((unsigned)grid),
-                       dim3(64 * RT * kMfmaSplit), 0, st, (const uint8_t*)w, (int)N, Kp, (int)M,
-                       q, d, s, y);
+    hipLaunchKernelGGL((k_small_m_mfma<FMT, MT, RT, KS, KP, G, R>), dim3((unsigned)grid),
+                       dim3(64 * RT * KS * KP), 0, st, (const uint8_t*)w, (int)N, (int)K, Kp,
+                       (int)M, q, d, s, y);
     return hipGetLastError();
 }
 
+// Matrices with fewer 16-row tiles than this also split K between waves.
+constexpr int64_t kMfmaWideTiles = 512;
+
+// Row m of a product depends only on activation row m and on the bucket of
+// M (1-16, 17-32, 33-48, 49-64 rows) and the shape, which fix the
+// configuration and so the fp32 summation order.
+template <int FMT>
 static hipError_t launch_mfma(const void* w, int64_t N, int64_t K, int64_t M, const int8_t* q,
                               const uint16_t* d, const int32_t* s, float* y, hipStream_t st) {
     const int mt = (int)((M + 15) / 16);
+    const bool wide = (N + 15) / 16 >= kMfmaWideTiles;
+    // Q6_K's larger units and per-16 sums leave LDS for 2 tiles from MT = 3
+    constexpr int RT34 = FMT == QGEMV_FMT_Q6_K ? 2 : 4;
+    if (wide) {
+        switch (mt) {
+        case 1: return launch_mfma_cfg<FMT, 1, 2, 2, 1, 2, 2>(w, N, K, M, q, d, s, y, st);
+        case 2: return launch_mfma_cfg<FMT, 2, 4, 2, 1, 2, 2>(w, N, K, M, q, d, s, y, st);
+        case 3: return launch_mfma_cfg<FMT, 3, RT34, 2, 1, 2, 2>(w, N, K, M, q, d, s, y, st);
+        default: return launch_mfma_cfg<FMT, 4, RT34, 2, 1, 2, 2>(w, N, K, M, q, d, s, y, st);
+        }
+    }
     switch (mt) {
-    case 1: return launch_mfma_mt<1, 2, 2>(w, N, K, M, q, d, s, y, st);
-    case 2: return launch_mfma_mt<2, 4, 2>(w, N, K, M, q, d, s, y, st);
-    case 3: return launch_mfma_mt<3, 4, 2>(w, N, K, M, q, d, s, y, st);
-    default: return launch_mfma_mt<4, 4, 2>(w, N, K, M, q, d, s, y, st);
+    case 1: return launch_mfma_cfg<FMT, 1, 1, 1, 8, 8, 2>(w, N, K, M, q, d, s, y, st);
+    case 2: return launch_mfma_cfg<FMT, 2, 1, 1, 4, 4, 2>(w, N, K, M, q, d, s, y, st);
+    case 3: return launch_mfma_cfg<FMT, 3, 1, 1, 2, 2, 2>(w, N, K, M, q, d, s, y, st);
+    default: return launch_mfma_cfg<FMT, 4, 1, 1, 2, 2, 2>(w, N, K, M, q, d, s, y, st);
     }
 }
 
@@ -503,11 +690,9 @@ static int dot4_tile_rows(int64_t K) {
 // AUTO: the MFMA variant from this many rows on (measured crossover).
 constexpr int kMfmaFromM = 3;
 
-hipError_t launch_small_m_q4k(const void* w, int64_t N, int64_t K, int64_t M, const int8_t* q,
-                              const uint16_t* d, const int32_t* s, float* y, int variant,
-                              hipStream_t st) {
-    if (variant == QGEMV_VARIANT_MFMA || (variant == QGEMV_VARIANT_AUTO && M >= kMfmaFromM))
-        return launch_mfma(w, N, K, M, q, d, s, y, st);
+static hipError_t launch_dot4_q4k(const void* w, int64_t N, int64_t K, int64_t M,
+                                  const int8_t* q, const uint16_t* d, const int32_t* s, float* y,
+                                  hipStream_t st) {
     int mt = dot4_tile_rows(K);
     if (M < mt) mt = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8;
     switch (mt) {
@@ -515,6 +700,38 @@ hipError_t launch_small_m_q4k(const void* w, int64_t N, int64_t K, int64_t M, co
     case 4: return launch_dot4_mt<4>(w, N, K, M, q, d, s, y, st);
     case 2: return launch_dot4_mt<2>(w, N, K, M, q, d, s, y, st);
     default: return launch_dot4_mt<1>(w, N, K, M, q, d, s, y, st);
+    }
+}
+
+// The DOT4 variant of the Q6_K and Q4_0 products: the batch-1 GEMV on each
+// activation row (row m of the product is by definition that GEMV).
+static hipError_t launch_rows_gemv(int fmt, const void* w, int64_t N, int64_t K, int64_t M,
+                                   const int8_t* q, const uint16_t* d, const int32_t* s,
+                                   float* y, hipStream_t st) {
+    const int64_t Kp = (K + 255) / 256 * 256;
+    for (int64_t m = 0; m < M; m++) {
+        const GemvArgs a{w, N, K, q + m * Kp, d + m * (Kp / 32), s + m * (Kp / 32), y + m * N};
+        const hipError_t e = launch_gemv(fmt, a, st);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_small_m(int fmt, const void* w, int64_t N, int64_t K, int64_t M,
+                          const int8_t* q, const uint16_t* d, const int32_t* s, float* y,
+                          int variant, hipStream_t st) {
+    const bool mfma =
+        variant == QGEMV_VARIANT_MFMA || (variant == QGEMV_VARIANT_AUTO && M >= kMfmaFromM);
+    switch (fmt) {
+    case QGEMV_FMT_Q4_K:
+        return mfma ? launch_mfma<QGEMV_FMT_Q4_K>(w, N, K, M, q, d, s, y, st)
+                    : launch_dot4_q4k(w, N, K, M, q, d, s, y, st);
+    case QGEMV_FMT_Q6_K:
+        return mfma ? launch_mfma<QGEMV_FMT_Q6_K>(w, N, K, M, q, d, s, y, st)
+                    : launch_rows_gemv(fmt, w, N, K, M, q, d, s, y, st);
+    default:
+        return mfma ? launch_mfma<QGEMV_FMT_Q4_0>(w, N, K, M, q, d, s, y, st)
+                    : launch_rows_gemv(fmt, w, N, K, M, q, d, s, y, st);
     }
 }
 

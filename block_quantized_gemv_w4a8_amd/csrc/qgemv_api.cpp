@@ -110,6 +110,32 @@ qgemv_status gemv_common(int fmt, const void* w, int64_t N, int64_t K, const int
     return launched(qgemv::launch_gemv(fmt, a, (hipStream_t)stream), name);
 }
 
+qgemv_status small_m_common(int fmt, const char* name, const void* w, int64_t N, int64_t K,
+                            int64_t M, const int8_t* q, const uint16_t* d, const int32_t* s,
+                            float* y, int variant, qgemv_stream_t stream) {
+    if (N < 0 || M < 0) return fail(QGEMV_E_SHAPE, "%s: negative N or M", name);
+    if (N == 0 || M == 0) return ok();
+    if (!w || !q || !d || !s || !y) return fail(QGEMV_E_NULL, "%s: NULL pointer argument", name);
+    qgemv_status st = check_k(K);
+    if (st != QGEMV_OK) return st;
+    if (N > INT32_MAX) return fail(QGEMV_E_SHAPE, "%s: N exceeds 2^31-1", name);
+    if (K > QGEMV_K_MAX)
+        return fail(QGEMV_E_UNSUPPORTED, "%s: K = %lld exceeds QGEMV_K_MAX", name, (long long)K);
+    if (M > QGEMV_M_MAX)
+        return fail(QGEMV_E_UNSUPPORTED, "%s: M = %lld exceeds QGEMV_M_MAX = %d", name,
+                    (long long)M, QGEMV_M_MAX);
+    if (variant != QGEMV_VARIANT_AUTO && variant != QGEMV_VARIANT_DOT4 &&
+        variant != QGEMV_VARIANT_MFMA)
+        return fail(QGEMV_E_UNSUPPORTED, "%s: unknown variant %d", name, variant);
+    if (!aligned(w, 16)) return fail(QGEMV_E_ALIGN, "%s: w must be 16-byte aligned", name);
+    if ((st = check_act_align(q, d, s)) != QGEMV_OK) return st;
+    if (!aligned(y, 4)) return fail(QGEMV_E_ALIGN, "%s: y must be 4-byte aligned", name);
+    if ((st = check_device()) != QGEMV_OK) return st;
+    return launched(qgemv::launch_small_m(fmt, w, N, K, M, q, d, s, y, variant,
+                                          (hipStream_t)stream),
+                    name);
+}
+
 }  // namespace
 
 extern "C" {
@@ -132,7 +158,8 @@ const char* qgemv_status_str(int status) {
 const char* qgemv_build_info(void) {
     return "libqgemv abi=1 arch=gfx950 formats=q4_0,q4_k,q6_k,q8_0 act=int8/32+fp16+int32sum "
            "gemv=v_dot4_i32_i8,lds-row-stream,lanes-per-row{4,8,16,32,64} "
-           "small_m=q4_k{dot4,mfma_i8_16x16x32} fused=q4_k_swiglu_quantize K_max=32768 M_max=64";
+           "small_m=q4_k{dot4,mfma_i8_16x16x32},q6_k/q4_0{gemv_rows,mfma_i8_16x16x32} "
+           "fused=q4_k_swiglu_quantize K_max=32768 M_max=64";
 }
 
 const char* qgemv_last_error(void) { return g_last_error; }
@@ -182,28 +209,22 @@ qgemv_status qgemv_q8_0(const void* w, int64_t N, int64_t K, const int8_t* q, co
 qgemv_status qgemm_q4_k_small_m(const void* w, int64_t N, int64_t K, int64_t M, const int8_t* q,
                                 const uint16_t* d, const int32_t* s, float* y, int variant,
                                 qgemv_stream_t stream) {
-    const char* name = "qgemm_q4_k_small_m";
-    if (N < 0 || M < 0) return fail(QGEMV_E_SHAPE, "%s: negative N or M", name);
-    if (N == 0 || M == 0) return ok();
-    if (!w || !q || !d || !s || !y) return fail(QGEMV_E_NULL, "%s: NULL pointer argument", name);
-    qgemv_status st = check_k(K);
-    if (st != QGEMV_OK) return st;
-    if (N > INT32_MAX) return fail(QGEMV_E_SHAPE, "%s: N exceeds 2^31-1", name);
-    if (K > QGEMV_K_MAX)
-        return fail(QGEMV_E_UNSUPPORTED, "%s: K = %lld exceeds QGEMV_K_MAX", name, (long long)K);
-    if (M > QGEMV_M_MAX)
-        return fail(QGEMV_E_UNSUPPORTED, "%s: M = %lld exceeds QGEMV_M_MAX = %d", name,
-                    (long long)M, QGEMV_M_MAX);
-    if (variant != QGEMV_VARIANT_AUTO && variant != QGEMV_VARIANT_DOT4 &&
-        variant != QGEMV_VARIANT_MFMA)
-        return fail(QGEMV_E_UNSUPPORTED, "%s: unknown variant %d", name, variant);
-    if (!aligned(w, 16)) return fail(QGEMV_E_ALIGN, "%s: w must be 16-byte aligned", name);
-    if ((st = check_act_align(q, d, s)) != QGEMV_OK) return st;
-    if (!aligned(y, 4)) return fail(QGEMV_E_ALIGN, "%s: y must be 4-byte aligned", name);
-    if ((st = check_device()) != QGEMV_OK) return st;
-    return launched(qgemv::launch_small_m_q4k(w, N, K, M, q, d, s, y, variant,
-                                              (hipStream_t)stream),
-                    name);
+    return small_m_common(QGEMV_FMT_Q4_K, "qgemm_q4_k_small_m", w, N, K, M, q, d, s, y, variant,
+                          stream);
+}
+
+qgemv_status qgemm_q6_k_small_m(const void* w, int64_t N, int64_t K, int64_t M, const int8_t* q,
+                                const uint16_t* d, const int32_t* s, float* y, int variant,
+                                qgemv_stream_t stream) {
+    return small_m_common(QGEMV_FMT_Q6_K, "qgemm_q6_k_small_m", w, N, K, M, q, d, s, y, variant,
+                          stream);
+}
+
+qgemv_status qgemm_q4_0_small_m(const void* w, int64_t N, int64_t K, int64_t M, const int8_t* q,
+                                const uint16_t* d, const int32_t* s, float* y, int variant,
+                                qgemv_stream_t stream) {
+    return small_m_common(QGEMV_FMT_Q4_0, "qgemm_q4_0_small_m", w, N, K, M, q, d, s, y, variant,
+                          stream);
 }
 
 qgemv_status qgemv_silu_mul_quantize(const float* gu, int64_t N, int8_t* q, uint16_t* d,

@@ -80,6 +80,33 @@ __device__ __forceinline__ int sbyte(uint32_t x, uint32_t k) {
 
 constexpr uint32_t LO4 = 0x0F0F0F0Fu;
 
+// LDS field readers.  Fields that sit 2 bytes off a 4-byte boundary are read
+// as aligned dwords and shifted into place with v_alignbyte: unaligned LDS
+// accesses stall the LDS pipeline on this chip, aligned dword reads do not.
+__device__ __forceinline__ u32x4 lds16(const uint8_t* base, int off) {
+    return *reinterpret_cast<const u32x4*>(base + off);
+}
+__device__ __forceinline__ uint32_t lds2(const uint8_t* base, int off) {
+    return *reinterpret_cast<const uint16_t*>(base + off);
+}
+__device__ __forceinline__ uint32_t abyte(uint32_t hi, uint32_t lo, uint32_t sh) {
+    return __builtin_amdgcn_alignbyte(hi, lo, sh);
+}
+// 16 bytes at any even LDS offset (reads up to 4 bytes past the field).
+__device__ __forceinline__ u32x4 lds16_a2(const uint8_t* base, int off) {
+    const uint32_t* d = reinterpret_cast<const uint32_t*>(base + (off & ~3));
+    const uint32_t sh = off & 3;
+    const uint32_t w0 = d[0], w1 = d[1], w2 = d[2], w3 = d[3], w4 = d[4];
+    return u32x4{abyte(w1, w0, sh), abyte(w2, w1, sh), abyte(w3, w2, sh), abyte(w4, w3, sh)};
+}
+// 8 bytes at any even LDS offset.
+__device__ __forceinline__ u32x2 lds8_a2(const uint8_t* base, int off) {
+    const uint32_t* d = reinterpret_cast<const uint32_t*>(base + (off & ~3));
+    const uint32_t sh = off & 3;
+    const uint32_t w0 = d[0], w1 = d[1], w2 = d[2];
+    return u32x2{abyte(w1, w0, sh), abyte(w2, w1, sh)};
+}
+
 // Activation view of one unit: 16 dwords of codes (elements 64u .. 64u+63 of
 // the activation row, as laid out for the weights of the format).
 struct Act16 {

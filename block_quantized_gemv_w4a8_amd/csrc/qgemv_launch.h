@@ -39,8 +39,9 @@ hipError_t launch_quantize_act(const float* x, int64_t M, int64_t K, int64_t ldx
                                uint16_t* d, int32_t* s, hipStream_t st);
 hipError_t launch_silu_mul_quantize(const float* gu, int64_t N, int8_t* q, uint16_t* d,
                                     int32_t* s, float* h, hipStream_t st);
-hipError_t launch_small_m_q4k(const void* w, int64_t N, int64_t K, int64_t M, const int8_t* q,
-                              const uint16_t* d, const int32_t* s, float* y, int variant,
-                              hipStream_t st);
+// fmt: QGEMV_FMT_Q4_K, QGEMV_FMT_Q6_K or QGEMV_FMT_Q4_0
+hipError_t launch_small_m(int fmt, const void* w, int64_t N, int64_t K, int64_t M,
+                          const int8_t* q, const uint16_t* d, const int32_t* s, float* y,
+                          int variant, hipStream_t st);
 
 }  // namespace qgemv

@@ -141,6 +141,20 @@ qgemv_status qgemm_q4_k_small_m(const void* w, int64_t N, int64_t K, int64_t M,
                                 const int8_t* q, const uint16_t* d, const int32_t* s,
                                 float* y, int variant, qgemv_stream_t stream);
 
+/* The same product for Q6_K and Q4_0 weights (the prefill chunk through the
+ * down projection and lm_head, which are Q6_K in a Q4_K_M model; "llambda.lisp"
+ * README, Features & Architecture).  Arguments, layouts, limits and errors as
+ * for qgemm_q4_k_small_m; K % 32 == 0 for Q4_0, any K <= QGEMV_K_MAX.
+ * variant: QGEMV_VARIANT_MFMA (int8 matrix cores), QGEMV_VARIANT_DOT4 (the
+ * batch-1 GEMV of this library on each activation row, one launch per row),
+ * or QGEMV_VARIANT_AUTO (chooses by M). */
+qgemv_status qgemm_q6_k_small_m(const void* w, int64_t N, int64_t K, int64_t M,
+                                const int8_t* q, const uint16_t* d, const int32_t* s,
+                                float* y, int variant, qgemv_stream_t stream);
+qgemv_status qgemm_q4_0_small_m(const void* w, int64_t N, int64_t K, int64_t M,
+                                const int8_t* q, const uint16_t* d, const int32_t* s,
+                                float* y, int variant, qgemv_stream_t stream);
+
 /* SwiGLU glue between the gate|up and down products (llambda.lisp README,
  * supported architectures; "Running an LLM on VKNN", SwiGLU):
  * gu fp32 [2N] = [gate (N) | up (N)], N % 32 == 0.

@@ -1,5 +1,6 @@
-"""Small-M (prefill chunk) Q4_K product on the GPU against the oracle; row m of
-the batched product is the batch-1 product of activation row m."""
+"""Small-M (prefill chunk) products on the GPU against the oracle, for Q4_K,
+Q6_K and Q4_0 weights; row m of the batched product is the batch-1 product
+of activation row m."""
 import numpy as np
 import pytest
 import torch
@@ -10,6 +11,8 @@ from gpu_util import act_host, check_y, dev, host, quantize, say
 
 pytestmark = pytest.mark.gpu
 
+WEIGHTS = {"q4_k": synth.q4_k_weights, "q6_k": synth.q6_k_weights, "q4_0": synth.q4_0_weights}
+
 
 @pytest.fixture(scope="module")
 def qg():
@@ -17,10 +20,10 @@ def qg():
     return qg
 
 
-def small_m(qg, wd, N, K, act, M, variant):
+def small_m(qg, fmt, wd, N, K, act, M, variant):
     q, d, s = act
     y = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda:0")
-    qg.qgemm_q4_k_small_m(wd, N, K, M, q, d, s, y, variant)
+    qg.SMALL_M[fmt](wd, N, K, M, q, d, s, y, variant)
     return host(y)
 
 
@@ -28,72 +31,130 @@ def variants(qg):
     return [qg.QGEMV_VARIANT_DOT4, qg.QGEMV_VARIANT_MFMA, qg.QGEMV_VARIANT_AUTO]
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 100, 256), (2, 65, 896), (3, 257, 4096), (5, 64, 4864),
-                                   (8, 300, 4096), (9, 129, 1024), (16, 64, 4096),
-                                   (17, 33, 768), (33, 70, 512), (48, 130, 2048),
-                                   (64, 96, 4096), (64, 1000, 1024), (7, 20, 32768)])
-def test_small_m_shapes(qg, M, N, K):
-    g = np.random.default_rng(M * 100 + N)
-    w = synth.q4_k_weights(g, N, K)
+SHAPES = [(1, 100, 256), (2, 65, 896), (3, 257, 4096), (5, 64, 4864), (8, 300, 4096),
+          (9, 129, 1024), (16, 64, 4096), (17, 33, 768), (33, 70, 512), (48, 130, 2048),
+          (64, 96, 4096), (64, 1000, 1024), (7, 20, 32768)]
+# Q4_0 rows need not hold whole 256-weight units: K = 32, 96, 1056, 4128
+Q40_EXTRA = [(3, 40, 32), (17, 50, 96), (8, 90, 1056), (64, 70, 4128)]
+
+
+@pytest.mark.parametrize("fmt,M,N,K", [("q4_k",) + sh for sh in SHAPES] +
+                         [("q6_k",) + sh for sh in SHAPES] +
+                         [("q4_0",) + sh for sh in SHAPES + Q40_EXTRA])
+def test_small_m_shapes(qg, fmt, M, N, K):
+    g = np.random.default_rng(M * 100 + N + 7 * K)
+    w = WEIGHTS[fmt](g, N, K)
     x, _ = synth.activation(g, M, K)
     act = quantize(qg, x)
     q, d, s = act_host(*act)
     wd = dev(w)
-    Y_ref, TT = oracle.gemm("q4_k", w, N, K, q, d, s)
+    Y_ref, TT = oracle.gemm(fmt, w, N, K, q, d, s)
     for v in variants(qg):
-        say("small_m", M, N, K, "variant", v)
-        Y = small_m(qg, wd, N, K, act, M, v)
-        check_y(Y.reshape(-1), Y_ref.reshape(-1), TT.reshape(-1), f"small_m M={M} N={N} K={K} v={v}")
+        say("small_m", fmt, M, N, K, "variant", v)
+        Y = small_m(qg, fmt, wd, N, K, act, M, v)
+        check_y(Y.reshape(-1), Y_ref.reshape(-1), TT.reshape(-1),
+                f"small_m {fmt} M={M} N={N} K={K} v={v}")
+
+
+def sampled(fmt, w, N, K, act, windows):
+    q, d, s = act
+    M = q.shape[0]
+    parts_y, parts_t = [], []
+    for r0, nr in windows:
+        yy, tt = oracle.gemm(fmt, w, N, K, q, d, s, rows=(r0, nr))
+        parts_y.append(yy)
+        parts_t.append(tt)
+    rows = np.concatenate([np.arange(r0, r0 + nr) for r0, nr in windows])
+    return rows, np.concatenate(parts_y, axis=1), np.concatenate(parts_t, axis=1)
 
 
 def test_config4_m8_m64(qg):
     c = synth.config4()
     N, K = c["N"], c["K"]
     wd = dev(c["w"])
-    rows = np.concatenate([np.arange(256), np.arange(N - 256, N), np.arange(7000, 7256)])
     for M, x in [(8, c["x8"]), (64, c["x64"])]:
         act = quantize(qg, x)
-        q, d, s = act_host(*act)
-        Y_ref = np.empty((M, rows.size))
-        TT = np.empty((M, rows.size))
-        for r0 in (0, 7000, N - 256):
-            yy, tt = oracle.gemm("q4_k", c["w"], N, K, q, d, s, rows=(r0, 256))
-            sl = {0: slice(0, 256), N - 256: slice(256, 512), 7000: slice(512, 768)}[r0]
-            Y_ref[:, sl] = yy
-            TT[:, sl] = tt
+        rows, Y_ref, TT = sampled("q4_k", c["w"], N, K, act_host(*act),
+                                  [(0, 256), (7000, 256), (N - 256, 256)])
         for v in variants(qg):
             say("config4", M, "variant", v)
-            Y = small_m(qg, wd, N, K, act, M, v)
+            Y = small_m(qg, "q4_k", wd, N, K, act, M, v)
             assert np.all(np.isfinite(Y))
             check_y(Y[:, rows].reshape(-1), Y_ref.reshape(-1), TT.reshape(-1), f"config4 M={M}")
 
 
-def test_row_independence(qg):
+def test_q6_k_down_shape_m8_m64(qg):
+    """The prefill chunk through the Llama-3.1-8B down projection (Q6_K 4096 x 14336)."""
+    g = np.random.default_rng(11)
+    N, K = 4096, 14336
+    w = synth.q6_k_weights(g, N, K)
+    wd = dev(w)
+    x64, _ = synth.activation(g, 64, K)
+    for M in (8, 64):
+        act = quantize(qg, x64[:M])
+        rows, Y_ref, TT = sampled("q6_k", w, N, K, act_host(*act), [(0, 128), (2000, 64), (N - 128, 128)])
+        for v in (qg.QGEMV_VARIANT_MFMA, qg.QGEMV_VARIANT_AUTO):
+            say("q6_k down shape", M, "variant", v)
+            Y = small_m(qg, "q6_k", wd, N, K, act, M, v)
+            assert np.all(np.isfinite(Y))
+            check_y(Y[:, rows].reshape(-1), Y_ref.reshape(-1), TT.reshape(-1), f"q6_k down M={M}")
+
+
+def test_q4_0_config0_shape_m64(qg):
+    c = synth.config0()
+    g = np.random.default_rng(12)
+    x64, _ = synth.activation(g, 64, 896)
+    act = quantize(qg, x64)
+    q, d, s = act_host(*act)
+    Y_ref, TT = oracle.gemm("q4_0", c["w"], 896, 896, q, d, s)
+    for v in variants(qg):
+        say("q4_0 config0 shape M=64 variant", v)
+        Y = small_m(qg, "q4_0", dev(c["w"]), 896, 896, act, 64, v)
+        check_y(Y.reshape(-1), Y_ref.reshape(-1), TT.reshape(-1), f"q4_0 896 M=64 v={v}")
+
+
+@pytest.mark.parametrize("fmt", ["q4_k", "q6_k", "q4_0"])
+def test_row_independence(qg, fmt):
     """Row m of an M-row call equals a 1-row call on activation row m, bit for bit."""
     g = np.random.default_rng(5)
     N, K, M = 200, 4096, 8
-    w = synth.q4_k_weights(g, N, K)
+    w = WEIGHTS[fmt](g, N, K)
     x, _ = synth.activation(g, M, K)
     wd = dev(w)
     q, d, s = quantize(qg, x)
     for v in (qg.QGEMV_VARIANT_DOT4, qg.QGEMV_VARIANT_MFMA):
-        Y = small_m(qg, wd, N, K, (q, d, s), M, v)
+        Y = small_m(qg, fmt, wd, N, K, (q, d, s), M, v)
         for m in (0, 3, 7):
-            Ym = small_m(qg, wd, N, K, (q[m:m + 1], d[m:m + 1], s[m:m + 1]), 1, v)
-            assert np.array_equal(Y[m].view(np.uint32), Ym[0].view(np.uint32)), (v, m)
+            Ym = small_m(qg, fmt, wd, N, K, (q[m:m + 1], d[m:m + 1], s[m:m + 1]), 1, v)
+            assert np.array_equal(Y[m].view(np.uint32), Ym[0].view(np.uint32)), (fmt, v, m)
 
 
-def test_variants_agree_and_mfma_matches_dots(qg):
-    """MFMA and DOT4 give the same rows within the tolerance of the definition,
-    and the MFMA result of one row matches the batch-1 GEMV within it too."""
-    g = np.random.default_rng(9)
-    N, K, M = 333, 2304, 24
-    w = synth.q4_k_weights(g, N, K)
+def test_rows_variant_is_the_gemv(qg):
+    """For Q6_K and Q4_0 the DOT4 variant is the batch-1 GEMV on each row: equal bit for bit."""
+    g = np.random.default_rng(13)
+    for fmt in ("q6_k", "q4_0"):
+        N, K, M = 300, 2048, 5
+        w = WEIGHTS[fmt](g, N, K)
+        x, _ = synth.activation(g, M, K)
+        wd = dev(w)
+        q, d, s = quantize(qg, x)
+        Y = small_m(qg, fmt, wd, N, K, (q, d, s), M, qg.QGEMV_VARIANT_DOT4)
+        for m in range(M):
+            y = torch.empty(N, dtype=torch.float32, device="cuda:0")
+            qg.GEMV[fmt](wd, N, K, q[m], d[m], s[m], y)
+            assert np.array_equal(Y[m].view(np.uint32), host(y).view(np.uint32)), (fmt, m)
+
+
+@pytest.mark.parametrize("fmt,M,N,K", [("q6_k", 8, 8200, 1024), ("q6_k", 40, 8192, 512),
+                                       ("q4_0", 20, 8224, 896), ("q4_0", 64, 8192, 256),
+                                       ("q4_k", 3, 8192, 2304)])
+def test_wide_shapes(qg, fmt, M, N, K):
+    """Matrices with many row tiles take the configuration without the K split."""
+    g = np.random.default_rng(N + K + M)
+    w = WEIGHTS[fmt](g, N, K)
     x, _ = synth.activation(g, M, K)
     act = quantize(qg, x)
-    q, d, s = act_host(*act)
-    wd = dev(w)
-    Y_ref, TT = oracle.gemm("q4_k", w, N, K, q, d, s)
-    for v in (qg.QGEMV_VARIANT_DOT4, qg.QGEMV_VARIANT_MFMA):
-        Y = small_m(qg, wd, N, K, act, M, v)
-        check_y(Y.reshape(-1), Y_ref.reshape(-1), TT.reshape(-1), f"variant {v}")
+    rows, Y_ref, TT = sampled(fmt, w, N, K, act_host(*act), [(0, 200), (4000, 100), (N - 150, 150)])
+    say("small_m wide", fmt, M, N, K)
+    Y = small_m(qg, fmt, dev(w), N, K, act, M, qg.QGEMV_VARIANT_MFMA)
+    check_y(Y[:, rows].reshape(-1), Y_ref.reshape(-1), TT.reshape(-1), f"wide {fmt} M={M} N={N} K={K}")
