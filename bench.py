@@ -34,7 +34,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
 METRIC = "quantized GEMV weight GB/s and % of HBM peak at Llama-3-8B shapes, 1 GPU"
 WORKLOAD = ("llama3.1-8b decode step, batch 1: ffn gate|up q4_k 28672x4096 with fused "
-            "silu*up requant -> down q6_k 4096x14336, then lm_head q6_k 128256x4096")
+            "silu*up requant -> down q6_k 4096x14336, then lm_head q6_k 128256x4096 "
+            "(q6_k repacked at load into aligned 8-super-block tiles, same bytes)")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_q6k_lm_head.json")
 KERNEL_SOURCES = ["qgemv_device.h", "qgemv_quant.h", "k_gemv.hip", "k_quantize.hip",
                   "qgemv_api.cpp"]
@@ -84,6 +85,16 @@ class HipTimer:
             self.hip.hipEventDestroy(e)
 
 
+def workload_name(args) -> str:
+    w = WORKLOAD
+    if args.unfused:
+        w = w.replace("with fused", "then a separate")
+    if args.native_q6k:
+        w = w.replace("(q6_k repacked at load into aligned 8-super-block tiles, same bytes)",
+                      "(q6_k in the on-disk layout)")
+    return w
+
+
 def kernel_fingerprint() -> str:
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:
@@ -104,6 +115,8 @@ def main():
     ap.add_argument("--event-every", type=int, default=10,
                     help="bracket every n-th lm_head launch of the timed steps with HIP events "
                          "(an event pair still costs ~4 us of queue time)")
+    ap.add_argument("--native-q6k", action="store_true",
+                    help="run the Q6_K GEMVs on the on-disk layout instead of the repacked one")
     ap.add_argument("--unfused", action="store_true",
                     help="gate|up GEMV and SiLU*up requant as two launches (comparison)")
     ap.add_argument("--calib-copy", action="store_true",
@@ -138,6 +151,18 @@ def main():
         w_gu.append(w_gu[0].clone())
         w_dn.append(w_dn[0].clone())
         w_hd.append(w_hd[0].clone())
+    # load-time repack of the Q6_K weights (outside the timed region; the
+    # repacked rows hold the same bytes, only moved into aligned tiles)
+    gemv_q6 = qg.qgemv_q6_k
+    if not args.native_q6k:
+        def repack(wt, N, K):
+            wr = torch.empty((N, qg.q6_k_r8_row_bytes(K)), dtype=torch.uint8, device=dev)
+            qg.qgemv_q6_k_repack(wt, N, K, wr)
+            return wr
+        w_dn = [repack(wt, Nd, Kd) for wt in w_dn]
+        w_hd = [repack(wt, Nh, Kh) for wt in w_hd]
+        torch.cuda.synchronize()
+        gemv_q6 = qg.qgemv_q6_k_r8
     x_ffn = torch.from_numpy(c2["x"]).to(dev)
     x_head = torch.from_numpy(c3["x"]).to(dev)
     q1, d1, s1 = qg.act_buffers(1, Kgu, dev)
@@ -165,11 +190,11 @@ def main():
         else:
             qg.qgemv_q4_k_swiglu_quantize(w_gu[c], Kd, Kgu, q1, d1, s1, q2, d2, s2, None, None,
                                           stream=sh)
-        qg.qgemv_q6_k(w_dn[c], Nd, Kd, q2, d2, s2, y_ffn, stream=sh)
+        gemv_q6(w_dn[c], Nd, Kd, q2, d2, s2, y_ffn, stream=sh)
         qg.qgemv_quantize_act(x_head, 1, Kh, Kh, q3, d3, s3, stream=sh)
         if ev is not None:
             ev.record(0, sh)
-        qg.qgemv_q6_k(w_hd[c], Nh, Kh, q3, d3, s3, logits, stream=sh)
+        gemv_q6(w_hd[c], Nh, Kh, q3, d3, s3, logits, stream=sh)
         if ev is not None:
             ev.record(1, sh)
 
@@ -212,7 +237,9 @@ def main():
             traffic = tr.get("bytes_per_launch")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                "kernel": "qgemv_q6_k lm_head 128256x4096", "avg_us": round(head_avg_us, 2),
+                "kernel": ("qgemv_q6_k lm_head 128256x4096" if args.native_q6k else
+                           "qgemv_q6_k_r8 lm_head 128256x4096 (repacked Q6_K)"),
+                "avg_us": round(head_avg_us, 2),
                 "timed_launches": len(head_us),
                 "alg_bytes_per_launch": head_alg}
 
@@ -245,8 +272,7 @@ def main():
         "vs_baseline": None,
         "dtype": "int8",
         "data": "synthetic (seeded; shapes and value distributions of the five workloads)",
-        "config": {"workload": WORKLOAD if not args.unfused else
-                   WORKLOAD.replace("with fused", "then a separate"), "batch": 1,
+        "config": {"workload": workload_name(args), "batch": 1,
                    "weight_bytes_per_step": step_wbytes, "weight_copies_rotated": R,
                    "steps_per_s": round(1e3 / ms_per_step, 1)},
         "hbm_peak_frac": round(value / HBM_PEAK_GBPS, 4),
@@ -375,6 +401,10 @@ def extras(qg, torch, np, synth, dev, R, c2, c3, args):
 
     def gemv_case(fmt, w_host, N, K, x, copies):
         ws = [torch.from_numpy(w_host).to(dev)]
+        if fmt == "q6_k_r8":
+            wr = torch.empty((N, qg.q6_k_r8_row_bytes(K)), dtype=torch.uint8, device=dev)
+            qg.qgemv_q6_k_repack(ws[0], N, K, wr)
+            ws = [wr]
         for _ in range(copies - 1):
             ws.append(ws[0].clone())
         q, d, s = qg.act_buffers(1, K, dev)
@@ -382,7 +412,7 @@ def extras(qg, torch, np, synth, dev, R, c2, c3, args):
         y = torch.empty(N, dtype=torch.float32, device=dev)
         f = qg.GEMV[fmt]
         us = time_kernel(torch, lambda c: f(ws[c], N, K, q, d, s, y), 100, copies)
-        wb = synth.logical_bytes(fmt, N, K)
+        wb = synth.logical_bytes(fmt.replace("_r8", ""), N, K)
         del ws
         return {"us": round(us, 2), "weight_GBps": round(wb / us / 1e3, 1),
                 "hbm_frac": round(wb / us / 1e3 / HBM_PEAK_GBPS, 4), "calls_per_s": round(1e6 / us)}
@@ -405,6 +435,8 @@ def extras(qg, torch, np, synth, dev, R, c2, c3, args):
     hx = np.random.default_rng(0).standard_normal((1, Kd)).astype(np.float32)
     ex["down_q6_k_4096x14336"] = gemv_case("q6_k", c2["w_down"], Nd, Kd, hx, 11)
     ex["lm_head_q6_k_128256x4096"] = gemv_case("q6_k", c3["w"], Nh, Kh, c3["x"], 2)
+    ex["lm_head_q6_k_r8_128256x4096"] = gemv_case("q6_k_r8", c3["w"], Nh, Kh, c3["x"], 2)
+    ex["down_q6_k_r8_4096x14336"] = gemv_case("q6_k_r8", c2["w_down"], Nd, Kd, hx, 11)
     # cache-resident (single 48 MB copy of down, read again and again)
     one = gemv_case("q6_k", c2["w_down"], Nd, Kd, hx, 1)
     ex["down_q6_k_cache_resident_single_copy"] = one

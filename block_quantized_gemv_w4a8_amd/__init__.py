@@ -32,6 +32,7 @@ QGEMV_E_DEVICE = 5
 QGEMV_E_LAUNCH = 6
 
 QGEMV_FMT_Q4_0, QGEMV_FMT_Q4_K, QGEMV_FMT_Q6_K, QGEMV_FMT_Q8_0 = 0, 1, 2, 3
+QGEMV_FMT_Q6_K_R8 = 4
 QGEMV_VARIANT_AUTO, QGEMV_VARIANT_DOT4, QGEMV_VARIANT_MFMA = 0, 1, 2
 QGEMV_K_MAX = 32768
 QGEMV_M_MAX = 64
@@ -40,6 +41,7 @@ QGEMV_M_MAX = 64
 EXPORTS = [
     "qgemv_abi_version", "qgemv_status_str", "qgemv_build_info", "qgemv_last_error",
     "qgemv_quantize_act", "qgemv_q4_0", "qgemv_q4_k", "qgemv_q6_k", "qgemv_q8_0",
+    "qgemv_q6_k_repack", "qgemv_q6_k_r8",
     "qgemm_q4_k_small_m", "qgemm_q6_k_small_m", "qgemm_q4_0_small_m",
     "qgemv_silu_mul_quantize", "qgemv_q4_k_swiglu_quantize",
     "qgemv_block_dots",
@@ -56,7 +58,7 @@ _lib.qgemv_last_error.restype = ctypes.c_char_p
 _lib.qgemv_last_error.argtypes = []
 _lib.qgemv_quantize_act.restype = _I
 _lib.qgemv_quantize_act.argtypes = [_P, _I64, _I64, _I64, _P, _P, _P, _P]
-for _n in ("qgemv_q4_0", "qgemv_q4_k", "qgemv_q6_k", "qgemv_q8_0"):
+for _n in ("qgemv_q4_0", "qgemv_q4_k", "qgemv_q6_k", "qgemv_q8_0", "qgemv_q6_k_r8"):
     getattr(_lib, _n).restype = _I
     getattr(_lib, _n).argtypes = [_P, _I64, _I64, _P, _P, _P, _P, _P]
 for _n in ("qgemm_q4_k_small_m", "qgemm_q6_k_small_m", "qgemm_q4_0_small_m"):
@@ -143,6 +145,25 @@ def qgemv_q6_k(w, N, K, q, d, s, y, stream=None):
     return _gemv("qgemv_q6_k", w, N, K, q, d, s, y, stream)
 
 
+def qgemv_q6_k_r8(w_r, N, K, q, d, s, y, stream=None):
+    return _gemv("qgemv_q6_k_r8", w_r, N, K, q, d, s, y, stream)
+
+
+_lib.qgemv_q6_k_repack.restype = _I
+_lib.qgemv_q6_k_repack.argtypes = [_P, _I64, _I64, _P, _P]
+
+
+def qgemv_q6_k_repack(w, N, K, w_r, stream=None):
+    return _check(_lib.qgemv_q6_k_repack(_ptr(w), N, K, _ptr(w_r), _stream(stream)),
+                  "qgemv_q6_k_repack")
+
+
+def q6_k_r8_row_bytes(K: int) -> int:
+    """Bytes of one row of Q6_K weights repacked by qgemv_q6_k_repack."""
+    nsb = (K + 255) // 256
+    return (nsb + 7) // 8 * 1680
+
+
 def qgemv_q8_0(w, N, K, q, d, s, y, stream=None):
     return _gemv("qgemv_q8_0", w, N, K, q, d, s, y, stream)
 
@@ -184,9 +205,10 @@ def qgemv_block_dots(fmt, w, N, K, row0, nrows, q, dots, stream=None):
                                         _stream(stream)), "qgemv_block_dots")
 
 
-GEMV = {"q4_0": qgemv_q4_0, "q4_k": qgemv_q4_k, "q6_k": qgemv_q6_k, "q8_0": qgemv_q8_0}
+GEMV = {"q4_0": qgemv_q4_0, "q4_k": qgemv_q4_k, "q6_k": qgemv_q6_k, "q8_0": qgemv_q8_0,
+        "q6_k_r8": qgemv_q6_k_r8}
 FMT_ID = {"q4_0": QGEMV_FMT_Q4_0, "q4_k": QGEMV_FMT_Q4_K, "q6_k": QGEMV_FMT_Q6_K,
-          "q8_0": QGEMV_FMT_Q8_0}
+          "q8_0": QGEMV_FMT_Q8_0, "q6_k_r8": QGEMV_FMT_Q6_K_R8}
 
 
 def act_buffers(M: int, K: int, device="cuda"):

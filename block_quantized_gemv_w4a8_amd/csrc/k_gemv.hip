@@ -91,6 +91,9 @@ struct ActReg<QGEMV_FMT_Q6_K> {
 };
 
 template <>
+struct ActReg<QGEMV_FMT_Q6_K_R8> : ActReg<QGEMV_FMT_Q6_K> {};
+
+template <>
 struct ActReg<QGEMV_FMT_Q4_0> {
     Act16 x;
     float dx[2];
@@ -161,6 +164,14 @@ struct Unit<QGEMV_FMT_Q6_K> {
         for (int j = 0; j < 4; j++)
             t = fmaf((float)D[j], fd * (float)Q6K::scale(w, u, j) * a.dx[j], t);
         return t;
+    }
+};
+template <>
+struct Unit<QGEMV_FMT_Q6_K_R8> {
+    using W = Q6K::W;
+    __device__ static void load(const uint8_t* rp, int u, bool, W& w) { Q6K::load_r8(rp, u, w); }
+    __device__ static float term(const W& w, const ActReg<QGEMV_FMT_Q6_K_R8>& a, int u, int nbw) {
+        return Unit<QGEMV_FMT_Q6_K>::term(w, a, u, nbw);
     }
 };
 template <>
@@ -336,6 +347,21 @@ struct UnitLds<QGEMV_FMT_Q6_K> {
     }
 };
 template <>
+struct UnitLds<QGEMV_FMT_Q6_K_R8> {
+    // slices start at tile boundaries, so off0 is a multiple of 16 and every
+    // field is read with one aligned LDS access
+    __device__ static void load(const uint8_t* b, int off0, int ul, bool, Q6K::W& w) {
+        const int S = ul >> 2, i = S & 7;
+        const int p = off0 + Q6K::TILE_BYTES * (S >> 3);
+        const int h = (ul >> 1) & 1, t = ul & 1;
+        w.qa = lds16(b, p + 128 * i + 64 * h + 16 * t);
+        w.qb = lds16(b, p + 128 * i + 64 * h + 32 + 16 * t);
+        w.qh = lds16(b, p + Q6K::T_QH + 64 * i + 32 * h + 16 * t);
+        w.sc = *reinterpret_cast<const u32x2*>(b + p + Q6K::T_SC + 16 * i + 8 * h);
+        w.d = lds2(b, p + Q6K::T_D + 2 * i);
+    }
+};
+template <>
 struct UnitLds<QGEMV_FMT_Q4_0> {
     static constexpr int UNITS_PER_BLK = 0, BLK_BYTES = 18;
     // a missing second block re-reads the first one and gets d1 = 0
@@ -370,6 +396,7 @@ template <int FMT>
 __host__ __device__ inline int unit_byte(int u) {
     if (FMT == QGEMV_FMT_Q4_K) return (u / 4) * 144;
     if (FMT == QGEMV_FMT_Q6_K) return (u / 4) * 210;
+    if (FMT == QGEMV_FMT_Q6_K_R8) return (u + 31) / 32 * Q6K::TILE_BYTES;   // whole tiles
     if (FMT == QGEMV_FMT_Q4_0) return u * 36;
     return u * 68;
 }
@@ -581,7 +608,7 @@ __global__ __launch_bounds__(WG) void k_block_dots(const uint8_t* __restrict__ w
     const uint8_t* rp = w + (row0 + rr) * (int64_t)row_bytes;
     int32_t* out = dots + rr * nblk;
     Act16 x;
-    if constexpr (FMT == QGEMV_FMT_Q6_K) {
+    if constexpr (FMT == QGEMV_FMT_Q6_K || FMT == QGEMV_FMT_Q6_K_R8) {
         int init[4], D[4];
 #pragma unroll
         for (int j = 0; j < 4; j++) {
@@ -593,7 +620,8 @@ __global__ __launch_bounds__(WG) void k_block_dots(const uint8_t* __restrict__ w
             init[j] = -32 * sum16(v.x, v.y, v.z, v.w);
         }
         Q6K::W wv;
-        Q6K::load(rp, u, wv);
+        if (FMT == QGEMV_FMT_Q6_K_R8) Q6K::load_r8(rp, u, wv);
+        else Q6K::load(rp, u, wv);
         Q6K::dots(wv, x, init, D);
 #pragma unroll
         for (int j = 0; j < 4; j++) out[Q6K::act_offset(u, j) >> 4] = D[j];
@@ -642,13 +670,15 @@ static int row_bytes_of(int fmt, int64_t K) {
     case QGEMV_FMT_Q4_0: return (int)(K / 32 * 18);
     case QGEMV_FMT_Q8_0: return (int)(K / 32 * 34);
     case QGEMV_FMT_Q4_K: return (int)(Kp / 256 * 144);
+    case QGEMV_FMT_Q6_K_R8: return (int)((Kp / 256 + 7) / 8 * Q6K::TILE_BYTES);
     default: return (int)(Kp / 256 * 210);
     }
 }
 
 static int units_of(int fmt, int64_t K) {
     const int64_t Kp = (K + 255) / 256 * 256;
-    if (fmt == QGEMV_FMT_Q4_K || fmt == QGEMV_FMT_Q6_K) return (int)(Kp / 64);
+    if (fmt == QGEMV_FMT_Q4_K || fmt == QGEMV_FMT_Q6_K || fmt == QGEMV_FMT_Q6_K_R8)
+        return (int)(Kp / 64);
     return (int)((K + 63) / 64);
 }
 
@@ -753,6 +783,7 @@ static SliceGeom slice_geom(int64_t K, int U, int WK) {
     SliceGeom g;
     g.US = (U + WK - 1) / WK;
     if (kq) g.US = (g.US + 3) / 4 * 4;  // slices start at super-block boundaries
+    if (FMT == QGEMV_FMT_Q6_K_R8) g.US = (g.US + 31) / 32 * 32;  // ... at tile boundaries
     g.nchunk = 0;
     for (int k = 0; k < WK; k++) {
         const int lo = k * g.US;
@@ -830,8 +861,50 @@ hipError_t launch_gemv(int fmt, const GemvArgs& a, hipStream_t st) {
     case QGEMV_FMT_Q4_0: return launch_gemv_fmt<QGEMV_FMT_Q4_0>(a, st);
     case QGEMV_FMT_Q4_K: return launch_gemv_fmt<QGEMV_FMT_Q4_K>(a, st);
     case QGEMV_FMT_Q6_K: return launch_gemv_fmt<QGEMV_FMT_Q6_K>(a, st);
+    case QGEMV_FMT_Q6_K_R8: return launch_gemv_fmt<QGEMV_FMT_Q6_K_R8>(a, st);
     default: return launch_gemv_fmt<QGEMV_FMT_Q8_0>(a, st);
     }
+}
+
+// Q6_K -> Q6_K_R8: one thread per (row, tile slot); a slot past the row's
+// super-blocks (the rest of a partial last tile) is written as zeros.  The
+// native super-block is 2-byte aligned, so it is copied as 16-bit words.
+__global__ __launch_bounds__(WG) void k_q6k_repack(const uint8_t* __restrict__ w, int64_t N,
+                                                   int nsb, int64_t row_bytes, int ntile,
+                                                   uint8_t* __restrict__ wr) {
+    const int64_t gt = (int64_t)blockIdx.x * WG + threadIdx.x;
+    const int64_t slots = (int64_t)ntile * Q6K::TILE_SB;
+    if (gt >= N * slots) return;
+    const int64_t r = gt / slots;
+    const int slot = (int)(gt - r * slots);
+    const int T = slot >> 3, i = slot & 7, S = slot;
+    uint8_t* tile = wr + r * (int64_t)ntile * Q6K::TILE_BYTES + (int64_t)T * Q6K::TILE_BYTES;
+    uint16_t* ql = reinterpret_cast<uint16_t*>(tile + 128 * i);
+    uint16_t* qh = reinterpret_cast<uint16_t*>(tile + Q6K::T_QH + 64 * i);
+    uint16_t* sc = reinterpret_cast<uint16_t*>(tile + Q6K::T_SC + 16 * i);
+    uint16_t* dd = reinterpret_cast<uint16_t*>(tile + Q6K::T_D + 2 * i);
+    if (S < nsb) {
+        const uint16_t* src = reinterpret_cast<const uint16_t*>(w + r * row_bytes + 210 * S);
+        for (int k = 0; k < 64; k++) ql[k] = src[k];
+        for (int k = 0; k < 32; k++) qh[k] = src[64 + k];
+        for (int k = 0; k < 8; k++) sc[k] = src[96 + k];
+        dd[0] = src[104];
+    } else {
+        for (int k = 0; k < 64; k++) ql[k] = 0;
+        for (int k = 0; k < 32; k++) qh[k] = 0;
+        for (int k = 0; k < 8; k++) sc[k] = 0;
+        dd[0] = 0;
+    }
+}
+
+hipError_t launch_q6k_repack(const void* w, int64_t N, int64_t K, void* wr, hipStream_t st) {
+    const int nsb = (int)((K + 255) / 256);
+    const int ntile = (nsb + Q6K::TILE_SB - 1) / Q6K::TILE_SB;
+    const int64_t threads = N * ntile * Q6K::TILE_SB;
+    const int64_t grid = (threads + WG - 1) / WG;
+    hipLaunchKernelGGL(k_q6k_repack, dim3((unsigned)grid), dim3(WG), 0, st, (const uint8_t*)w, N,
+                       nsb, (int64_t)nsb * 210, ntile, (uint8_t*)wr);
+    return hipGetLastError();
 }
 
 hipError_t launch_block_dots(int fmt, const void* w, int64_t K, int64_t row0, int64_t nrows,
@@ -840,7 +913,7 @@ hipError_t launch_block_dots(int fmt, const void* w, int64_t K, int64_t row0, in
     const int nbw = (int)(K / 32);
     const int rb = row_bytes_of(fmt, K);
     const int64_t Kp = (K + 255) / 256 * 256;
-    int nblk = (fmt == QGEMV_FMT_Q6_K) ? (int)(Kp / 16)
+    int nblk = (fmt == QGEMV_FMT_Q6_K || fmt == QGEMV_FMT_Q6_K_R8) ? (int)(Kp / 16)
                                         : (fmt == QGEMV_FMT_Q4_K ? (int)(Kp / 32) : nbw);
     const int64_t grid = (nrows * U + WG - 1) / WG;
     const uint8_t* wp = (const uint8_t*)w;
@@ -856,6 +929,10 @@ hipError_t launch_block_dots(int fmt, const void* w, int64_t K, int64_t row0, in
     case QGEMV_FMT_Q6_K:
         hipLaunchKernelGGL(k_block_dots<QGEMV_FMT_Q6_K>, dim3((unsigned)grid), dim3(WG), 0, st,
                            wp, row0, nrows, U, nbw, rb, nblk, q, dots);
+        break;
+    case QGEMV_FMT_Q6_K_R8:
+        hipLaunchKernelGGL(k_block_dots<QGEMV_FMT_Q6_K_R8>, dim3((unsigned)grid), dim3(WG), 0,
+                           st, wp, row0, nrows, U, nbw, rb, nblk, q, dots);
         break;
     default:
         hipLaunchKernelGGL(k_block_dots<QGEMV_FMT_Q8_0>, dim3((unsigned)grid), dim3(WG), 0, st,

@@ -86,6 +86,7 @@ const char* fmt_name(int fmt) {
     case QGEMV_FMT_Q4_K: return "qgemv_q4_k";
     case QGEMV_FMT_Q6_K: return "qgemv_q6_k";
     case QGEMV_FMT_Q8_0: return "qgemv_q8_0";
+    case QGEMV_FMT_Q6_K_R8: return "qgemv_q6_k_r8";
     default: return "qgemv";
     }
 }
@@ -156,7 +157,7 @@ const char* qgemv_status_str(int status) {
 }
 
 const char* qgemv_build_info(void) {
-    return "libqgemv abi=1 arch=gfx950 formats=q4_0,q4_k,q6_k,q8_0 act=int8/32+fp16+int32sum "
+    return "libqgemv abi=1 arch=gfx950 formats=q4_0,q4_k,q6_k,q8_0,q6_k_r8(repacked) act=int8/32+fp16+int32sum "
            "gemv=v_dot4_i32_i8,lds-row-stream,lanes-per-row{4,8,16,32,64} "
            "small_m=q4_k{dot4,mfma_i8_16x16x32},q6_k/q4_0{gemv_rows,mfma_i8_16x16x32} "
            "fused=q4_k_swiglu_quantize K_max=32768 M_max=64";
@@ -204,6 +205,29 @@ qgemv_status qgemv_q6_k(const void* w, int64_t N, int64_t K, const int8_t* q, co
 qgemv_status qgemv_q8_0(const void* w, int64_t N, int64_t K, const int8_t* q, const uint16_t* d,
                         const int32_t* s, float* y, qgemv_stream_t stream) {
     return gemv_common(QGEMV_FMT_Q8_0, w, N, K, q, d, s, y, stream);
+}
+
+qgemv_status qgemv_q6_k_r8(const void* w_r, int64_t N, int64_t K, const int8_t* q,
+                           const uint16_t* d, const int32_t* s, float* y, qgemv_stream_t stream) {
+    return gemv_common(QGEMV_FMT_Q6_K_R8, w_r, N, K, q, d, s, y, stream);
+}
+
+qgemv_status qgemv_q6_k_repack(const void* w, int64_t N, int64_t K, void* w_r,
+                               qgemv_stream_t stream) {
+    const char* name = "qgemv_q6_k_repack";
+    if (N < 0) return fail(QGEMV_E_SHAPE, "%s: N = %lld is negative", name, (long long)N);
+    if (N == 0) return ok();
+    if (!w || !w_r) return fail(QGEMV_E_NULL, "%s: NULL pointer argument", name);
+    qgemv_status st = check_k(K);
+    if (st != QGEMV_OK) return st;
+    if (N > INT32_MAX) return fail(QGEMV_E_SHAPE, "%s: N = %lld exceeds 2^31-1", name, (long long)N);
+    if (K > QGEMV_K_MAX)
+        return fail(QGEMV_E_UNSUPPORTED, "%s: K = %lld exceeds QGEMV_K_MAX = %d", name,
+                    (long long)K, QGEMV_K_MAX);
+    if (!aligned(w, 16) || !aligned(w_r, 16))
+        return fail(QGEMV_E_ALIGN, "%s: w and w_r must be 16-byte aligned", name);
+    if ((st = check_device()) != QGEMV_OK) return st;
+    return launched(qgemv::launch_q6k_repack(w, N, K, w_r, (hipStream_t)stream), name);
 }
 
 qgemv_status qgemm_q4_k_small_m(const void* w, int64_t N, int64_t K, int64_t M, const int8_t* q,
@@ -284,7 +308,7 @@ qgemv_status qgemv_block_dots(int fmt, const void* w, int64_t N, int64_t K, int6
     if (!w || !q || !dots) return fail(QGEMV_E_NULL, "%s: NULL pointer argument", name);
     qgemv_status st = check_k(K);
     if (st != QGEMV_OK) return st;
-    if (fmt < QGEMV_FMT_Q4_0 || fmt > QGEMV_FMT_Q8_0)
+    if (fmt < QGEMV_FMT_Q4_0 || fmt > QGEMV_FMT_Q6_K_R8)
         return fail(QGEMV_E_UNSUPPORTED, "%s: unknown format %d", name, fmt);
     if (K > QGEMV_K_MAX) return fail(QGEMV_E_UNSUPPORTED, "%s: K exceeds QGEMV_K_MAX", name);
     if (nrows * ((K + 255) / 64) / 256 >= ((int64_t)1 << 31))

@@ -193,6 +193,22 @@ struct Q6K {
         w.sc = ld8(p + 192 + 8 * h);             // scales of groups 8h .. 8h+7
         w.d = ld2(p + 208);
     }
+    // The repacked layout (QGEMV_FMT_Q6_K_R8): a row is tiles of 8
+    // super-blocks, each tile 1680 bytes = ql[8][128] | qh[8][64] | sc[8][16]
+    // | d[8] (fp16); super-block i of a tile keeps its bytes, only moved, so
+    // every field of a unit starts on a 16-byte (sc: 8-byte) boundary.
+    static constexpr int TILE_SB = 8, TILE_BYTES = 1680;
+    static constexpr int T_QH = 1024, T_SC = 1536, T_D = 1664;
+    __device__ static __forceinline__ void load_r8(const uint8_t* row, int u, W& w) {
+        const int S = u >> 2, i = S & 7;
+        const uint8_t* p = row + TILE_BYTES * (S >> 3);
+        const int h = (u >> 1) & 1, t = u & 1;
+        w.qa = ld16(p + 128 * i + 64 * h + 16 * t);
+        w.qb = ld16(p + 128 * i + 64 * h + 32 + 16 * t);
+        w.qh = ld16(p + T_QH + 64 * i + 32 * h + 16 * t);
+        w.sc = ld8(p + T_SC + 16 * i + 8 * h);
+        w.d = ld2(p + T_D + 2 * i);
+    }
     // Activation of unit u = quarter (h, t): group j (elements
     // 128h + 16t + 32j + 0..15 of the super-block) is a[4j .. 4j+3].
     // init[j] = -32 * (sum of those 16 activation codes) folds the code offset

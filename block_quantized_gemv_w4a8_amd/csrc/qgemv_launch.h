@@ -32,6 +32,7 @@ struct SwigluOut {
 };
 
 hipError_t launch_gemv(int fmt, const GemvArgs& a, hipStream_t st);
+hipError_t launch_q6k_repack(const void* w, int64_t N, int64_t K, void* wr, hipStream_t st);
 hipError_t launch_q4k_swiglu(const GemvArgs& a, const SwigluOut& so, hipStream_t st);
 hipError_t launch_block_dots(int fmt, const void* w, int64_t K, int64_t row0, int64_t nrows,
                              const int8_t* q, int32_t* dots, hipStream_t st);

@@ -78,7 +78,14 @@ typedef enum {
     QGEMV_E_LAUNCH = 6       /* the kernel launch itself failed */
 } qgemv_status;
 
-enum { QGEMV_FMT_Q4_0 = 0, QGEMV_FMT_Q4_K = 1, QGEMV_FMT_Q6_K = 2, QGEMV_FMT_Q8_0 = 3 };
+/* QGEMV_FMT_Q6_K_R8: Q6_K repacked by qgemv_q6_k_repack (see there). */
+enum {
+    QGEMV_FMT_Q4_0 = 0,
+    QGEMV_FMT_Q4_K = 1,
+    QGEMV_FMT_Q6_K = 2,
+    QGEMV_FMT_Q8_0 = 3,
+    QGEMV_FMT_Q6_K_R8 = 4
+};
 enum { QGEMV_VARIANT_AUTO = 0, QGEMV_VARIANT_DOT4 = 1, QGEMV_VARIANT_MFMA = 2 };
 
 /* Returns QGEMV_ABI_VERSION of the loaded library.  A caller built against a
@@ -185,11 +192,31 @@ qgemv_status qgemv_q4_k_swiglu_quantize(const void* w, int64_t N, int64_t K,
                                         uint16_t* d_out, int32_t* s_out, float* gu,
                                         float* h, qgemv_stream_t stream);
 
+/* Load-time repack of Q6_K weights for this device ("Backends and hardware",
+ * section "Repacking is a per-device decision now": a layout is chosen per
+ * device at load, the on-disk format stays the default).  Q6_K super-blocks
+ * are 210 bytes, so their fields sit at 2-byte alignment; the repacked row is
+ * tiles of 8 super-blocks, 1680 bytes each:
+ *   ql[8][128] | qh[8][64] | sc[8][16] | d[8] (fp16 bits)
+ * (super-block i of the tile keeps its ql, qh, sc and d bytes unchanged), so
+ * every field starts on a 16-byte boundary (sc: 8).  A row of S = Kp/256
+ * super-blocks takes ceil(S/8) * 1680 bytes -- the same as the native 210 * S
+ * when S % 8 == 0 -- and the super-blocks of a partial last tile are zero.
+ * w: native Q6_K [N rows], w_r: [N][ceil(S/8) * 1680] bytes; both 16-byte
+ * aligned, caller-owned, not overlapping.  Gates as for qgemv_q6_k. */
+qgemv_status qgemv_q6_k_repack(const void* w, int64_t N, int64_t K, void* w_r,
+                               qgemv_stream_t stream);
+/* qgemv_q6_k on weights repacked by qgemv_q6_k_repack (same K): the same
+ * arithmetic, with every weight field read from an aligned address. */
+qgemv_status qgemv_q6_k_r8(const void* w_r, int64_t N, int64_t K, const int8_t* q,
+                           const uint16_t* d, const int32_t* s, float* y,
+                           qgemv_stream_t stream);
+
 /* Validation: the int32 block dots of weight rows [row0, row0+nrows) against
  * one activation row q [Kp], computed by the same device code as the GEMV
  * kernels.  dots: int32 [nrows][nblk] with nblk = K/32 (Q4_0, Q8_0),
- * Kp/32 (Q4_K: sub-blocks of 32, codes 0..15, no min), Kp/16 (Q6_K: groups of
- * 16, codes minus 32); Q4_0 dots include the -8 offset.  "The way to tell a
+ * Kp/32 (Q4_K: sub-blocks of 32, codes 0..15, no min), Kp/16 (Q6_K and
+ * Q6_K_R8: groups of 16, codes minus 32); Q4_0 dots include the -8 offset.  "The way to tell a
  * SIMD bug from a block bug" ("Backends and hardware", section "CPU"). */
 qgemv_status qgemv_block_dots(int fmt, const void* w, int64_t N, int64_t K,
                               int64_t row0, int64_t nrows, const int8_t* q,

@@ -97,6 +97,15 @@ def test_gates_null_shape_limits_align():
     assert _status("qgemv_q6_k", A, 10, 65536, A, A, A, A, S) == qg.QGEMV_E_UNSUPPORTED
     assert _status("qgemm_q4_k_small_m", A, 8, 256, 65, A, A, A, A, 1, S) == qg.QGEMV_E_UNSUPPORTED
     assert _status("qgemm_q4_k_small_m", A, 8, 256, 4, A, A, A, A, 9, S) == qg.QGEMV_E_UNSUPPORTED
+    assert _status("qgemv_q6_k_repack", A, 4, 256, None, S) == qg.QGEMV_E_NULL
+    assert _status("qgemv_q6_k_repack", A, 4, 48, A, S) == qg.QGEMV_E_SHAPE
+    assert _status("qgemv_q6_k_repack", A, 4, 65536, A, S) == qg.QGEMV_E_UNSUPPORTED
+    assert _status("qgemv_q6_k_repack", A, 4, 256, A + 2, S) == qg.QGEMV_E_ALIGN
+    assert _status("qgemv_q6_k_repack", None, 0, 256, None, S) == qg.QGEMV_OK
+    assert _status("qgemv_q6_k_r8", A, 10, 256, A, A, A, None, S) == qg.QGEMV_E_NULL
+    assert _status("qgemv_q6_k_r8", A + 8, 10, 256, A, A, A, A, S) == qg.QGEMV_E_ALIGN
+    assert _status("qgemv_block_dots", 4, A, 4, 256, 0, 4, A, None, S) == qg.QGEMV_E_NULL
+    assert _status("qgemv_block_dots", 5, A, 4, 256, 0, 4, A, A, S) == qg.QGEMV_E_UNSUPPORTED
     for fn in ("qgemm_q6_k_small_m", "qgemm_q4_0_small_m"):
         assert _status(fn, A, 8, 256, 65, A, A, A, A, 1, S) == qg.QGEMV_E_UNSUPPORTED
         assert _status(fn, A, 8, 256, 4, A, A, A, A, 7, S) == qg.QGEMV_E_UNSUPPORTED
