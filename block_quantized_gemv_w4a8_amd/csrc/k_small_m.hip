@@ -182,11 +182,13 @@ struct MfmaGeom {
     static constexpr int BUF = WBYTES + G * ASTAGE;
 };
 
-// Wave (rt, kq, ks) of the workgroup computes weight tile rt (rows 16*rt ..
-// 16*rt + 15) over units kq, kq + KP, ... of every step and, within each,
-// over 32-blocks ks*BPW .. ks*BPW + BPW-1 (BPW = 8/KS); the KS*KP partial
-// sums of a tile are added in LDS at the end, always in the same order.  KP
-// splits K between waves where the matrix has too few rows to fill the chip.  Lane l: weight row 16*rt + l%16, K part 8*(l/16) of
+// Wave (rt, ms, kq, ks) of the workgroup computes weight tile rt (rows
+// 16*rt .. 16*rt + 15) against activation tiles ms*TPW .. ms*TPW + TPW-1
+// (TPW = MT/MS tiles of 16 rows), over units kq, kq + KP, ... of every step
+// and, within each, over 32-blocks ks*BPW .. ks*BPW + BPW-1 (BPW = 8/KS); the
+// KS*KP partial sums of a tile are added in LDS at the end, always in the
+// same order.  KP splits K between waves where the matrix has too few rows
+// to fill the chip; MS splits the activation rows where M is large.  Lane l: weight row 16*rt + l%16, K part 8*(l/16) of
 // each 32-block (the i8 MFMA operand layout); its outputs are rows
 // 16t + 4*(l/16) + i of that weight row.
 //
@@ -204,8 +206,8 @@ struct MfmaGeom {
 //   Q6_K  y += d*sc_g*dx*D  - (32*d*sc_g)(dx*sum16) (w = d*sc*(code - 32))
 // The second product of each line is a small dense product over the blocks
 // (groups) of a unit and goes to the fp32 MFMA.
-template <int FMT, int MT, int RT, int KS, int KP, int G, int R>
-__global__ __launch_bounds__(64 * RT * KS * KP) void k_small_m_mfma(const uint8_t* __restrict__ w,
+template <int FMT, int MT, int RT, int KS, int KP, int MS, int G, int R>
+__global__ __launch_bounds__(64 * RT * KS * KP * MS) void k_small_m_mfma(const uint8_t* __restrict__ w,
                                                                int N, int K, int Kp, int M,
                                                                const int8_t* __restrict__ q,
                                                                const uint16_t* __restrict__ d,
@@ -213,10 +215,12 @@ __global__ __launch_bounds__(64 * RT * KS * KP) void k_small_m_mfma(const uint8_
                                                                float* __restrict__ y) {
     static_assert(KS == 1 || KS == 2 || KS == 4, "32-blocks split over 1, 2 or 4 waves");
     static_assert(G % KP == 0 && (KP > 1 || G <= 2), "units of a step split evenly over KP");
+    static_assert(MT % MS == 0, "activation tiles split evenly over MS");
+    constexpr int TPW = MT / MS;                             // activation tiles per wave
     using GM = MfmaGeom<FMT, MT, RT, G>;
     using U = SmUnit<FMT>;
     constexpr int MP = GM::MP, ROWS = GM::ROWS, NCH = GM::NCH;
-    constexpr int NT = 64 * RT * KS * KP;                    // threads
+    constexpr int NT = 64 * RT * KS * KP * MS;               // threads
     constexpr int BPW = 8 / KS;                              // 32-blocks per wave and unit
     constexpr int WCH = ROWS * NCH;                          // 16-byte weight chunks per step
     constexpr int WPT = (WCH + NT - 1) / NT;
@@ -231,8 +235,10 @@ __global__ __launch_bounds__(64 * RT * KS * KP) void k_small_m_mfma(const uint8_
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int rt = wave % RT, part = wave / RT;               // part = ks + KS * kq
+    const int rt = wave % RT, ms = (wave / RT) % MS;
+    const int part = wave / (RT * MS);                        // part = ks + KS * kq
     const int ks = part % KS, kq = part / KS;
+    const int t0 = ms * TPW;                                  // first activation tile
     const int nl = lane & 15, kp = lane >> 4;
     const int row0 = blockIdx.x * ROWS;
     const int n = row0 + 16 * rt + nl;
@@ -348,13 +354,13 @@ __global__ __launch_bounds__(64 * RT * KS * KP) void k_small_m_mfma(const uint8_
     // one accumulator set per unit of a step (G independent chains), or a
     // single set, with the block order pinned, where MT is large and
     // registers are short (Q6_K and Q4_0 need more registers per block)
-    constexpr bool BIG = FMT == QGEMV_FMT_Q4_K ? MT >= 3 : MT >= 2;
+    constexpr bool BIG = FMT == QGEMV_FMT_Q4_K ? TPW >= 3 : TPW >= 2;
     constexpr int AG = (BIG || KP > 1) ? 1 : G;
-    f32x4 acc[AG][MT], acc2[AG][MT];
+    f32x4 acc[AG][TPW], acc2[AG][TPW];
 #pragma unroll
     for (int g = 0; g < AG; g++)
 #pragma unroll
-        for (int t = 0; t < MT; t++) {
+        for (int t = 0; t < TPW; t++) {
             acc[g][t] = f32x4{0.f, 0.f, 0.f, 0.f};
             acc2[g][t] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
@@ -403,7 +409,7 @@ __global__ __launch_bounds__(64 * RT * KS * KP) void k_small_m_mfma(const uint8_
             return blk0 + j < nbw ? h2f(lds2(smem, ow + 18 * j)) : 0.0f;
         };
 
-        auto mfma_block = [&](int jj, i32x4 (&D)[ND][MT]) {
+        auto mfma_block = [&](int jj, i32x4 (&D)[ND][TPW]) {
             const int j = P * BPW + jj;
             int o2 = oa + 32 * j;
             long B[ND];
@@ -439,15 +445,15 @@ __global__ __launch_bounds__(64 * RT * KS * KP) void k_small_m_mfma(const uint8_
                 B[1] = kp < 2 ? 0 : Bc;
             }
 #pragma unroll
-            for (int t = 0; t < MT; t++) {
+            for (int t = 0; t < TPW; t++) {
                 const long A = *reinterpret_cast<const long*>(
-                    smem + o2 + (16 * t + nl) * GM::ASTRIDE + 8 * kp);
+                    smem + o2 + (16 * (t0 + t) + nl) * GM::ASTRIDE + 8 * kp);
 #pragma unroll
                 for (int e = 0; e < ND; e++)
                     D[e][t] = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, B[e], zero, 0, 0, 0);
             }
         };
-        auto scale_block = [&](int jj, const i32x4 (&D)[ND][MT]) {
+        auto scale_block = [&](int jj, const i32x4 (&D)[ND][TPW]) {
             const int j = P * BPW + jj;
             float ws0, ws1 = 0.0f;
             if constexpr (FMT == QGEMV_FMT_Q4_K) {
@@ -462,8 +468,9 @@ __global__ __launch_bounds__(64 * RT * KS * KP) void k_small_m_mfma(const uint8_
             int o = oa + GM::ACODES + 4 * j * MP;
             if (PIN) asm volatile("" : "+s"(o));
 #pragma unroll
-            for (int t = 0; t < MT; t++) {
-                const f32x4 x4 = *reinterpret_cast<const f32x4*>(smem + o + 4 * (16 * t + 4 * kp));
+            for (int t = 0; t < TPW; t++) {
+                const f32x4 x4 =
+                    *reinterpret_cast<const f32x4*>(smem + o + 4 * (16 * (t0 + t) + 4 * kp));
 #pragma unroll
                 for (int i = 0; i < 4; i++) {
                     if constexpr (ND == 1) {
@@ -476,10 +483,10 @@ __global__ __launch_bounds__(64 * RT * KS * KP) void k_small_m_mfma(const uint8_
             }
             if (PIN) {
 #pragma unroll
-                for (int t = 0; t < MT; t++) asm volatile("" : "+v"(acc[ga][t]));
+                for (int t = 0; t < TPW; t++) asm volatile("" : "+v"(acc[ga][t]));
             }
         };
-        i32x4 D2[2][ND][MT];
+        i32x4 D2[2][ND][TPW];
         mfma_block(0, D2[0]);
 #pragma unroll
         for (int jj = 1; jj < BPW; jj++) {
@@ -500,8 +507,8 @@ __global__ __launch_bounds__(64 * RT * KS * KP) void k_small_m_mfma(const uint8_
                 const uint32_t sc = lds2(smem, ow + 192 + (gi & ~1));
                 const float b = 32.0f * fd * (float)sbyte(sc, gi & 1);
 #pragma unroll
-                for (int t = 0; t < MT; t++) {
-                    const int m = 16 * t + nl;
+                for (int t = 0; t < TPW; t++) {
+                    const int m = 16 * (t0 + t) + nl;
                     const float a = dx[(gi >> 1) * MP + m] * (float)s16[gi * MP + m];
                     acc2[ga][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc2[ga][t], 0, 0, 0);
                 }
@@ -520,8 +527,8 @@ __global__ __launch_bounds__(64 * RT * KS * KP) void k_small_m_mfma(const uint8_
                     b = mine ? 8.0f * q40_scale(jg + kp) : 0.0f;
                 }
 #pragma unroll
-                for (int t = 0; t < MT; t++) {
-                    const float a = dxs[(jg + kp) * MP + 16 * t + nl];
+                for (int t = 0; t < TPW; t++) {
+                    const float a = dxs[(jg + kp) * MP + 16 * (t0 + t) + nl];
                     acc2[ga][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc2[ga][t], 0, 0, 0);
                 }
             }
@@ -581,25 +588,25 @@ __global__ __launch_bounds__(64 * RT * KS * KP) void k_small_m_mfma(const uint8_
         for (int g = 1; g < AG; g++) v += acc[g][t][i] - acc2[g][t][i];
         return v;
     };
-    auto pidx = [&](int p, int t, int i) {
-        return (((p - 1) * RT + rt) * MT * 4 + 4 * t + i) * 64 + lane;
+    auto pidx = [&](int p, int t, int i) {   // t: this wave's tile index 0 .. TPW-1
+        return (((p - 1) * RT + rt) * MT * 4 + 4 * (t0 + t) + i) * 64 + lane;
     };
     if (NPART > 1 && part > 0) {
 #pragma unroll
-        for (int t = 0; t < MT; t++)
+        for (int t = 0; t < TPW; t++)
 #pragma unroll
             for (int i = 0; i < 4; i++) pbuf[pidx(part, t, i)] = partial(t, i);
     }
     if (NPART > 1) __syncthreads();
     if (part == 0 && n < N) {
 #pragma unroll
-        for (int t = 0; t < MT; t++)
+        for (int t = 0; t < TPW; t++)
 #pragma unroll
             for (int i = 0; i < 4; i++) {
                 float v = partial(t, i);
 #pragma unroll
                 for (int p = 1; p < NPART; p++) v += pbuf[pidx(p, t, i)];
-                const int m = 16 * t + 4 * kp + i;
+                const int m = 16 * (t0 + t) + 4 * kp + i;
                 if (m < M) y[(int64_t)m * N + n] = v;
             }
     }
@@ -608,15 +615,15 @@ __global__ __launch_bounds__(64 * RT * KS * KP) void k_small_m_mfma(const uint8_
 // RT: weight tiles per workgroup (the activation staged by a workgroup is
 // shared by 16*RT weight rows); KS, KP: waves sharing a tile's 32-blocks and
 // units; G: units per step; R: steps of global loads in flight.
-template <int FMT, int MT, int RT, int KS, int KP, int G, int R>
+template <int FMT, int MT, int RT, int KS, int KP, int MS, int G, int R>
 static hipError_t launch_mfma_cfg(const void* w, int64_t N, int64_t K, int64_t M,
                                   const int8_t* q, const uint16_t* d, const int32_t* s, float* y,
                                   hipStream_t st) {
     const int Kp = (int)((K + 255) / 256 * 256);
     const int64_t grid = (N + 16 * RT - 1) / (16 * RT);
-    hipLaunchKernelGGL((k_small_m_mfma<FMT, MT, RT, KS, KP, G, R>), dim3((unsigned)grid),
-                       dim3(64 * RT * KS * KP), 0, st, (const uint8_t*)w, (int)N, (int)K, Kp,
-                       (int)M, q, d, s, y);
+    hipLaunchKernelGGL((k_small_m_mfma<FMT, MT, RT, KS, KP, MS, G, R>), dim3((unsigned)grid),
+                       dim3(64 * RT * KS * KP * MS), 0, st, (const uint8_t*)w, (int)N, (int)K,
+                       Kp, (int)M, q, d, s, y);
     return hipGetLastError();
 }
 
@@ -631,21 +638,27 @@ static hipError_t launch_mfma(const void* w, int64_t N, int64_t K, int64_t M, co
                               const uint16_t* d, const int32_t* s, float* y, hipStream_t st) {
     const int mt = (int)((M + 15) / 16);
     const bool wide = (N + 15) / 16 >= kMfmaWideTiles;
-    // Q6_K's larger units and per-16 sums leave LDS for 2 tiles from MT = 3
+    // <FMT, MT, RT, KS, KP, MS, G, R>.  Wide matrices: 64 weight rows per
+    // workgroup share the staged activation and each wave takes every
+    // activation tile (splitting the tiles there costs more activation
+    // traffic than it gains; Q6_K's larger units leave LDS for 2 row tiles
+    // from MT = 3).  Narrow matrices also split K between waves and, from
+    // MT = 2, give each wave one activation tile (MS = MT), so a wave needs
+    // the registers of MT = 1 and the chip gets MT times the waves.
     constexpr int RT34 = FMT == QGEMV_FMT_Q6_K ? 2 : 4;
     if (wide) {
         switch (mt) {
-        case 1: return launch_mfma_cfg<FMT, 1, 2, 2, 1, 2, 2>(w, N, K, M, q, d, s, y, st);
-        case 2: return launch_mfma_cfg<FMT, 2, 4, 2, 1, 2, 2>(w, N, K, M, q, d, s, y, st);
-        case 3: return launch_mfma_cfg<FMT, 3, RT34, 2, 1, 2, 2>(w, N, K, M, q, d, s, y, st);
-        default: return launch_mfma_cfg<FMT, 4, RT34, 2, 1, 2, 2>(w, N, K, M, q, d, s, y, st);
+        case 1: return launch_mfma_cfg<FMT, 1, 2, 2, 1, 1, 2, 2>(w, N, K, M, q, d, s, y, st);
+        case 2: return launch_mfma_cfg<FMT, 2, 4, 2, 1, 1, 2, 2>(w, N, K, M, q, d, s, y, st);
+        case 3: return launch_mfma_cfg<FMT, 3, RT34, 2, 1, 1, 2, 2>(w, N, K, M, q, d, s, y, st);
+        default: return launch_mfma_cfg<FMT, 4, RT34, 2, 1, 1, 2, 2>(w, N, K, M, q, d, s, y, st);
         }
     }
     switch (mt) {
-    case 1: return launch_mfma_cfg<FMT, 1, 1, 1, 8, 8, 2>(w, N, K, M, q, d, s, y, st);
-    case 2: return launch_mfma_cfg<FMT, 2, 1, 1, 4, 4, 2>(w, N, K, M, q, d, s, y, st);
-    case 3: return launch_mfma_cfg<FMT, 3, 1, 1, 2, 2, 2>(w, N, K, M, q, d, s, y, st);
-    default: return launch_mfma_cfg<FMT, 4, 1, 1, 2, 2, 2>(w, N, K, M, q, d, s, y, st);
+    case 1: return launch_mfma_cfg<FMT, 1, 1, 1, 8, 1, 8, 2>(w, N, K, M, q, d, s, y, st);
+    case 2: return launch_mfma_cfg<FMT, 2, 1, 1, 4, 2, 4, 2>(w, N, K, M, q, d, s, y, st);
+    case 3: return launch_mfma_cfg<FMT, 3, 1, 1, 2, 3, 2, 2>(w, N, K, M, q, d, s, y, st);
+    default: return launch_mfma_cfg<FMT, 4, 1, 1, 2, 4, 2, 2>(w, N, K, M, q, d, s, y, st);
     }
 }
 
