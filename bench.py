@@ -483,6 +483,13 @@ def extras(qg, torch, np, synth, dev, R, c2, c3, args):
             us = time_kernel(torch, lambda c: qg.qgemm_q4_k_small_m(
                 w4[c], N4, K4, M, qm, dm, smm, ym, v), 50, 16)
             sm[f"M{M}_{vname}_us"] = round(us, 2)
+    for M in (1, 2):
+        xm = torch.from_numpy(np.ascontiguousarray(c4["x64"][:M])).to(dev)
+        qm, dm, smm = qg.act_buffers(M, K4, dev)
+        qg.qgemv_quantize_act(xm, M, K4, K4, qm, dm, smm)
+        ym = torch.empty((M, N4), dtype=torch.float32, device=dev)
+        sm[f"M{M}_auto_us"] = round(time_kernel(torch, lambda c: qg.qgemm_q4_k_small_m(
+            w4[c], N4, K4, M, qm, dm, smm, ym, qg.QGEMV_VARIANT_AUTO), 50, 16), 2)
     for M in (8, 64):
         best = min(sm[f"M{M}_dot4_us"], sm[f"M{M}_mfma_us"])
         sm[f"M{M}_weight_GBps"] = round(33030144 / best / 1e3, 1)

@@ -737,6 +737,9 @@ hipError_t launch_small_m(int fmt, const void* w, int64_t N, int64_t K, int64_t 
         variant == QGEMV_VARIANT_MFMA || (variant == QGEMV_VARIANT_AUTO && M >= kMfmaFromM);
     switch (fmt) {
     case QGEMV_FMT_Q4_K:
+        // one row under AUTO: the batch-1 GEMV streams the matrix fastest
+        if (variant == QGEMV_VARIANT_AUTO && M == 1)
+            return launch_rows_gemv(fmt, w, N, K, M, q, d, s, y, st);
         return mfma ? launch_mfma<QGEMV_FMT_Q4_K>(w, N, K, M, q, d, s, y, st)
                     : launch_dot4_q4k(w, N, K, M, q, d, s, y, st);
     case QGEMV_FMT_Q6_K:

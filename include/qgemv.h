@@ -143,7 +143,8 @@ qgemv_status qgemv_q8_0(const void* w, int64_t N, int64_t K, const int8_t* q,
  * gates: C = A x B is row-independent).  q [M][Kp], d/s [M][Kp/32],
  * y fp32 [M][N] row-major, 1 <= M <= QGEMV_M_MAX.
  * variant: QGEMV_VARIANT_DOT4 (4 x int8 dots), QGEMV_VARIANT_MFMA (int8
- * matrix cores), or QGEMV_VARIANT_AUTO (chooses by M). */
+ * matrix cores), or QGEMV_VARIANT_AUTO (chooses by M; M = 1 is qgemv_q4_k
+ * itself). */
 qgemv_status qgemm_q4_k_small_m(const void* w, int64_t N, int64_t K, int64_t M,
                                 const int8_t* q, const uint16_t* d, const int32_t* s,
                                 float* y, int variant, qgemv_stream_t stream);

@@ -143,6 +143,16 @@ def test_rows_variant_is_the_gemv(qg):
             y = torch.empty(N, dtype=torch.float32, device="cuda:0")
             qg.GEMV[fmt](wd, N, K, q[m], d[m], s[m], y)
             assert np.array_equal(Y[m].view(np.uint32), host(y).view(np.uint32)), (fmt, m)
+    # Q4_K under AUTO with one row is the batch-1 GEMV itself
+    N, K = 300, 4096
+    w = synth.q4_k_weights(g, N, K)
+    x, _ = synth.activation(g, 1, K)
+    wd = dev(w)
+    q, d, s = quantize(qg, x)
+    Y = small_m(qg, "q4_k", wd, N, K, (q, d, s), 1, qg.QGEMV_VARIANT_AUTO)
+    y = torch.empty(N, dtype=torch.float32, device="cuda:0")
+    qg.qgemv_q4_k(wd, N, K, q[0], d[0], s[0], y)
+    assert np.array_equal(Y[0].view(np.uint32), host(y).view(np.uint32))
 
 
 @pytest.mark.parametrize("fmt,M,N,K", [("q6_k", 8, 8200, 1024), ("q6_k", 40, 8192, 512),
