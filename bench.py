@@ -115,6 +115,9 @@ def main():
     ap.add_argument("--event-every", type=int, default=10,
                     help="bracket every n-th lm_head launch of the timed steps with HIP events "
                          "(an event pair still costs ~4 us of queue time)")
+    ap.add_argument("--small-m-profile", action="store_true",
+                    help="only run the small-M MFMA products (Q4_K 14336x4096, Q6_K 4096x14336 "
+                         "at M = 8 and 64), 20 calls each, for counter collection")
     ap.add_argument("--native-q6k", action="store_true",
                     help="run the Q6_K GEMVs on the on-disk layout instead of the repacked one")
     ap.add_argument("--unfused", action="store_true",
@@ -137,6 +140,9 @@ def main():
 
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    if args.small_m_profile:
+        small_m_profile(qg, torch, np, synth, dev)
+        return
     t0 = time.time()
     c2 = synth.config2()
     c3 = synth.config3()
@@ -282,6 +288,23 @@ def main():
     if extra:
         out["extra"] = extra
     print(json.dumps(out), flush=True)
+
+
+def small_m_profile(qg, torch, np, synth, dev):
+    """The small-M MFMA products alone, for rocprofv3 counter passes."""
+    g = np.random.default_rng(4)
+    for fmt, N, K in (("q4_k", 14336, 4096), ("q6_k", 4096, 14336)):
+        w = torch.from_numpy(synth.weights(fmt, g, N, K)).to(dev)
+        x64, _ = synth.activation(g, 64, K)
+        for M in (8, 64):
+            q, d, s = qg.act_buffers(M, K, dev)
+            qg.qgemv_quantize_act(torch.from_numpy(np.ascontiguousarray(x64[:M])).to(dev), M, K, K,
+                                  q, d, s)
+            y = torch.empty((M, N), dtype=torch.float32, device=dev)
+            for _ in range(20):
+                qg.SMALL_M[fmt](w, N, K, M, q, d, s, y, qg.QGEMV_VARIANT_MFMA)
+            torch.cuda.synchronize()
+            log(f"[small-m-profile] {fmt} {N}x{K} M={M} done")
 
 
 def time_kernel(torch, fn, iters, R):
