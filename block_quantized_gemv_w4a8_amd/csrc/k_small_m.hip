@@ -1,22 +1,26 @@
-// k_small_m.hip -- a few activation rows (the prefill chunk) against Q4_K
-// weights.  Output row m equals the batch-1 GEMV of activation row m (colibri
-// GPU backends, eligibility gates: C = A x B is row-independent).
+// k_small_m.hip -- a few activation rows (the prefill chunk) against Q4_K,
+// Q6_K or Q4_0 weights.  Output row m equals the batch-1 GEMV of activation
+// row m (colibri GPU backends, eligibility gates: C = A x B is
+// row-independent).
 //
-// DOT4 variant: the GEMV kernel's mapping (LPR lanes per weight row, one
-// 64-weight unit per lane step), except that each weight unit is loaded and
-// unpacked once and then dotted against MT activation rows staged in LDS, so
-// the weight stream is shared by the MT rows ("Backends and hardware",
-// section "CUDA": W4A8 inner product on 4 x int8 dots).
+// DOT4 variant (Q4_K): the GEMV kernel's mapping (LPR lanes per weight row,
+// one 64-weight unit per lane step), except that each weight unit is loaded
+// and unpacked once and then dotted against MT activation rows staged in
+// LDS, so the weight stream is shared by the MT rows ("Backends and
+// hardware", section "CUDA": W4A8 inner product on 4 x int8 dots).  For Q6_K
+// and Q4_0 the DOT4 variant is the batch-1 GEMV launched on each row.
 //
-// MFMA variant: where the work is a dense contraction (many rows), the int8
-// matrix cores do it.  Each 32-wide K block gets its own int8 MFMA
-// (v_mfma_i32_16x16x32_i8: a 16 x 16 tile of exact int32 block dots), because
-// both sides carry a scale per 32-block; the fp32 epilogue then adds
-// D * (d * sc_j) * dx per tile element.  The min term
-// sum_b (dmin * m_j) * (dx * s) is itself a small dense product and goes to
-// the fp32 MFMA (v_mfma_f32_16x16x4f32) instead of the vector ALUs.  Weights
-// and activation are staged through LDS with coalesced 16-byte loads, and
-// the eight sub-blocks of a super-block are split between two waves.
+// MFMA variant (all three formats): where the work is a dense contraction
+// (many rows), the int8 matrix cores do it.  Each 32-wide K block gets its
+// own int8 MFMA (v_mfma_i32_16x16x32_i8: a 16 x 16 tile of exact int32 block
+// dots; a Q6_K block takes two, one per 16-group), because both sides carry a
+// scale per block; the fp32 epilogue then applies the weight and activation
+// scales per tile element.  The remaining terms (the Q4_K min, the Q4_0 and
+// Q6_K code offsets) are small dense products over the blocks and go to the
+// fp32 MFMA (v_mfma_f32_16x16x4f32) instead of the vector ALUs.  Weights and
+// activation are staged through LDS with coalesced 16-byte loads; the waves
+// of a workgroup split the 32-blocks, the units of K and the activation tiles
+// as the matrix shape and M call for.
 #include <type_traits>
 
 #include "qgemv_device.h"

@@ -24,6 +24,8 @@
  *                               16 int8 scales (one per 16) | fp16 d;
  *                               w = d*scale*(code-32)
  *   Q8_0  34 B per 32 weights : fp16 d | 32 int8 codes; w = d*code
+ *   Q6_K_R8: Q6_K rows rearranged at load into aligned tiles of 8
+ *            super-blocks by qgemv_q6_k_repack (see there)
  * K-quant (Q4_K, Q6_K) rows hold ceil(K/256) super-blocks; the weights past K
  * in the last one must have zero codes, scales and mins.  Q4_0 / Q8_0 rows
  * hold exactly K/32 blocks.
