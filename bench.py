@@ -4,9 +4,12 @@
 One step = one batch-1 Llama-3.1-8B decode pass over the Llama-shaped
 matrices of the hot path, stream-ordered on one HIP stream with no host
 round trip:
-    quantize(x) -> gate|up  Q4_K 28672 x 4096 -> SiLU(gate)*up + requantize
-                -> down     Q6_K  4096 x 14336
-    quantize(x') -> lm_head Q6_K 128256 x 4096
+    quantize(x) + gate|up Q4_K 28672 x 4096 + SiLU(gate)*up + requantize
+                           (one launch)
+    -> down Q6_K 4096 x 14336
+    quantize(x') + lm_head Q6_K 128256 x 4096 (one launch)
+(--separate-quant quantizes x and x' in launches of their own; --unfused also
+splits gate|up from SiLU*up + requantize.)
 All inputs are seeded synthetic data (synth module) resident in HBM before the
 timed region; weights are rotated over --copies copies so consecutive steps do
 not read the same bytes (one copy is already 545 MB, twice the 256 MB
@@ -35,7 +38,8 @@ HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
 METRIC = "quantized GEMV weight GB/s and % of HBM peak at Llama-3-8B shapes, 1 GPU"
 WORKLOAD = ("llama3.1-8b decode step, batch 1: ffn gate|up q4_k 28672x4096 with fused "
             "silu*up requant -> down q6_k 4096x14336, then lm_head q6_k 128256x4096 "
-            "(q6_k repacked at load into aligned 8-super-block tiles, same bytes)")
+            "(activation quantization inside the gate|up and lm_head launches; "
+            "q6_k repacked at load into aligned 8-super-block tiles, same bytes)")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_q6k_lm_head.json")
 KERNEL_SOURCES = ["qgemv_device.h", "qgemv_quant.h", "k_gemv.hip", "k_quantize.hip",
                   "qgemv_api.cpp"]
@@ -87,6 +91,9 @@ class HipTimer:
 
 def workload_name(args) -> str:
     w = WORKLOAD
+    if args.unfused or args.separate_quant:
+        w = w.replace("activation quantization inside the gate|up and lm_head launches; ",
+                      "activation quantization in launches of its own; ")
     if args.unfused:
         w = w.replace("with fused", "then a separate")
     if args.native_q6k:
@@ -107,21 +114,26 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=300)
-    ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=1000,
+                    help="untimed steps first (0.1 s: the clocks settle; 30 steps read ~1 us "
+                         "per step slower)")
     ap.add_argument("--copies", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the per-kernel/config extras")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--event-every", type=int, default=10,
+    ap.add_argument("--event-every", type=int, default=30,
                     help="bracket every n-th lm_head launch of the timed steps with HIP events "
-                         "(an event pair still costs ~4 us of queue time)")
+                         "(each pair costs ~20 us of step time, so they are sampled)")
     ap.add_argument("--small-m-profile", action="store_true",
                     help="only run the small-M MFMA products (Q4_K 14336x4096, Q6_K 4096x14336 "
                          "at M = 8 and 64), 20 calls each, for counter collection")
     ap.add_argument("--native-q6k", action="store_true",
                     help="run the Q6_K GEMVs on the on-disk layout instead of the repacked one")
     ap.add_argument("--unfused", action="store_true",
-                    help="gate|up GEMV and SiLU*up requant as two launches (comparison)")
+                    help="gate|up GEMV and SiLU*up requant as two launches, and the activation "
+                         "quantizations as launches of their own (comparison)")
+    ap.add_argument("--separate-quant", action="store_true",
+                    help="quantize x and x' in launches of their own (comparison)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (for counter calibration)")
     args = ap.parse_args()
@@ -160,6 +172,7 @@ def main():
     # load-time repack of the Q6_K weights (outside the timed region; the
     # repacked rows hold the same bytes, only moved into aligned tiles)
     gemv_q6 = qg.qgemv_q6_k
+    fmt_q6 = qg.QGEMV_FMT_Q6_K
     if not args.native_q6k:
         def repack(wt, N, K):
             wr = torch.empty((N, qg.q6_k_r8_row_bytes(K)), dtype=torch.uint8, device=dev)
@@ -169,6 +182,7 @@ def main():
         w_hd = [repack(wt, Nh, Kh) for wt in w_hd]
         torch.cuda.synchronize()
         gemv_q6 = qg.qgemv_q6_k_r8
+        fmt_q6 = qg.QGEMV_FMT_Q6_K_R8
     x_ffn = torch.from_numpy(c2["x"]).to(dev)
     x_head = torch.from_numpy(c3["x"]).to(dev)
     q1, d1, s1 = qg.act_buffers(1, Kgu, dev)
@@ -187,20 +201,31 @@ def main():
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
 
+    sep_quant = args.unfused or args.separate_quant
+
     def step(i, ev=None):
         c = i % R
-        qg.qgemv_quantize_act(x_ffn, 1, Kgu, Kgu, q1, d1, s1, stream=sh)
+        if sep_quant:
+            qg.qgemv_quantize_act(x_ffn, 1, Kgu, Kgu, q1, d1, s1, stream=sh)
         if args.unfused:
             qg.qgemv_q4_k(w_gu[c], Ngu, Kgu, q1, d1, s1, gu, stream=sh)
             qg.qgemv_silu_mul_quantize(gu, Kd, q2, d2, s2, None, stream=sh)
-        else:
+        elif sep_quant:
             qg.qgemv_q4_k_swiglu_quantize(w_gu[c], Kd, Kgu, q1, d1, s1, q2, d2, s2, None, None,
                                           stream=sh)
+        else:
+            qg.qgemv_quantize_q4_k_swiglu(w_gu[c], Kd, Kgu, x_ffn, q1, d1, s1, q2, d2, s2,
+                                          None, None, stream=sh)
         gemv_q6(w_dn[c], Nd, Kd, q2, d2, s2, y_ffn, stream=sh)
-        qg.qgemv_quantize_act(x_head, 1, Kh, Kh, q3, d3, s3, stream=sh)
+        if sep_quant:
+            qg.qgemv_quantize_act(x_head, 1, Kh, Kh, q3, d3, s3, stream=sh)
         if ev is not None:
             ev.record(0, sh)
-        gemv_q6(w_hd[c], Nh, Kh, q3, d3, s3, logits, stream=sh)
+        if sep_quant:
+            gemv_q6(w_hd[c], Nh, Kh, q3, d3, s3, logits, stream=sh)
+        else:
+            qg.qgemv_quantize_gemv(fmt_q6, w_hd[c], Nh, Kh, x_head, q3, d3, s3, logits,
+                                   stream=sh)
         if ev is not None:
             ev.record(1, sh)
 
@@ -232,9 +257,10 @@ def main():
         f"event-bracketed launches")
 
     # dominant kernel roofline: algorithmic bytes per launch of the lm_head GEMV
-    # = N rows x (row weight bytes + 4 B output) + one activation row
+    # = N rows x (row weight bytes + 4 B output) + one activation row (codes,
+    # scales, sums) + (quantization in the launch) the fp32 input row
     act_bytes = Kh + 2 * (Kh // 32) + 4 * (Kh // 32)
-    head_alg = Nh * (synth.row_bytes("q6_k", Kh) + 4) + act_bytes
+    head_alg = Nh * (synth.row_bytes("q6_k", Kh) + 4) + act_bytes + (0 if sep_quant else 4 * Kh)
     achieved = head_alg / (head_avg_us * 1e-6) / 1e9
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
@@ -243,8 +269,10 @@ def main():
             traffic = tr.get("bytes_per_launch")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                "kernel": ("qgemv_q6_k lm_head 128256x4096" if args.native_q6k else
-                           "qgemv_q6_k_r8 lm_head 128256x4096 (repacked Q6_K)"),
+                "kernel": (("qgemv_q6_k lm_head 128256x4096" if args.native_q6k else
+                            "qgemv_q6_k_r8 lm_head 128256x4096 (repacked Q6_K)") +
+                           ("" if sep_quant else ", activation quantized in the launch "
+                            "(qgemv_quantize_gemv)")),
                 "avg_us": round(head_avg_us, 2),
                 "timed_launches": len(head_us),
                 "alg_bytes_per_launch": head_alg}
@@ -454,12 +482,35 @@ def extras(qg, torch, np, synth, dev, R, c2, c3, args):
     ex["gate_up_swiglu_fused_q4_k_28672x4096"] = {
         "us": round(us, 2), "weight_GBps": round(wb / us / 1e3, 1),
         "hbm_frac": round(wb / us / 1e3 / HBM_PEAK_GBPS, 4), "calls_per_s": round(1e6 / us)}
+    # ... and with the quantisation of x in the same launch
+    xg = torch.from_numpy(c2["x"]).to(dev)
+    us = time_kernel(torch, lambda c: qg.qgemv_quantize_q4_k_swiglu(
+        wsw[c], Kd, Kgu, xg, qa, da, sa, qo, do, so, None, None), 100, 8)
+    ex["quantize_gate_up_swiglu_fused_q4_k_28672x4096"] = {
+        "us": round(us, 2), "weight_GBps": round(wb / us / 1e3, 1),
+        "hbm_frac": round(wb / us / 1e3 / HBM_PEAK_GBPS, 4), "calls_per_s": round(1e6 / us)}
     del wsw
     hx = np.random.default_rng(0).standard_normal((1, Kd)).astype(np.float32)
     ex["down_q6_k_4096x14336"] = gemv_case("q6_k", c2["w_down"], Nd, Kd, hx, 11)
     ex["lm_head_q6_k_128256x4096"] = gemv_case("q6_k", c3["w"], Nh, Kh, c3["x"], 2)
     ex["lm_head_q6_k_r8_128256x4096"] = gemv_case("q6_k_r8", c3["w"], Nh, Kh, c3["x"], 2)
     ex["down_q6_k_r8_4096x14336"] = gemv_case("q6_k_r8", c2["w_down"], Nd, Kd, hx, 11)
+    # lm_head (repacked) with the quantisation of x in the same launch
+    wh = torch.from_numpy(c3["w"]).to(dev)
+    whr = [torch.empty((Nh, qg.q6_k_r8_row_bytes(Kh)), dtype=torch.uint8, device=dev)]
+    qg.qgemv_q6_k_repack(wh, Nh, Kh, whr[0])
+    del wh
+    whr.append(whr[0].clone())
+    xh = torch.from_numpy(c3["x"]).to(dev)
+    qh, dh, sh_ = qg.act_buffers(1, Kh, dev)
+    yh = torch.empty(Nh, dtype=torch.float32, device=dev)
+    us = time_kernel(torch, lambda c: qg.qgemv_quantize_gemv(
+        qg.QGEMV_FMT_Q6_K_R8, whr[c], Nh, Kh, xh, qh, dh, sh_, yh), 100, 2)
+    wb = synth.logical_bytes("q6_k", Nh, Kh)
+    ex["lm_head_quantize_gemv_q6_k_r8_128256x4096"] = {
+        "us": round(us, 2), "weight_GBps": round(wb / us / 1e3, 1),
+        "hbm_frac": round(wb / us / 1e3 / HBM_PEAK_GBPS, 4), "calls_per_s": round(1e6 / us)}
+    del whr
     # cache-resident (single 48 MB copy of down, read again and again)
     one = gemv_case("q6_k", c2["w_down"], Nd, Kd, hx, 1)
     ex["down_q6_k_cache_resident_single_copy"] = one

@@ -44,6 +44,7 @@ EXPORTS = [
     "qgemv_q6_k_repack", "qgemv_q6_k_r8",
     "qgemm_q4_k_small_m", "qgemm_q6_k_small_m", "qgemm_q4_0_small_m",
     "qgemv_silu_mul_quantize", "qgemv_q4_k_swiglu_quantize",
+    "qgemv_quantize_gemv", "qgemv_quantize_q4_k_swiglu",
     "qgemv_block_dots",
 ]
 
@@ -68,6 +69,11 @@ _lib.qgemv_silu_mul_quantize.restype = _I
 _lib.qgemv_silu_mul_quantize.argtypes = [_P, _I64, _P, _P, _P, _P, _P]
 _lib.qgemv_q4_k_swiglu_quantize.restype = _I
 _lib.qgemv_q4_k_swiglu_quantize.argtypes = [_P, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P]
+_lib.qgemv_quantize_q4_k_swiglu.restype = _I
+_lib.qgemv_quantize_q4_k_swiglu.argtypes = [_P, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                            _P]
+_lib.qgemv_quantize_gemv.restype = _I
+_lib.qgemv_quantize_gemv.argtypes = [_I, _P, _I64, _I64, _P, _P, _P, _P, _P, _P]
 _lib.qgemv_block_dots.restype = _I
 _lib.qgemv_block_dots.argtypes = [_I, _P, _I64, _I64, _I64, _I64, _P, _P, _P]
 
@@ -198,6 +204,19 @@ def qgemv_q4_k_swiglu_quantize(w, N, K, q, d, s, q_out, d_out, s_out, gu=None, h
                                                   _ptr(q_out), _ptr(d_out), _ptr(s_out), _ptr(gu),
                                                   _ptr(h), _stream(stream)),
                   "qgemv_q4_k_swiglu_quantize")
+
+
+def qgemv_quantize_q4_k_swiglu(w, N, K, x, q, d, s, q_out, d_out, s_out, gu=None, h=None,
+                               stream=None):
+    return _check(_lib.qgemv_quantize_q4_k_swiglu(_ptr(w), N, K, _ptr(x), _ptr(q), _ptr(d),
+                                                  _ptr(s), _ptr(q_out), _ptr(d_out), _ptr(s_out),
+                                                  _ptr(gu), _ptr(h), _stream(stream)),
+                  "qgemv_quantize_q4_k_swiglu")
+
+
+def qgemv_quantize_gemv(fmt, w, N, K, x, q, d, s, y, stream=None):
+    return _check(_lib.qgemv_quantize_gemv(fmt, _ptr(w), N, K, _ptr(x), _ptr(q), _ptr(d), _ptr(s),
+                                           _ptr(y), _stream(stream)), "qgemv_quantize_gemv")
 
 
 def qgemv_block_dots(fmt, w, N, K, row0, nrows, q, dots, stream=None):

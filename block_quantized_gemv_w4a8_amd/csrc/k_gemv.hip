@@ -392,6 +392,63 @@ struct UnitLds<QGEMV_FMT_Q8_0> {
 };
 
 // Byte offset of unit u within a row, and the first block of unit u.
+// An fp32 activation row quantised by the whole workgroup into LDS: codes
+// aq [Kp], fp16 scale bits ad [Kp/32] and code sums as [Kp/32], blocks past K
+// zero.  The block quantiser is the one of k_quantize_act with 2 lanes per
+// block of 32 (16 consecutive values each) instead of 8: max and sum are
+// exact, so the bits are the same, and the per-block work (max, scale, sum)
+// is shared by 16 values per lane.  One pass covers 128 blocks; each load's
+// address is clamped into x and half-blocks past K are masked to zero.  The
+// first pass's loads are issued by the caller (xq_load) ahead of its weight
+// loads.
+constexpr int XQ_BATCH = WG / 2;   // blocks per pass
+
+__device__ __forceinline__ void xq_load(const float* __restrict__ x, int K, int b0,
+                                        f32x4 (&v)[4]) {
+    const int e = 32 * (b0 + (threadIdx.x >> 1)) + 16 * (threadIdx.x & 1);
+#pragma unroll
+    for (int k = 0; k < 4; k++) v[k] = *reinterpret_cast<const f32x4*>(x + min(e + 4 * k, K - 4));
+}
+
+__device__ __forceinline__ void xq_batch(const f32x4 (&v)[4], int K, int nb, int b0, int8_t* aq,
+                                         uint16_t* ad, int32_t* as) {
+    const int b = b0 + (threadIdx.x >> 1), half = threadIdx.x & 1;
+    const int e = 32 * b + 16 * half;
+    const bool in = e < K;
+    float vv[16];
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+        vv[4 * k] = in ? v[k].x : 0.0f;
+        vv[4 * k + 1] = in ? v[k].y : 0.0f;
+        vv[4 * k + 2] = in ? v[k].z : 0.0f;
+        vv[4 * k + 3] = in ? v[k].w : 0.0f;
+    }
+    const QBlockL<2> r = quantize_block<2>(vv);
+    if (b < nb) {
+        *reinterpret_cast<u32x4*>(aq + e) = u32x4{r.packed[0], r.packed[1], r.packed[2], r.packed[3]};
+        if (half == 0) {
+            ad[b] = (uint16_t)r.dbits;
+            as[b] = r.sum;
+        }
+    }
+}
+
+__device__ __forceinline__ void quantize_row_lds(const float* __restrict__ x, int K, int Kp,
+                                                 const f32x4 (&first)[4], int8_t* aq,
+                                                 uint16_t* ad, int32_t* as) {
+    const int nb = Kp / 32;
+    xq_batch(first, K, nb, 0, aq, ad, as);
+    for (int b0 = XQ_BATCH; b0 < nb; b0 += XQ_BATCH) {
+        f32x4 v[4];
+        xq_load(x, K, b0, v);
+        xq_batch(v, K, nb, b0, aq, ad, as);
+    }
+}
+
+// Bytes of LDS an in-kernel quantised activation row takes (codes, fp16
+// scales, int32 sums).
+__host__ __device__ inline int act_lds_bytes(int Kp) { return Kp + Kp / 16 + Kp / 8; }
+
 template <int FMT>
 __host__ __device__ inline int unit_byte(int u) {
     if (FMT == QGEMV_FMT_Q4_K) return (u / 4) * 144;
@@ -423,17 +480,19 @@ __host__ __device__ inline int unit_byte(int u) {
 // (the same device functions as k_silu_mul_quantize); the [gate | up] and h
 // values are stored only where asked for.  Workgroup 0 also zeroes the
 // activation blocks between nh and the next multiple of 256.
-template <int FMT, int UPL, int WK, int NL, bool NT, bool SW>
+template <int FMT, int UPL, int WK, int NL, bool NT, bool SW, bool XQ>
 __global__ __launch_bounds__(WG) void k_gemv_lds(const uint8_t* __restrict__ w, int N, int U,
                                                   int US, int nbw, int row_bytes, int buf_bytes,
                                                   const int8_t* __restrict__ q,
                                                   const uint16_t* __restrict__ d,
                                                   const int32_t* __restrict__ s,
-                                                  float* __restrict__ y, const SwigluOut so) {
+                                                  float* __restrict__ y, const SwigluOut so,
+                                                  const ActIn ai) {
     extern __shared__ __align__(16) uint8_t lds[];
     constexpr int LPR = 64;
     constexpr int RPP = 4 / WK;
     __shared__ float part[SEGP * RPP * WK];
+    __shared__ float hseg[SW ? 32 * (SEGP * RPP / 64) : 1];   // SW: h of a segment's blocks
     using UnitT = Unit<FMT>;
     using WT = typename UnitT::W;
     using UL = UnitLds<FMT>;
@@ -448,15 +507,23 @@ __global__ __launch_bounds__(WG) void k_gemv_lds(const uint8_t* __restrict__ w, 
     ActReg<FMT> A[UPL];
     int ul[UPL];
     bool ok[UPL], has1[UPL];
+    auto load_act = [&](const int8_t* aq, const uint16_t* ad, const int32_t* as) {
 #pragma unroll
-    for (int i = 0; i < UPL; i++) {
-        const int u = u_lo + lane + LPR * i;
-        ok[i] = u < u_hi;
-        const int uc = ok[i] ? u : u_hi - 1;
-        A[i].load(q, d, s, uc);
-        ul[i] = uc - u_lo;
-        has1[i] = 2 * uc + 1 < nbw;
-    }
+        for (int i = 0; i < UPL; i++) {
+            const int u = u_lo + lane + LPR * i;
+            ok[i] = u < u_hi;
+            const int uc = ok[i] ? u : u_hi - 1;
+            A[i].load(aq, ad, as, uc);
+            ul[i] = uc - u_lo;
+            has1[i] = 2 * uc + 1 < nbw;
+        }
+    };
+    if constexpr (!XQ) load_act(q, d, s);
+    // XQ: the activation row, quantised in this workgroup, after the slice buffers
+    const int Kp = (32 * nbw + 255) / 256 * 256;
+    int8_t* const aq = reinterpret_cast<int8_t*>(lds + 8 * buf_bytes);
+    uint16_t* const ad = reinterpret_cast<uint16_t*>(lds + 8 * buf_bytes + Kp);
+    int32_t* const as = reinterpret_cast<int32_t*>(lds + 8 * buf_bytes + Kp + Kp / 16);
 
     uint8_t* buf0 = lds + (2 * wave) * buf_bytes;
     uint8_t* buf1 = buf0 + buf_bytes;
@@ -526,13 +593,39 @@ __global__ __launch_bounds__(WG) void k_gemv_lds(const uint8_t* __restrict__ w, 
     for (int64_t p0 = 0; p0 < npass_all; p0 += SEGP) {
         const int np = (int)min((int64_t)SEGP, npass_all - p0);
         u32x4 Ra[NL], Rb[NL];
-        int da = stage(Ra, row_of(p0));
-        commit(Ra, da, buf0);
-        int d0 = da, d1;
-        da = stage(Ra, row_of(p0 + 1));
-        __builtin_amdgcn_sched_barrier(0);
-        int db = stage(Rb, row_of(p0 + 2));
-        __builtin_amdgcn_sched_barrier(0);
+        int da, db, d0, d1;
+        {
+            // three rows requested before the first is committed (XQ: after
+            // the loads of x, which is what the waves wait for first; the
+            // rows stream in while the workgroup quantises x)
+            const bool xq = XQ && p0 == 0;
+            f32x4 xv[4];
+            if (xq) xq_load(ai.x, 32 * nbw, 0, xv);
+            __builtin_amdgcn_sched_barrier(0);
+            u32x4 Rc[NL];
+            const int dc = stage(Rc, row_of(p0));
+            __builtin_amdgcn_sched_barrier(0);
+            da = stage(Ra, row_of(p0 + 1));
+            __builtin_amdgcn_sched_barrier(0);
+            db = stage(Rb, row_of(p0 + 2));
+            __builtin_amdgcn_sched_barrier(0);
+            if (xq) {
+                quantize_row_lds(ai.x, 32 * nbw, Kp, xv, aq, ad, as);
+                __syncthreads();
+                load_act(aq, ad, as);
+                if (blockIdx.x == 0) {
+                    for (int t = threadIdx.x; t < Kp / 16; t += WG)
+                        *reinterpret_cast<u32x4*>(ai.q + 16 * t) =
+                            *reinterpret_cast<const u32x4*>(aq + 16 * t);
+                    for (int t = threadIdx.x; t < Kp / 32; t += WG) {
+                        ai.d[t] = ad[t];
+                        ai.s[t] = as[t];
+                    }
+                }
+            }
+            commit(Rc, dc, buf0);
+            d0 = dc;
+        }
         for (int p = 0; p < np; p += 2) {
             finish_row(dot_row(buf0, d0), p);
             commit(Ra, da, buf1);
@@ -557,29 +650,34 @@ __global__ __launch_bounds__(WG) void k_gemv_lds(const uint8_t* __restrict__ w, 
                 }
             }
         } else {
-            // row l of the segment's output block j is part[(64 j + l) * WK + kq]
+            // row l of the segment's output block j is part[(64 j + l) * WK + kq];
+            // one thread per value forms h, then 8 lanes per block quantise it
             const int nblk = np / GPB;
             const int t = threadIdx.x;
+            if (t < 32 * nblk) {
+                const int j = t >> 5, i = t & 31;
+                const int64_t hb = blockIdx.x + (p0 / GPB + j) * G;
+                float g = part[(64 * j + i) * WK], u = part[(64 * j + 32 + i) * WK];
+#pragma unroll
+                for (int kk = 1; kk < WK; kk++) {
+                    g += part[(64 * j + i) * WK + kk];
+                    u += part[(64 * j + 32 + i) * WK + kk];
+                }
+                const float hv = silu_mul(g, u);
+                hseg[t] = hv;
+                if (so.gu) {
+                    so.gu[32 * hb + i] = g;
+                    so.gu[so.nh + 32 * hb + i] = u;
+                }
+                if (so.h) so.h[32 * hb + i] = hv;
+            }
+            __syncthreads();
             if (t < 8 * nblk) {
                 const int j = t >> 3, sub = t & 7;
                 const int64_t hb = blockIdx.x + (p0 / GPB + j) * G;
                 float v[4];
 #pragma unroll
-                for (int k = 0; k < 4; k++) {
-                    const int i = 4 * sub + k;
-                    float g = part[(64 * j + i) * WK], u = part[(64 * j + 32 + i) * WK];
-#pragma unroll
-                    for (int kk = 1; kk < WK; kk++) {
-                        g += part[(64 * j + i) * WK + kk];
-                        u += part[(64 * j + 32 + i) * WK + kk];
-                    }
-                    v[k] = silu_mul(g, u);
-                    if (so.gu) {
-                        so.gu[32 * hb + i] = g;
-                        so.gu[so.nh + 32 * hb + i] = u;
-                    }
-                    if (so.h) so.h[32 * hb + i] = v[k];
-                }
+                for (int k = 0; k < 4; k++) v[k] = hseg[32 * j + 4 * sub + k];
                 const QBlock r = quantize_block8(v);
                 *reinterpret_cast<uint32_t*>(so.q + 32 * hb + 4 * sub) = r.packed;
                 if (sub == 0) {
@@ -724,7 +822,7 @@ static hipError_t launch_gemv_cfg(const GemvArgs& a, int U, hipStream_t st) {
 constexpr bool kLdsStream = true;
 constexpr bool kStreamNT = true;
 
-template <int FMT, int UPL, int WK, int NL, bool SW>
+template <int FMT, int UPL, int WK, int NL, bool SW, bool XQ>
 static int resident_workgroups_lds(int smem) {
     static std::atomic<int> cache[64];
     int dev = 0;
@@ -733,7 +831,7 @@ static int resident_workgroups_lds(int smem) {
     if (v > 0) return v;
     int per_cu = 0, cus = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, k_gemv_lds<FMT, UPL, WK, NL, kStreamNT, SW>, WG, smem) != hipSuccess ||
+            &per_cu, k_gemv_lds<FMT, UPL, WK, NL, kStreamNT, SW, XQ>, WG, smem) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         per_cu <= 0 || cus <= 0) {
         (void)hipGetLastError();
@@ -749,14 +847,16 @@ static int resident_workgroups_lds(int smem) {
 // fastest; more waves add in-flight requests without adding bandwidth.
 constexpr int kLdsWgPerCu = 2;
 
-template <int FMT, int UPL, int WK, int NL, bool SW>
-static hipError_t launch_lds_cfg(const GemvArgs& a, const SwigluOut& so, int U, int US,
-                                 int buf_bytes, hipStream_t st) {
+template <int FMT, int UPL, int WK, int NL, bool SW, bool XQ>
+static hipError_t launch_lds_cfg(const GemvArgs& a, const SwigluOut& so, const ActIn& ai, int U,
+                                 int US, int buf_bytes, hipStream_t st) {
     constexpr int RPP = 4 / WK;
-    const int smem = 8 * buf_bytes;  // 4 waves x 2 buffers
+    const int Kp = (int)((a.K + 255) / 256 * 256);
+    // 4 waves x 2 slice buffers, then (XQ) the quantised activation row
+    const int smem = 8 * buf_bytes + (XQ ? act_lds_bytes(Kp) : 0);
     // work items: row groups, or (SW) output blocks of 32
     const int64_t items = SW ? so.nh / 32 : (a.N + RPP - 1) / RPP;
-    int64_t resident = resident_workgroups_lds<FMT, UPL, WK, NL, SW>(smem);
+    int64_t resident = resident_workgroups_lds<FMT, UPL, WK, NL, SW, XQ>(smem);
     int cus = 0, dev = 0;
     if (hipGetDevice(&dev) == hipSuccess &&
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
@@ -764,9 +864,9 @@ static hipError_t launch_lds_cfg(const GemvArgs& a, const SwigluOut& so, int U, 
         resident = (int64_t)kLdsWgPerCu * cus;
     const int64_t passes = (items + resident - 1) / resident;
     const int64_t grid = (items + passes - 1) / passes;
-    hipLaunchKernelGGL((k_gemv_lds<FMT, UPL, WK, NL, kStreamNT, SW>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((k_gemv_lds<FMT, UPL, WK, NL, kStreamNT, SW, XQ>), dim3((unsigned)grid),
                        dim3(WG), smem, st, (const uint8_t*)a.w, (int)a.N, U, US, (int)(a.K / 32),
-                       row_bytes_of(FMT, a.K), buf_bytes, a.q, a.d, a.s, a.y, so);
+                       row_bytes_of(FMT, a.K), buf_bytes, a.q, a.d, a.s, a.y, so, ai);
     return hipGetLastError();
 }
 
@@ -799,37 +899,44 @@ static SliceGeom slice_geom(int64_t K, int U, int WK) {
 }
 
 // The LDS-streaming kernels take at most 8 chunks per lane and 8 slice
-// buffers (each with 16 bytes of slack for the aligned-dword field reads)
-// within 64 KB of LDS minus the parked row results.
+// buffers (each with 16 bytes of slack for the aligned-dword field reads),
+// plus the quantised activation row when they form it themselves, within
+// 64 KB of LDS minus the parked row results.
 template <int FMT>
-static bool lds_slice_fits(const SliceGeom& g) {
-    return (g.nchunk + 63) / 64 <= 8 && 8 * (16 * g.nchunk + 16) <= 65536 - 8192;
+static bool lds_slice_fits(const SliceGeom& g, int act_bytes = 0) {
+    return (g.nchunk + 63) / 64 <= 8 && 8 * (16 * g.nchunk + 16) + act_bytes <= 65536 - 8192;
 }
 
-template <int FMT, int UPL, int WK, bool SW = false>
+template <int FMT, int UPL, int WK, bool SW = false, bool XQ = false>
 static hipError_t launch_lds_wk(const GemvArgs& a, int U, const SliceGeom& g, hipStream_t st,
-                                const SwigluOut& so = SwigluOut{}) {
+                                const SwigluOut& so = SwigluOut{}, const ActIn& ai = ActIn{}) {
     const int buf_bytes = 16 * g.nchunk + 16;
     const int nl = (g.nchunk + 63) / 64;  // 16-byte chunks per lane
-    if (nl <= 2) return launch_lds_cfg<FMT, UPL, WK, 2, SW>(a, so, U, g.US, buf_bytes, st);
-    if (nl <= 3) return launch_lds_cfg<FMT, UPL, WK, 3, SW>(a, so, U, g.US, buf_bytes, st);
-    if (nl <= 4) return launch_lds_cfg<FMT, UPL, WK, 4, SW>(a, so, U, g.US, buf_bytes, st);
-    if (nl <= 6) return launch_lds_cfg<FMT, UPL, WK, 6, SW>(a, so, U, g.US, buf_bytes, st);
-    return launch_lds_cfg<FMT, UPL, WK, 8, SW>(a, so, U, g.US, buf_bytes, st);
+    if (nl <= 2) return launch_lds_cfg<FMT, UPL, WK, 2, SW, XQ>(a, so, ai, U, g.US, buf_bytes, st);
+    if (nl <= 3) return launch_lds_cfg<FMT, UPL, WK, 3, SW, XQ>(a, so, ai, U, g.US, buf_bytes, st);
+    if (nl <= 4) return launch_lds_cfg<FMT, UPL, WK, 4, SW, XQ>(a, so, ai, U, g.US, buf_bytes, st);
+    if (nl <= 6) return launch_lds_cfg<FMT, UPL, WK, 6, SW, XQ>(a, so, ai, U, g.US, buf_bytes, st);
+    return launch_lds_cfg<FMT, UPL, WK, 8, SW, XQ>(a, so, ai, U, g.US, buf_bytes, st);
+}
+
+// Split-K of the LDS-streaming kernel: waves per row.
+static int lds_wk(int U) { return U > 128 ? 4 : (U > 64 ? 2 : 1); }
+
+template <int FMT, bool SW, bool XQ>
+static hipError_t launch_lds_fmt(const GemvArgs& a, int U, const SliceGeom& g, hipStream_t st,
+                                 const SwigluOut& so, const ActIn& ai) {
+    if (U > 256) return launch_lds_wk<FMT, 2, 4, SW, XQ>(a, U, g, st, so, ai);
+    if (U > 128) return launch_lds_wk<FMT, 1, 4, SW, XQ>(a, U, g, st, so, ai);
+    if (U > 64) return launch_lds_wk<FMT, 1, 2, SW, XQ>(a, U, g, st, so, ai);
+    return launch_lds_wk<FMT, 1, 1, SW, XQ>(a, U, g, st, so, ai);
 }
 
 template <int FMT>
 static hipError_t launch_gemv_fmt(const GemvArgs& a, hipStream_t st) {
     const int U = units_of(FMT, a.K);
     if (kLdsStream && U > 32) {
-        const int WK = U > 128 ? 4 : (U > 64 ? 2 : 1);
-        const SliceGeom g = slice_geom<FMT>(a.K, U, WK);
-        if (lds_slice_fits<FMT>(g)) {
-            if (U > 256) return launch_lds_wk<FMT, 2, 4>(a, U, g, st);
-            if (U > 128) return launch_lds_wk<FMT, 1, 4>(a, U, g, st);
-            if (U > 64) return launch_lds_wk<FMT, 1, 2>(a, U, g, st);
-            return launch_lds_wk<FMT, 1, 1>(a, U, g, st);
-        }
+        const SliceGeom g = slice_geom<FMT>(a.K, U, lds_wk(U));
+        if (lds_slice_fits<FMT>(g)) return launch_lds_fmt<FMT, false, false>(a, U, g, st, {}, {});
     }
     if (U > 256) return launch_gemv_cfg<FMT, 64, 2, 4>(a, U, st);
     if (U > 128) return launch_gemv_cfg<FMT, 64, 1, 4>(a, U, st);
@@ -841,19 +948,46 @@ static hipError_t launch_gemv_fmt(const GemvArgs& a, hipStream_t st) {
     return launch_gemv_cfg<FMT, 4, 1, 1>(a, U, st);
 }
 
+// Quantise x and multiply in one launch where the rows take the LDS-streaming
+// kernel and its LDS also holds the activation row; otherwise the two
+// launches it stands for (same bits either way).
+template <int FMT>
+static hipError_t launch_quantize_gemv_fmt(const GemvArgs& a, const ActIn& ai, hipStream_t st) {
+    const int U = units_of(FMT, a.K);
+    const int Kp = (int)((a.K + 255) / 256 * 256);
+    if (kLdsStream && U > 32) {
+        const SliceGeom g = slice_geom<FMT>(a.K, U, lds_wk(U));
+        if (lds_slice_fits<FMT>(g, act_lds_bytes(Kp)))
+            return launch_lds_fmt<FMT, false, true>(a, U, g, st, {}, ai);
+    }
+    hipError_t e = launch_quantize_act(ai.x, 1, a.K, a.K, ai.q, ai.d, ai.s, st);
+    if (e != hipSuccess) return e;
+    GemvArgs b = a;
+    b.q = ai.q;
+    b.d = ai.d;
+    b.s = ai.s;
+    return launch_gemv_fmt<FMT>(b, st);
+}
+
 // The fused gate|up product always takes the LDS-streaming kernel (with the
 // split-K of launch_gemv_fmt); every Q4_K row up to QGEMV_K_MAX fits its
-// slice buffers.
+// slice buffers, and its activation row too when the kernel forms it.
 hipError_t launch_q4k_swiglu(const GemvArgs& a, const SwigluOut& so, hipStream_t st) {
     constexpr int FMT = QGEMV_FMT_Q4_K;
     const int U = units_of(FMT, a.K);
-    const int WK = U > 128 ? 4 : (U > 64 ? 2 : 1);
-    const SliceGeom g = slice_geom<FMT>(a.K, U, WK);
+    const SliceGeom g = slice_geom<FMT>(a.K, U, lds_wk(U));
     if (!lds_slice_fits<FMT>(g)) return hipErrorInvalidValue;
-    if (U > 256) return launch_lds_wk<FMT, 2, 4, true>(a, U, g, st, so);
-    if (U > 128) return launch_lds_wk<FMT, 1, 4, true>(a, U, g, st, so);
-    if (U > 64) return launch_lds_wk<FMT, 1, 2, true>(a, U, g, st, so);
-    return launch_lds_wk<FMT, 1, 1, true>(a, U, g, st, so);
+    return launch_lds_fmt<FMT, true, false>(a, U, g, st, so, {});
+}
+
+hipError_t launch_quantize_q4k_swiglu(const GemvArgs& a, const SwigluOut& so, const ActIn& ai,
+                                      hipStream_t st) {
+    constexpr int FMT = QGEMV_FMT_Q4_K;
+    const int U = units_of(FMT, a.K);
+    const int Kp = (int)((a.K + 255) / 256 * 256);
+    const SliceGeom g = slice_geom<FMT>(a.K, U, lds_wk(U));
+    if (!lds_slice_fits<FMT>(g, act_lds_bytes(Kp))) return hipErrorInvalidValue;
+    return launch_lds_fmt<FMT, true, true>(a, U, g, st, so, ai);
 }
 
 hipError_t launch_gemv(int fmt, const GemvArgs& a, hipStream_t st) {
@@ -863,6 +997,16 @@ hipError_t launch_gemv(int fmt, const GemvArgs& a, hipStream_t st) {
     case QGEMV_FMT_Q6_K: return launch_gemv_fmt<QGEMV_FMT_Q6_K>(a, st);
     case QGEMV_FMT_Q6_K_R8: return launch_gemv_fmt<QGEMV_FMT_Q6_K_R8>(a, st);
     default: return launch_gemv_fmt<QGEMV_FMT_Q8_0>(a, st);
+    }
+}
+
+hipError_t launch_quantize_gemv(int fmt, const GemvArgs& a, const ActIn& ai, hipStream_t st) {
+    switch (fmt) {
+    case QGEMV_FMT_Q4_0: return launch_quantize_gemv_fmt<QGEMV_FMT_Q4_0>(a, ai, st);
+    case QGEMV_FMT_Q4_K: return launch_quantize_gemv_fmt<QGEMV_FMT_Q4_K>(a, ai, st);
+    case QGEMV_FMT_Q6_K: return launch_quantize_gemv_fmt<QGEMV_FMT_Q6_K>(a, ai, st);
+    case QGEMV_FMT_Q6_K_R8: return launch_quantize_gemv_fmt<QGEMV_FMT_Q6_K_R8>(a, ai, st);
+    default: return launch_quantize_gemv_fmt<QGEMV_FMT_Q8_0>(a, ai, st);
     }
 }
 

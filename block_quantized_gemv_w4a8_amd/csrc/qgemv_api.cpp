@@ -137,6 +137,40 @@ qgemv_status small_m_common(int fmt, const char* name, const void* w, int64_t N,
                     name);
 }
 
+// Gates shared by the two fused gate|up entries; x == NULL for the one whose
+// activation codes are given.
+qgemv_status swiglu_common(const char* name, const void* w, int64_t N, int64_t K,
+                           const float* x, const int8_t* q, const uint16_t* d, const int32_t* s,
+                           int8_t* q_out, uint16_t* d_out, int32_t* s_out, float* gu, float* h,
+                           qgemv_stream_t stream) {
+    if (N < 0) return fail(QGEMV_E_SHAPE, "%s: N = %lld is negative", name, (long long)N);
+    if (N == 0) return ok();
+    if (!w || !q || !d || !s || !q_out || !d_out || !s_out)
+        return fail(QGEMV_E_NULL, "%s: NULL pointer argument", name);
+    qgemv_status st = check_k(K);
+    if (st != QGEMV_OK) return st;
+    if (N % 32 != 0)
+        return fail(QGEMV_E_SHAPE, "%s: N = %lld must be a multiple of 32", name, (long long)N);
+    if (2 * N > INT32_MAX)
+        return fail(QGEMV_E_SHAPE, "%s: 2N = %lld exceeds 2^31-1", name, (long long)(2 * N));
+    if (K > QGEMV_K_MAX)
+        return fail(QGEMV_E_UNSUPPORTED, "%s: K = %lld exceeds QGEMV_K_MAX = %d", name,
+                    (long long)K, QGEMV_K_MAX);
+    if (!aligned(w, 16)) return fail(QGEMV_E_ALIGN, "%s: w must be 16-byte aligned", name);
+    if (x && !aligned(x, 16)) return fail(QGEMV_E_ALIGN, "%s: x must be 16-byte aligned", name);
+    if ((st = check_act_align(q, d, s)) != QGEMV_OK) return st;
+    if ((st = check_act_align(q_out, d_out, s_out)) != QGEMV_OK) return st;
+    if (gu && !aligned(gu, 4)) return fail(QGEMV_E_ALIGN, "%s: gu must be 4-byte aligned", name);
+    if (h && !aligned(h, 4)) return fail(QGEMV_E_ALIGN, "%s: h must be 4-byte aligned", name);
+    if ((st = check_device()) != QGEMV_OK) return st;
+    const qgemv::GemvArgs a{w, 2 * N, K, q, d, s, nullptr};
+    const qgemv::SwigluOut so{N, q_out, d_out, s_out, gu, h};
+    if (!x) return launched(qgemv::launch_q4k_swiglu(a, so, (hipStream_t)stream), name);
+    const qgemv::ActIn ai{x, const_cast<int8_t*>(q), const_cast<uint16_t*>(d),
+                          const_cast<int32_t*>(s)};
+    return launched(qgemv::launch_quantize_q4k_swiglu(a, so, ai, (hipStream_t)stream), name);
+}
+
 }  // namespace
 
 extern "C" {
@@ -160,7 +194,7 @@ const char* qgemv_build_info(void) {
     return "libqgemv abi=1 arch=gfx950 formats=q4_0,q4_k,q6_k,q8_0,q6_k_r8(repacked) act=int8/32+fp16+int32sum "
            "gemv=v_dot4_i32_i8,lds-row-stream,lanes-per-row{4,8,16,32,64} "
            "small_m=q4_k{dot4,mfma_i8_16x16x32},q6_k/q4_0{gemv_rows,mfma_i8_16x16x32} "
-           "fused=q4_k_swiglu_quantize K_max=32768 M_max=64";
+           "fused=q4_k_swiglu_quantize,quantize_gemv,quantize_q4_k_swiglu K_max=32768 M_max=64";
 }
 
 const char* qgemv_last_error(void) { return g_last_error; }
@@ -210,6 +244,32 @@ qgemv_status qgemv_q8_0(const void* w, int64_t N, int64_t K, const int8_t* q, co
 qgemv_status qgemv_q6_k_r8(const void* w_r, int64_t N, int64_t K, const int8_t* q,
                            const uint16_t* d, const int32_t* s, float* y, qgemv_stream_t stream) {
     return gemv_common(QGEMV_FMT_Q6_K_R8, w_r, N, K, q, d, s, y, stream);
+}
+
+qgemv_status qgemv_quantize_gemv(int fmt, const void* w, int64_t N, int64_t K, const float* x,
+                                 int8_t* q, uint16_t* d, int32_t* s, float* y,
+                                 qgemv_stream_t stream) {
+    const char* name = "qgemv_quantize_gemv";
+    if (N < 0) return fail(QGEMV_E_SHAPE, "%s: N = %lld is negative", name, (long long)N);
+    if (N == 0) return ok();
+    if (!w || !x || !q || !d || !s || !y)
+        return fail(QGEMV_E_NULL, "%s: NULL pointer argument", name);
+    qgemv_status st = check_k(K);
+    if (st != QGEMV_OK) return st;
+    if (N > INT32_MAX) return fail(QGEMV_E_SHAPE, "%s: N = %lld exceeds 2^31-1", name, (long long)N);
+    if (fmt < QGEMV_FMT_Q4_0 || fmt > QGEMV_FMT_Q6_K_R8)
+        return fail(QGEMV_E_UNSUPPORTED, "%s: unknown format %d", name, fmt);
+    if (K > QGEMV_K_MAX)
+        return fail(QGEMV_E_UNSUPPORTED, "%s: K = %lld exceeds QGEMV_K_MAX = %d", name,
+                    (long long)K, QGEMV_K_MAX);
+    if (!aligned(w, 16)) return fail(QGEMV_E_ALIGN, "%s: w must be 16-byte aligned", name);
+    if (!aligned(x, 16)) return fail(QGEMV_E_ALIGN, "%s: x must be 16-byte aligned", name);
+    if ((st = check_act_align(q, d, s)) != QGEMV_OK) return st;
+    if (!aligned(y, 4)) return fail(QGEMV_E_ALIGN, "%s: y must be 4-byte aligned", name);
+    if ((st = check_device()) != QGEMV_OK) return st;
+    const qgemv::GemvArgs a{w, N, K, q, d, s, y};
+    const qgemv::ActIn ai{x, q, d, s};
+    return launched(qgemv::launch_quantize_gemv(fmt, a, ai, (hipStream_t)stream), name);
 }
 
 qgemv_status qgemv_q6_k_repack(const void* w, int64_t N, int64_t K, void* w_r,
@@ -272,29 +332,17 @@ qgemv_status qgemv_q4_k_swiglu_quantize(const void* w, int64_t N, int64_t K, con
                                         const uint16_t* d, const int32_t* s, int8_t* q_out,
                                         uint16_t* d_out, int32_t* s_out, float* gu, float* h,
                                         qgemv_stream_t stream) {
-    const char* name = "qgemv_q4_k_swiglu_quantize";
-    if (N < 0) return fail(QGEMV_E_SHAPE, "%s: N = %lld is negative", name, (long long)N);
-    if (N == 0) return ok();
-    if (!w || !q || !d || !s || !q_out || !d_out || !s_out)
-        return fail(QGEMV_E_NULL, "%s: NULL pointer argument", name);
-    qgemv_status st = check_k(K);
-    if (st != QGEMV_OK) return st;
-    if (N % 32 != 0)
-        return fail(QGEMV_E_SHAPE, "%s: N = %lld must be a multiple of 32", name, (long long)N);
-    if (2 * N > INT32_MAX)
-        return fail(QGEMV_E_SHAPE, "%s: 2N = %lld exceeds 2^31-1", name, (long long)(2 * N));
-    if (K > QGEMV_K_MAX)
-        return fail(QGEMV_E_UNSUPPORTED, "%s: K = %lld exceeds QGEMV_K_MAX = %d", name,
-                    (long long)K, QGEMV_K_MAX);
-    if (!aligned(w, 16)) return fail(QGEMV_E_ALIGN, "%s: w must be 16-byte aligned", name);
-    if ((st = check_act_align(q, d, s)) != QGEMV_OK) return st;
-    if ((st = check_act_align(q_out, d_out, s_out)) != QGEMV_OK) return st;
-    if (gu && !aligned(gu, 4)) return fail(QGEMV_E_ALIGN, "%s: gu must be 4-byte aligned", name);
-    if (h && !aligned(h, 4)) return fail(QGEMV_E_ALIGN, "%s: h must be 4-byte aligned", name);
-    if ((st = check_device()) != QGEMV_OK) return st;
-    const qgemv::GemvArgs a{w, 2 * N, K, q, d, s, nullptr};
-    const qgemv::SwigluOut so{N, q_out, d_out, s_out, gu, h};
-    return launched(qgemv::launch_q4k_swiglu(a, so, (hipStream_t)stream), name);
+    return swiglu_common("qgemv_q4_k_swiglu_quantize", w, N, K, nullptr, q, d, s, q_out, d_out,
+                         s_out, gu, h, stream);
+}
+
+qgemv_status qgemv_quantize_q4_k_swiglu(const void* w, int64_t N, int64_t K, const float* x,
+                                        int8_t* q, uint16_t* d, int32_t* s, int8_t* q_out,
+                                        uint16_t* d_out, int32_t* s_out, float* gu, float* h,
+                                        qgemv_stream_t stream) {
+    const char* name = "qgemv_quantize_q4_k_swiglu";
+    if (N > 0 && !x) return fail(QGEMV_E_NULL, "%s: NULL pointer argument", name);
+    return swiglu_common(name, w, N, K, x, q, d, s, q_out, d_out, s_out, gu, h, stream);
 }
 
 qgemv_status qgemv_block_dots(int fmt, const void* w, int64_t N, int64_t K, int64_t row0,

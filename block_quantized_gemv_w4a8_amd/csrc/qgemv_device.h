@@ -25,6 +25,7 @@ namespace qgemv {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // Loads of packed weight bytes.  The vector types carry 2-byte alignment so
 // that one dwordx4 / dwordx2 load is emitted even where the address is only

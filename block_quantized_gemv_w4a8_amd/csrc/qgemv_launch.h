@@ -31,9 +31,26 @@ struct SwigluOut {
     float* h;
 };
 
+// An fp32 activation row x [K] (16-byte aligned) quantised inside the
+// product's own launch: every workgroup forms the codes of x in its LDS and
+// workgroup 0 also writes them to q [Kp], d [Kp/32], s [Kp/32], exactly as
+// launch_quantize_act would.
+struct ActIn {
+    const float* x;
+    int8_t* q;
+    uint16_t* d;
+    int32_t* s;
+};
+
 hipError_t launch_gemv(int fmt, const GemvArgs& a, hipStream_t st);
+// launch_quantize_act on ai then launch_gemv on its codes, in one launch
+// where the rows take the LDS-streaming kernel (else in those two launches)
+hipError_t launch_quantize_gemv(int fmt, const GemvArgs& a, const ActIn& ai, hipStream_t st);
 hipError_t launch_q6k_repack(const void* w, int64_t N, int64_t K, void* wr, hipStream_t st);
 hipError_t launch_q4k_swiglu(const GemvArgs& a, const SwigluOut& so, hipStream_t st);
+// the same with the gate|up activation quantised from ai.x in the launch
+hipError_t launch_quantize_q4k_swiglu(const GemvArgs& a, const SwigluOut& so, const ActIn& ai,
+                                      hipStream_t st);
 hipError_t launch_block_dots(int fmt, const void* w, int64_t K, int64_t row0, int64_t nrows,
                              const int8_t* q, int32_t* dots, hipStream_t st);
 hipError_t launch_quantize_act(const float* x, int64_t M, int64_t K, int64_t ldx, int8_t* q,

@@ -195,6 +195,22 @@ qgemv_status qgemv_q4_k_swiglu_quantize(const void* w, int64_t N, int64_t K,
                                         uint16_t* d_out, int32_t* s_out, float* gu,
                                         float* h, qgemv_stream_t stream);
 
+/* The gate|up product above with its own activation quantisation in the same
+ * launch: equal, bit for bit, to qgemv_quantize_act(x, M = 1, K) into q, d,
+ * s followed by qgemv_q4_k_swiglu_quantize on those codes ("Running an LLM
+ * on VKNN", Performance: every launch besides the matmuls is overhead; the
+ * quantisation is the once-per-matmul step of "Backends and hardware",
+ * section "CPU").  x: fp32 [K], 16-byte aligned.  q [Kp], d [Kp/32],
+ * s [Kp/32] receive the codes of x (written by the kernel; nothing in the
+ * launch reads them back).  Every workgroup quantises x into its own LDS
+ * while its first weight rows load.  Other arguments, limits and errors as
+ * for qgemv_q4_k_swiglu_quantize; x must not overlap any output. */
+qgemv_status qgemv_quantize_q4_k_swiglu(const void* w, int64_t N, int64_t K,
+                                        const float* x, int8_t* q, uint16_t* d,
+                                        int32_t* s, int8_t* q_out, uint16_t* d_out,
+                                        int32_t* s_out, float* gu, float* h,
+                                        qgemv_stream_t stream);
+
 /* Load-time repack of Q6_K weights for this device ("Backends and hardware",
  * section "Repacking is a per-device decision now": a layout is chosen per
  * device at load, the on-disk format stays the default).  Q6_K super-blocks
@@ -214,6 +230,22 @@ qgemv_status qgemv_q6_k_repack(const void* w, int64_t N, int64_t K, void* w_r,
 qgemv_status qgemv_q6_k_r8(const void* w_r, int64_t N, int64_t K, const int8_t* q,
                            const uint16_t* d, const int32_t* s, float* y,
                            qgemv_stream_t stream);
+
+/* Activation quantisation and one GEMV in a single launch: equal, bit for
+ * bit, to qgemv_quantize_act(x, M = 1, K) into q, d, s followed by the GEMV
+ * of format fmt (QGEMV_FMT_Q4_0, _Q4_K, _Q6_K, _Q8_0 or _Q6_K_R8 for weights
+ * from qgemv_q6_k_repack) on those codes ("Running an LLM on VKNN",
+ * Performance: every launch besides the matmuls is overhead; "Backends and
+ * hardware", section "CPU": the activation is quantised once per matmul).
+ * x: fp32 [K], 16-byte aligned; q [Kp], d [Kp/32], s [Kp/32] receive the
+ * codes of x; y: fp32 [N].  Rows of more than 32 units of 64 weights are
+ * served by one launch in which every workgroup quantises x into its own LDS
+ * while its first weight rows load; shorter rows take the two launches.
+ * Other arguments, limits and errors as for the format's GEMV; x must not
+ * overlap any output. */
+qgemv_status qgemv_quantize_gemv(int fmt, const void* w, int64_t N, int64_t K,
+                                 const float* x, int8_t* q, uint16_t* d, int32_t* s,
+                                 float* y, qgemv_stream_t stream);
 
 /* Validation: the int32 block dots of weight rows [row0, row0+nrows) against
  * one activation row q [Kp], computed by the same device code as the GEMV

@@ -132,6 +132,38 @@ def test_gates_null_shape_limits_align():
     assert "aligned" in qg.qgemv_last_error()
 
 
+def test_gates_quantize_fused_entries():
+    """qgemv_quantize_gemv and qgemv_quantize_q4_k_swiglu: NULL, shape, limit,
+    format and alignment gates (x must be 16-byte aligned), and empty calls."""
+    qg = _lib()
+    S = 0
+    QG = "qgemv_quantize_gemv"          # fmt, w, N, K, x, q, d, s, y, stream
+    for fmt in range(5):
+        assert _status(QG, fmt, A, 10, 256, None, A, A, A, A, S) == qg.QGEMV_E_NULL
+        assert _status(QG, fmt, A, 10, 256, A, A, A, A, None, S) == qg.QGEMV_E_NULL
+        assert _status(QG, fmt, A, 10, 48, A, A, A, A, A, S) == qg.QGEMV_E_SHAPE
+        assert _status(QG, fmt, A, 10, 65536, A, A, A, A, A, S) == qg.QGEMV_E_UNSUPPORTED
+        assert _status(QG, fmt, A, 10, 256, A + 4, A, A, A, A, S) == qg.QGEMV_E_ALIGN
+        assert _status(QG, fmt, A, 10, 256, A, A + 4, A, A, A, S) == qg.QGEMV_E_ALIGN
+        assert _status(QG, fmt, A, 10, 256, A, A, A, A, A + 2, S) == qg.QGEMV_E_ALIGN
+        assert _status(QG, fmt, None, 0, 256, None, None, None, None, None, S) == qg.QGEMV_OK
+    assert _status(QG, 5, A, 10, 256, A, A, A, A, A, S) == qg.QGEMV_E_UNSUPPORTED
+    assert _status(QG, -1, A, 10, 256, A, A, A, A, A, S) == qg.QGEMV_E_UNSUPPORTED
+    assert _status(QG, 1, A, -1, 256, A, A, A, A, A, S) == qg.QGEMV_E_SHAPE
+    XS = "qgemv_quantize_q4_k_swiglu"   # w, N, K, x, q, d, s, q_out, d_out, s_out, gu, h, stream
+    assert _status(XS, A, 64, 256, None, A, A, A, A, A, A, None, None, S) == qg.QGEMV_E_NULL
+    assert _status(XS, A, 64, 256, A, None, A, A, A, A, A, None, None, S) == qg.QGEMV_E_NULL
+    assert _status(XS, A, 64, 256, A, A, A, A, None, A, A, None, None, S) == qg.QGEMV_E_NULL
+    assert _status(XS, A, 48, 256, A, A, A, A, A, A, A, None, None, S) == qg.QGEMV_E_SHAPE
+    assert _status(XS, A, 64, 48, A, A, A, A, A, A, A, None, None, S) == qg.QGEMV_E_SHAPE
+    assert _status(XS, A, 64, 65536, A, A, A, A, A, A, A, None, None, S) == qg.QGEMV_E_UNSUPPORTED
+    assert _status(XS, A, 64, 256, A + 8, A, A, A, A, A, A, None, None, S) == qg.QGEMV_E_ALIGN
+    assert _status(XS, A, 64, 256, A, A + 4, A, A, A, A, A, None, None, S) == qg.QGEMV_E_ALIGN
+    assert _status(XS, A, 64, 256, A, A, A, A, A, A, A, A + 2, None, S) == qg.QGEMV_E_ALIGN
+    assert _status(XS, None, 0, 256, None, None, None, None, None, None, None, None, None,
+                   S) == qg.QGEMV_OK
+
+
 def test_gate_order_null_before_shape_before_align():
     qg = _lib()
     # a NULL pointer wins over a bad K and a misaligned pointer

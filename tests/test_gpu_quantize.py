@@ -61,6 +61,31 @@ def test_quantize_special_blocks(qg):
     _cmp(qg, y, None, "tiny and large")
 
 
+@pytest.mark.parametrize("seed", [0, 1])
+def test_quantize_dense_near_ties(qg, seed):
+    """Every value within 1..40 ulp of a rounding boundary (k + 1/2) d of its
+    block, over scales from 1e-30 to 1e30: the codes must still be those of the
+    correctly rounded quotient."""
+    g = np.random.default_rng(100 + seed)
+    M, K = 16, 4096
+    nb = K // 32
+    amax = (10.0 ** g.uniform(-30, 30, size=(M, nb, 1))).astype(np.float32)
+    d32 = (amax / np.float32(127)).astype(np.float32)
+    k = g.integers(-127, 127, size=(M, nb, 31)).astype(np.float32)
+    xv = ((k + np.float32(0.5)) * d32).astype(np.float32)
+    steps = g.integers(-40, 41, size=xv.shape)
+    for s in range(40):
+        move = np.abs(steps) > s
+        xv = np.where(move, np.nextafter(xv, np.where(steps > 0, np.float32(np.inf),
+                                                      np.float32(-np.inf))), xv)
+    xv = np.clip(xv, -amax, amax).astype(np.float32)
+    x = np.concatenate([amax * np.where(g.integers(0, 2, (M, nb, 1)) == 0, 1, -1), xv],
+                       axis=2).astype(np.float32)
+    perm = g.permuted(np.tile(np.arange(32), (M, nb, 1)), axis=2)
+    x = np.take_along_axis(x, perm, axis=2).reshape(M, K)
+    _cmp(qg, x, None, f"dense near-ties seed {seed}")
+
+
 def test_quantize_padding_and_empty(qg):
     import torch
     x = np.ones((2, 96), np.float32)
