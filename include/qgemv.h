@@ -75,7 +75,8 @@ typedef enum {
     QGEMV_E_NULL = 1,        /* a required pointer is NULL */
     QGEMV_E_SHAPE = 2,       /* negative size, K not a positive multiple of 32, ldx < K, ... */
     QGEMV_E_UNSUPPORTED = 3, /* valid but declined by this build (K > QGEMV_K_MAX, M > QGEMV_M_MAX, bad enum) */
-    QGEMV_E_ALIGN = 4,       /* w, q not 16-byte aligned; d 2-byte; x, s, y, h, gu, dots 4-byte */
+    QGEMV_E_ALIGN = 4,       /* w, q not 16-byte aligned; d 2-byte; x, s, y, h, gu, dots 4-byte
+                                (x 16-byte for the products that quantise it) */
     QGEMV_E_DEVICE = 5,      /* no current HIP device, or it is not gfx950 */
     QGEMV_E_LAUNCH = 6       /* the kernel launch itself failed */
 } qgemv_status;
