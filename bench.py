@@ -377,6 +377,33 @@ def graph_time(torch, calls, reps=20):
     return g, a.elapsed_time(b) * 1e3 / reps
 
 
+def graph_config0_fused(qg, torch, np, dev, c0, copies):
+    """Config 0 with the activation quantised in each GEMV's own launch
+    (qgemv_quantize_gemv), one graph of `copies` launches; a replay's output
+    must equal the eager call's bit for bit."""
+    ws = [torch.from_numpy(c0["w"]).to(dev)]
+    for _ in range(copies - 1):
+        ws.append(ws[0].clone())
+    x = torch.from_numpy(c0["x"]).to(dev)
+    q, d, s = qg.act_buffers(1, 896, dev)
+    ys = torch.empty((copies, 896), dtype=torch.float32, device=dev)
+    F = qg.QGEMV_FMT_Q4_0
+    calls = [lambda c=c: qg.qgemv_quantize_gemv(F, ws[c], 896, 896, x, q, d, s, ys[c])
+             for c in range(copies)]
+    eager = torch.empty(896, dtype=torch.float32, device=dev)
+    qg.qgemv_quantize_gemv(F, ws[0], 896, 896, x, q, d, s, eager)
+    g, us = graph_time(torch, calls)
+    ys.fill_(float("nan"))
+    g.replay()
+    torch.cuda.synchronize()
+    same = bool(torch.equal(ys[0].view(torch.int32), eager.view(torch.int32)) and
+                torch.equal(ys[-1].view(torch.int32), eager.view(torch.int32)))
+    per = us / copies
+    del ws, g
+    return {"us_per_quantize_gemv": round(per, 3), "weight_GBps": round(451584 / per / 1e3, 1),
+            "calls_per_s": round(1e6 / per), "replay_equals_eager": same}
+
+
 def graph_config0(qg, torch, np, dev, c0, copies):
     """Config 0 (Q4_0 896x896) as one graph of `copies` GEMVs over rotated
     weight copies; a replay's output must equal the eager call's bit for bit."""
@@ -401,9 +428,10 @@ def graph_config0(qg, torch, np, dev, c0, copies):
             "calls_per_s": round(1e6 / per), "replay_equals_eager": same}
 
 
-def graph_config1(qg, torch, np, dev, c1, layers):
-    """One config-1 layer (3 activation quantisations + 7 Q4_K GEMVs) per
-    rotated weight copy, `layers` layers in one graph."""
+def graph_config1(qg, torch, np, dev, c1, layers, fused=False):
+    """One config-1 layer (3 activation quantisations + 7 Q4_K GEMVs, or with
+    `fused` 7 GEMVs that quantise their own input) per rotated weight copy,
+    `layers` layers in one graph."""
     mats = c1["mats"]
     wl = {n: [torch.from_numpy(m["w"]).to(dev)] for n, m in mats.items()}
     for n in wl:
@@ -418,6 +446,13 @@ def graph_config1(qg, torch, np, dev, c1, layers):
     ys = {n: torch.empty(m["N"], dtype=torch.float32, device=dev) for n, m in mats.items()}
 
     def layer(c):
+        if fused:
+            calls = []
+            for n, m in mats.items():
+                x, _, a = xs[m["x"].tobytes()]
+                calls.append(lambda n=n, m=m, x=x, a=a: qg.qgemv_quantize_gemv(
+                    qg.QGEMV_FMT_Q4_K, wl[n][c], m["N"], m["K"], x, *a, ys[n]))
+            return calls
         calls = [lambda x=x, K=K, a=a: qg.qgemv_quantize_act(x, 1, K, K, *a)
                  for x, K, a in xs.values()]
         for n, m in mats.items():
@@ -530,6 +565,8 @@ def extras(qg, torch, np, synth, dev, R, c2, c3, args):
     c0 = synth.config0()
     ex["config0_q4_0_896x896"] = gemv_case("q4_0", c0["w"], 896, 896, c0["x"], 1200)
     ex["config0_q4_0_896x896"]["graph"] = graph_config0(qg, torch, np, dev, c0, 1200)
+    ex["config0_q4_0_896x896"]["graph_quantize_in_launch"] = graph_config0_fused(
+        qg, torch, np, dev, c0, 1200)
     c1 = synth.config1()
     layer_us = 0.0
     per = {}
@@ -539,7 +576,9 @@ def extras(qg, torch, np, synth, dev, R, c2, c3, args):
         layer_us += r["us"]
     ex["config1_q4_k_layer"] = {"per_matrix_us": per, "sum_us": round(layer_us, 2),
                                 "weight_GBps": round(8386560 / layer_us / 1e3, 1),
-                                "graph": graph_config1(qg, torch, np, dev, c1, 64)}
+                                "graph": graph_config1(qg, torch, np, dev, c1, 64),
+                                "graph_quantize_in_launch": graph_config1(qg, torch, np, dev, c1, 64,
+                                                                          fused=True)}
 
     # config 4: small-M Q4_K 14336 x 4096
     c4 = synth.config4()

@@ -129,6 +129,63 @@ struct ActReg<QGEMV_FMT_Q8_0> {
     }
 };
 
+// An fp32 activation row quantised by the whole workgroup into LDS: codes
+// aq [Kp], fp16 scale bits ad [Kp/32] and code sums as [Kp/32], blocks past K
+// zero.  The block quantiser is the one of k_quantize_act with 2 lanes per
+// block of 32 (16 consecutive values each) instead of 8: max and sum are
+// exact, so the bits are the same, and the per-block work (max, scale, sum)
+// is shared by 16 values per lane.  One pass covers 128 blocks; each load's
+// address is clamped into x and half-blocks past K are masked to zero.  The
+// first pass's loads are issued by the caller (xq_load) ahead of its weight
+// loads.
+constexpr int XQ_BATCH = WG / 2;   // blocks per pass
+
+__device__ __forceinline__ void xq_load(const float* __restrict__ x, int K, int b0,
+                                        f32x4 (&v)[4]) {
+    const int e = 32 * (b0 + (threadIdx.x >> 1)) + 16 * (threadIdx.x & 1);
+#pragma unroll
+    for (int k = 0; k < 4; k++) v[k] = *reinterpret_cast<const f32x4*>(x + min(e + 4 * k, K - 4));
+}
+
+__device__ __forceinline__ void xq_batch(const f32x4 (&v)[4], int K, int nb, int b0, int8_t* aq,
+                                         uint16_t* ad, int32_t* as) {
+    const int b = b0 + (threadIdx.x >> 1), half = threadIdx.x & 1;
+    const int e = 32 * b + 16 * half;
+    const bool in = e < K;
+    float vv[16];
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+        vv[4 * k] = in ? v[k].x : 0.0f;
+        vv[4 * k + 1] = in ? v[k].y : 0.0f;
+        vv[4 * k + 2] = in ? v[k].z : 0.0f;
+        vv[4 * k + 3] = in ? v[k].w : 0.0f;
+    }
+    const QBlockL<2> r = quantize_block<2>(vv);
+    if (b < nb) {
+        *reinterpret_cast<u32x4*>(aq + e) = u32x4{r.packed[0], r.packed[1], r.packed[2], r.packed[3]};
+        if (half == 0) {
+            ad[b] = (uint16_t)r.dbits;
+            as[b] = r.sum;
+        }
+    }
+}
+
+__device__ __forceinline__ void quantize_row_lds(const float* __restrict__ x, int K, int Kp,
+                                                 const f32x4 (&first)[4], int8_t* aq,
+                                                 uint16_t* ad, int32_t* as) {
+    const int nb = Kp / 32;
+    xq_batch(first, K, nb, 0, aq, ad, as);
+    for (int b0 = XQ_BATCH; b0 < nb; b0 += XQ_BATCH) {
+        f32x4 v[4];
+        xq_load(x, K, b0, v);
+        xq_batch(v, K, nb, b0, aq, ad, as);
+    }
+}
+
+// Bytes of LDS an in-kernel quantised activation row takes (codes, fp16
+// scales, int32 sums).
+__host__ __device__ inline int act_lds_bytes(int Kp) { return Kp + Kp / 16 + Kp / 8; }
+
 template <int FMT>
 struct Unit;
 template <>
@@ -214,13 +271,17 @@ constexpr int SEGP = 64;  // passes whose split-K partial sums are buffered in L
 // visits, so its activation lives in registers for the whole kernel.  Two row
 // buffers are used in turn: the next row's loads are in flight while the
 // current row is computed.
-template <int FMT, int LPR, int UPL, int WK>
+// Rows of this kernel that quantise their own activation (XQ) are at most
+// this long (the LDS-streaming kernel takes longer ones).
+constexpr int kXqShortKp = 2048;
+
+template <int FMT, int LPR, int UPL, int WK, bool XQ>
 __global__ __launch_bounds__(WG) void k_gemv(const uint8_t* __restrict__ w, int N, int U,
                                               int nbw, int row_bytes,
                                               const int8_t* __restrict__ q,
                                               const uint16_t* __restrict__ d,
                                               const int32_t* __restrict__ s,
-                                              float* __restrict__ y) {
+                                              float* __restrict__ y, const ActIn ai) {
     static_assert(WK == 1 || LPR == 64, "split-K needs whole waves per row");
     constexpr int RPW = 64 / LPR;
     constexpr int NRG = 4 / WK;
@@ -246,8 +307,15 @@ __global__ __launch_bounds__(WG) void k_gemv(const uint8_t* __restrict__ w, int 
         const int u = u_lo + li + LPR * i;
         ok[i] = u < u_hi;
         uu[i] = ok[i] ? u : u_hi - 1;
-        A[i].load(q, d, s, uu[i]);
+        if constexpr (!XQ) A[i].load(q, d, s, uu[i]);
     }
+    // XQ: the activation row quantised in this workgroup (codes, fp16
+    // scales, sums; Kp <= kXqShortKp)
+    __shared__ __align__(16) uint8_t xq_lds[XQ ? kXqShortKp + kXqShortKp / 16 + kXqShortKp / 8 : 16];
+    const int Kp = (32 * nbw + 255) / 256 * 256;
+    int8_t* const aq = reinterpret_cast<int8_t*>(xq_lds);
+    uint16_t* const ad = reinterpret_cast<uint16_t*>(xq_lds + Kp);
+    int32_t* const as = reinterpret_cast<int32_t*>(xq_lds + Kp + Kp / 16);
 
     const int my_off = rg * RPW + sub;  // this lane's row within a group
     const int64_t G = gridDim.x;
@@ -286,6 +354,26 @@ __global__ __launch_bounds__(WG) void k_gemv(const uint8_t* __restrict__ w, int 
         const int np = (int)min((int64_t)SEGP, npass_all - p0);
         WT wa[UPL], wb[UPL];
         load_row(wa, row_of(p0));
+        if constexpr (XQ) {
+            if (p0 == 0) {
+                // the first row's weights are on their way; quantise x
+                f32x4 xv[4];
+                xq_load(ai.x, 32 * nbw, 0, xv);
+                quantize_row_lds(ai.x, 32 * nbw, Kp, xv, aq, ad, as);
+                __syncthreads();
+#pragma unroll
+                for (int i = 0; i < UPL; i++) A[i].load(aq, ad, as, uu[i]);
+                if (blockIdx.x == 0) {
+                    for (int t = threadIdx.x; t < Kp / 16; t += WG)
+                        *reinterpret_cast<u32x4*>(ai.q + 16 * t) =
+                            *reinterpret_cast<const u32x4*>(aq + 16 * t);
+                    for (int t = threadIdx.x; t < Kp / 32; t += WG) {
+                        ai.d[t] = ad[t];
+                        ai.s[t] = as[t];
+                    }
+                }
+            }
+        }
         // (sched_barrier keeps the compiler from sinking a row's loads below
         // the wait for the previous row.)
         for (int p = 0; p < np; p += 2) {
@@ -392,63 +480,6 @@ struct UnitLds<QGEMV_FMT_Q8_0> {
 };
 
 // Byte offset of unit u within a row, and the first block of unit u.
-// An fp32 activation row quantised by the whole workgroup into LDS: codes
-// aq [Kp], fp16 scale bits ad [Kp/32] and code sums as [Kp/32], blocks past K
-// zero.  The block quantiser is the one of k_quantize_act with 2 lanes per
-// block of 32 (16 consecutive values each) instead of 8: max and sum are
-// exact, so the bits are the same, and the per-block work (max, scale, sum)
-// is shared by 16 values per lane.  One pass covers 128 blocks; each load's
-// address is clamped into x and half-blocks past K are masked to zero.  The
-// first pass's loads are issued by the caller (xq_load) ahead of its weight
-// loads.
-constexpr int XQ_BATCH = WG / 2;   // blocks per pass
-
-__device__ __forceinline__ void xq_load(const float* __restrict__ x, int K, int b0,
-                                        f32x4 (&v)[4]) {
-    const int e = 32 * (b0 + (threadIdx.x >> 1)) + 16 * (threadIdx.x & 1);
-#pragma unroll
-    for (int k = 0; k < 4; k++) v[k] = *reinterpret_cast<const f32x4*>(x + min(e + 4 * k, K - 4));
-}
-
-__device__ __forceinline__ void xq_batch(const f32x4 (&v)[4], int K, int nb, int b0, int8_t* aq,
-                                         uint16_t* ad, int32_t* as) {
-    const int b = b0 + (threadIdx.x >> 1), half = threadIdx.x & 1;
-    const int e = 32 * b + 16 * half;
-    const bool in = e < K;
-    float vv[16];
-#pragma unroll
-    for (int k = 0; k < 4; k++) {
-        vv[4 * k] = in ? v[k].x : 0.0f;
-        vv[4 * k + 1] = in ? v[k].y : 0.0f;
-        vv[4 * k + 2] = in ? v[k].z : 0.0f;
-        vv[4 * k + 3] = in ? v[k].w : 0.0f;
-    }
-    const QBlockL<2> r = quantize_block<2>(vv);
-    if (b < nb) {
-        *reinterpret_cast<u32x4*>(aq + e) = u32x4{r.packed[0], r.packed[1], r.packed[2], r.packed[3]};
-        if (half == 0) {
-            ad[b] = (uint16_t)r.dbits;
-            as[b] = r.sum;
-        }
-    }
-}
-
-__device__ __forceinline__ void quantize_row_lds(const float* __restrict__ x, int K, int Kp,
-                                                 const f32x4 (&first)[4], int8_t* aq,
-                                                 uint16_t* ad, int32_t* as) {
-    const int nb = Kp / 32;
-    xq_batch(first, K, nb, 0, aq, ad, as);
-    for (int b0 = XQ_BATCH; b0 < nb; b0 += XQ_BATCH) {
-        f32x4 v[4];
-        xq_load(x, K, b0, v);
-        xq_batch(v, K, nb, b0, aq, ad, as);
-    }
-}
-
-// Bytes of LDS an in-kernel quantised activation row takes (codes, fp16
-// scales, int32 sums).
-__host__ __device__ inline int act_lds_bytes(int Kp) { return Kp + Kp / 16 + Kp / 8; }
-
 template <int FMT>
 __host__ __device__ inline int unit_byte(int u) {
     if (FMT == QGEMV_FMT_Q4_K) return (u / 4) * 144;
@@ -782,7 +813,7 @@ static int units_of(int fmt, int64_t K) {
 
 // Workgroups of one kernel instantiation that fit on the device at once
 // (occupancy x compute units), cached per device.
-template <int FMT, int LPR, int UPL, int WK>
+template <int FMT, int LPR, int UPL, int WK, bool XQ = false>
 static int resident_workgroups() {
     static std::atomic<int> cache[64];
     int dev = 0;
@@ -790,7 +821,7 @@ static int resident_workgroups() {
     int v = cache[dev].load(std::memory_order_relaxed);
     if (v > 0) return v;
     int per_cu = 0, cus = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_gemv<FMT, LPR, UPL, WK>, WG, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_gemv<FMT, LPR, UPL, WK, XQ>, WG, 0) !=
             hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         per_cu <= 0 || cus <= 0) {
@@ -802,18 +833,19 @@ static int resident_workgroups() {
     return v;
 }
 
-template <int FMT, int LPR, int UPL, int WK>
-static hipError_t launch_gemv_cfg(const GemvArgs& a, int U, hipStream_t st) {
+template <int FMT, int LPR, int UPL, int WK, bool XQ = false>
+static hipError_t launch_gemv_cfg(const GemvArgs& a, int U, hipStream_t st,
+                                  const ActIn& ai = ActIn{}) {
     constexpr int RPP = (4 / WK) * (64 / LPR);
     const int64_t ngroups = (a.N + RPP - 1) / RPP;
     // as many workgroups as fit at once, then evened out so that every
     // workgroup gets the same number of passes (to within one)
-    const int64_t resident = resident_workgroups<FMT, LPR, UPL, WK>();
+    const int64_t resident = resident_workgroups<FMT, LPR, UPL, WK, XQ>();
     const int64_t passes = (ngroups + resident - 1) / resident;
     const int64_t grid = (ngroups + passes - 1) / passes;
-    hipLaunchKernelGGL((k_gemv<FMT, LPR, UPL, WK>), dim3((unsigned)grid), dim3(WG), 0, st,
+    hipLaunchKernelGGL((k_gemv<FMT, LPR, UPL, WK, XQ>), dim3((unsigned)grid), dim3(WG), 0, st,
                        (const uint8_t*)a.w, (int)a.N, U, (int)(a.K / 32), row_bytes_of(FMT, a.K),
-                       a.q, a.d, a.s, a.y);
+                       a.q, a.d, a.s, a.y, ai);
     return hipGetLastError();
 }
 
@@ -959,6 +991,12 @@ static hipError_t launch_quantize_gemv_fmt(const GemvArgs& a, const ActIn& ai, h
         const SliceGeom g = slice_geom<FMT>(a.K, U, lds_wk(U));
         if (lds_slice_fits<FMT>(g, act_lds_bytes(Kp)))
             return launch_lds_fmt<FMT, false, true>(a, U, g, st, {}, ai);
+    } else if (U <= 32 && Kp <= kXqShortKp) {
+        // short rows: the lanes-per-row kernel, same mapping as the GEMV
+        if (U > 16) return launch_gemv_cfg<FMT, 32, 1, 1, true>(a, U, st, ai);
+        if (U > 8) return launch_gemv_cfg<FMT, 16, 1, 1, true>(a, U, st, ai);
+        if (U > 4) return launch_gemv_cfg<FMT, 8, 1, 1, true>(a, U, st, ai);
+        return launch_gemv_cfg<FMT, 4, 1, 1, true>(a, U, st, ai);
     }
     hipError_t e = launch_quantize_act(ai.x, 1, a.K, a.K, ai.q, ai.d, ai.s, st);
     if (e != hipSuccess) return e;

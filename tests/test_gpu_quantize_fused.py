@@ -203,3 +203,27 @@ def test_config2_chain_with_fused_quantisation(qg):
     qg.qgemv_q4_k_swiglu_quantize(wgu, Kd, Kgu, *act2, *out2, None, None)
     for a, b in zip(out, out2):
         assert same_bits(a, b)
+
+
+def test_config0_and_config1_quantize_gemv(qg):
+    """The launch-bound workloads: Q4_0 896x896 and every matrix of the
+    Qwen2.5-0.5B-shaped Q4_K layer (K = 896 rows take the lanes-per-row
+    kernel, down's K = 4864 the LDS-streaming one), each with its activation
+    quantised in the launch; equal to the two-call path bit for bit and to
+    the oracle within the tolerance."""
+    c0 = synth.config0()
+    cases = [("q4_0", c0["w"], 896, 896, c0["x"], "config0")]
+    for name, m in synth.config1()["mats"].items():
+        cases.append(("q4_k", m["w"], m["N"], m["K"], m["x"], f"config1 {name}"))
+    for fmt, w, N, K, x, what in cases:
+        say("quantize_gemv", what)
+        wd = dev(w)
+        xd = dev(np.ascontiguousarray(x.reshape(-1), dtype=np.float32))
+        act, y = fused_gemv(qg, fmt, wd, N, K, xd)
+        q, d, s = act_host(*act)
+        y_ref, T = oracle.gemv(fmt, w, N, K, q, d, s)
+        check_y(host(y), y_ref, T, f"quantize_gemv {what}")
+        act2, y2 = two_call_gemv(qg, fmt, wd, N, K, x)
+        for a, b in zip(act, act2):
+            assert same_bits(a, b), what
+        assert same_bits(y, y2), what
