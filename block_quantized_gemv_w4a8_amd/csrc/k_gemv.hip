@@ -138,8 +138,7 @@ struct ActReg<QGEMV_FMT_Q8_0> {
 // address is clamped into x and half-blocks past K are masked to zero.  The
 // first pass's loads are issued by the caller (xq_load) ahead of its weight
 // loads.
-constexpr int XQ_BATCH = WG / 2;   // blocks per pass
-
+template <int NTH = WG>
 __device__ __forceinline__ void xq_load(const float* __restrict__ x, int K, int b0,
                                         f32x4 (&v)[4]) {
     const int e = 32 * (b0 + (threadIdx.x >> 1)) + 16 * (threadIdx.x & 1);
@@ -147,6 +146,7 @@ __device__ __forceinline__ void xq_load(const float* __restrict__ x, int K, int 
     for (int k = 0; k < 4; k++) v[k] = *reinterpret_cast<const f32x4*>(x + min(e + 4 * k, K - 4));
 }
 
+template <int NTH = WG>
 __device__ __forceinline__ void xq_batch(const f32x4 (&v)[4], int K, int nb, int b0, int8_t* aq,
                                          uint16_t* ad, int32_t* as) {
     const int b = b0 + (threadIdx.x >> 1), half = threadIdx.x & 1;
@@ -170,15 +170,29 @@ __device__ __forceinline__ void xq_batch(const f32x4 (&v)[4], int K, int nb, int
     }
 }
 
+template <int NTH = WG>
 __device__ __forceinline__ void quantize_row_lds(const float* __restrict__ x, int K, int Kp,
                                                  const f32x4 (&first)[4], int8_t* aq,
                                                  uint16_t* ad, int32_t* as) {
     const int nb = Kp / 32;
-    xq_batch(first, K, nb, 0, aq, ad, as);
-    for (int b0 = XQ_BATCH; b0 < nb; b0 += XQ_BATCH) {
+    constexpr int BATCH = NTH / 2;   // blocks per pass
+    xq_batch<NTH>(first, K, nb, 0, aq, ad, as);
+    for (int b0 = BATCH; b0 < nb; b0 += BATCH) {
         f32x4 v[4];
-        xq_load(x, K, b0, v);
-        xq_batch(v, K, nb, b0, aq, ad, as);
+        xq_load<NTH>(x, K, b0, v);
+        xq_batch<NTH>(v, K, nb, b0, aq, ad, as);
+    }
+}
+
+// Workgroup 0 of a product that quantised x itself writes the codes out.
+template <int NTH = WG>
+__device__ __forceinline__ void xq_write_out(const ActIn& ai, int Kp, const int8_t* aq,
+                                             const uint16_t* ad, const int32_t* as) {
+    for (int t = threadIdx.x; t < Kp / 16; t += NTH)
+        *reinterpret_cast<u32x4*>(ai.q + 16 * t) = *reinterpret_cast<const u32x4*>(aq + 16 * t);
+    for (int t = threadIdx.x; t < Kp / 32; t += NTH) {
+        ai.d[t] = ad[t];
+        ai.s[t] = as[t];
     }
 }
 
@@ -721,6 +735,183 @@ __global__ __launch_bounds__(WG) void k_gemv_lds(const uint8_t* __restrict__ w, 
     }
 }
 
+// Dynamic-row LDS-streaming GEMV: one workgroup of DW = 8 waves per compute
+// unit, the same per-row work as k_gemv_lds, but the rows of a workgroup are
+// handed to its waves one at a time from a counter in LDS.  With two
+// 4-wave workgroups per compute unit and a fixed share each, the workgroup
+// dispatched first ran 16-36% faster than its co-resident twin (its waves
+// are older and win the issue arbitration), and the unit finished with the
+// slow one; pulling rows from a shared counter lets every wave of the unit
+// work until the unit's rows are done.  A workgroup owns the row groups of
+// DRG rows b, b + G, b + 2G, ...; with split-K (WK > 1) each of the WK
+// slices of a row has its own counter (the waves holding that slice's
+// activation pull from it) and the slices' partial sums meet in LDS, added
+// in slice order as in k_gemv_lds, so every output has the same bits.
+constexpr int DW = 8;           // waves of a dynamic-row workgroup
+constexpr int DWG = 64 * DW;    // its threads
+constexpr int DRG = 8;          // rows per row group of the static split
+
+template <int FMT, int UPL, int WK, int NL, bool XQ>
+__global__ __launch_bounds__(DWG) void k_gemv_dyn(const uint8_t* __restrict__ w, int N, int U,
+                                                   int US, int nbw, int row_bytes, int buf_bytes,
+                                                   const int8_t* __restrict__ q,
+                                                   const uint16_t* __restrict__ d,
+                                                   const int32_t* __restrict__ s,
+                                                   float* __restrict__ y, const ActIn ai) {
+    static_assert(DW % WK == 0, "whole waves per slice");
+    extern __shared__ __align__(16) uint8_t lds[];
+    __shared__ int cnt[WK];
+    constexpr int LPR = 64;
+    using UnitT = Unit<FMT>;
+    using WT = typename UnitT::W;
+    using UL = UnitLds<FMT>;
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int kq = wave % WK;
+    const int u_lo = kq * US;
+    const int u_hi = min(U, u_lo + US);
+    const int sbeg = unit_byte<FMT>(u_lo);
+    const int slen = min(unit_byte<FMT>(u_hi), row_bytes) - sbeg;
+
+    // this workgroup's rows; indices past them (and rows past N) map to row
+    // N - 1, whose bytes the prefetch then reads from cache
+    const int G = gridDim.x, b = blockIdx.x;
+    const int ngr = (N + DRG - 1) / DRG;
+    const int pool_n = ngr > b ? (ngr - b + G - 1) / G * DRG : 0;
+    auto row_raw = [&](int i) { return DRG * (b + (i / DRG) * G) + i % DRG; };
+    auto row_of = [&](int i) { return i < pool_n ? min(row_raw(i), N - 1) : N - 1; };
+
+    if (threadIdx.x < WK) cnt[threadIdx.x] = 0;
+    ActReg<FMT> A[UPL];
+    int ul[UPL];
+    bool ok[UPL], has1[UPL];
+    auto load_act = [&](const int8_t* aq, const uint16_t* ad, const int32_t* as) {
+#pragma unroll
+        for (int i = 0; i < UPL; i++) {
+            const int u = u_lo + lane + LPR * i;
+            ok[i] = u < u_hi;
+            const int uc = ok[i] ? u : u_hi - 1;
+            A[i].load(aq, ad, as, uc);
+            ul[i] = uc - u_lo;
+            has1[i] = 2 * uc + 1 < nbw;
+        }
+    };
+    if constexpr (!XQ) load_act(q, d, s);
+    const int Kp = (32 * nbw + 255) / 256 * 256;
+    int8_t* const aq = reinterpret_cast<int8_t*>(lds + 2 * DW * buf_bytes);
+    uint16_t* const ad = reinterpret_cast<uint16_t*>(lds + 2 * DW * buf_bytes + Kp);
+    int32_t* const as = reinterpret_cast<int32_t*>(lds + 2 * DW * buf_bytes + Kp + Kp / 16);
+    float* const part =
+        reinterpret_cast<float*>(lds + 2 * DW * buf_bytes + (XQ ? act_lds_bytes(Kp) : 0));
+    uint8_t* buf0 = lds + (2 * wave) * buf_bytes;
+    uint8_t* buf1 = buf0 + buf_bytes;
+    __syncthreads();   // the counters are zero
+
+    // the next row index of this wave's slice: one LDS atomic per row,
+    // issued a step before its value is read (take) so that its latency
+    // stays off the path to the row's loads
+    auto grab_issue = [&]() {
+        int v = 0;
+        if (lane == 0) v = atomicAdd(&cnt[kq], 1);
+        return v;
+    };
+    auto take = [&](int v) { return __builtin_amdgcn_readfirstlane(v); };
+    auto grab = [&]() { return take(grab_issue()); };
+    auto chunk_off = [&](int k, int delta) { return min(16 * (lane + 64 * k), delta + slen - 16); };
+    auto stage = [&](u32x4 (&R)[NL], int row) {
+        const uint8_t* a = w + (int64_t)row * row_bytes + sbeg;
+        const int delta = (int)((uintptr_t)a & 15);
+        const uint8_t* ab = a - delta;
+#pragma unroll
+        for (int k = 0; k < NL; k++) R[k] = ld16_stream<true>(ab + chunk_off(k, delta));
+        return delta;
+    };
+    auto commit = [&](const u32x4 (&R)[NL], int delta, uint8_t* buf) {
+#pragma unroll
+        for (int k = 0; k < NL; k++) st16(buf + chunk_off(k, delta), R[k]);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
+    auto dot_row = [&](const uint8_t* buf, int delta) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int i = 0; i < UPL; i++) {
+            WT wv;
+            UL::load(buf, delta, ul[i], has1[i], wv);
+            const float t = UnitT::term(wv, A[i], u_lo + ul[i], nbw);
+            acc += ok[i] ? t : 0.0f;
+        }
+        return group_sum<LPR>(acc);
+    };
+    auto finish_row = [&](float acc, int i) {
+        if (lane == LPR - 1 && i < pool_n && row_raw(i) < N) {
+            if constexpr (WK == 1) y[row_raw(i)] = acc;
+            else part[i * WK + kq] = acc;
+        }
+    };
+
+    u32x4 Ra[NL], Rb[NL];
+    int ia, ib, i0, d0, d1, da, db;
+    {
+        // three rows requested before the first is committed (XQ: after the
+        // loads of x; the rows stream in while the workgroup quantises x)
+        f32x4 xv[4];
+        if (XQ) xq_load<DWG>(ai.x, 32 * nbw, 0, xv);
+        __builtin_amdgcn_sched_barrier(0);
+        u32x4 Rc[NL];
+        const int ic = grab();
+        const int dc = stage(Rc, row_of(ic));
+        __builtin_amdgcn_sched_barrier(0);
+        ia = grab();
+        da = stage(Ra, row_of(ia));
+        __builtin_amdgcn_sched_barrier(0);
+        ib = grab();
+        db = stage(Rb, row_of(ib));
+        __builtin_amdgcn_sched_barrier(0);
+        if (XQ) {
+            quantize_row_lds<DWG>(ai.x, 32 * nbw, Kp, xv, aq, ad, as);
+            __syncthreads();
+            load_act(aq, ad, as);
+            if (b == 0) xq_write_out<DWG>(ai, Kp, aq, ad, as);
+        }
+        commit(Rc, dc, buf0);
+        d0 = dc;
+        i0 = ic;
+    }
+    int tn = grab_issue();   // the index after ib, in flight
+    // a wave's indices increase, so once one is past the pool all later are
+    while (i0 < pool_n) {
+        finish_row(dot_row(buf0, d0), i0);
+        commit(Ra, da, buf1);
+        d1 = da;
+        const int i1 = ia;
+        ia = take(tn);
+        tn = grab_issue();
+        da = stage(Ra, row_of(ia));
+        __builtin_amdgcn_sched_barrier(0);
+        if (i1 < pool_n) finish_row(dot_row(buf1, d1), i1);
+        commit(Rb, db, buf0);
+        d0 = db;
+        i0 = ib;
+        ib = take(tn);
+        tn = grab_issue();
+        db = stage(Rb, row_of(ib));
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (WK > 1) {
+        __syncthreads();
+        for (int i = threadIdx.x; i < pool_n; i += DWG) {
+            if (row_raw(i) < N) {
+                float v = part[i * WK];
+#pragma unroll
+                for (int k = 1; k < WK; k++) v += part[i * WK + k];
+                y[row_raw(i)] = v;
+            }
+        }
+    }
+}
+
 // Block-dots validation kernel: one thread per (row, unit); the activation is
 // read from global memory, the weights with the same unit loaders and the
 // integer dots with the same unit dot functions as the GEMV kernels.
@@ -954,9 +1145,76 @@ static hipError_t launch_lds_wk(const GemvArgs& a, int U, const SliceGeom& g, hi
 // Split-K of the LDS-streaming kernel: waves per row.
 static int lds_wk(int U) { return U > 128 ? 4 : (U > 64 ? 2 : 1); }
 
+// Compute units of the current device (cached per device).
+static int cu_count() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+        (void)hipGetLastError();
+        return 256;
+    }
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        v <= 0) {
+        (void)hipGetLastError();
+        return 256;
+    }
+    cache[dev].store(v, std::memory_order_relaxed);
+    return v;
+}
+
+// The dynamic-row kernel: one workgroup per compute unit.  Returns
+// hipErrorNotSupported (nothing launched) where its slice buffers, the
+// activation row and the partial sums would not fit in 64 KB of LDS.
+template <int FMT, int UPL, int WK, int NL, bool XQ>
+static hipError_t launch_dyn_cfg(const GemvArgs& a, const ActIn& ai, int U, int US, int buf_bytes,
+                                 hipStream_t st) {
+    const int cus = cu_count();
+    const int64_t ngr = (a.N + DRG - 1) / DRG;
+    const int64_t grid = ngr < cus ? ngr : cus;
+    const int64_t pool_cap = (ngr + grid - 1) / grid * DRG;
+    const int Kp = (int)((a.K + 255) / 256 * 256);
+    const int64_t smem = 2 * DW * (int64_t)buf_bytes + (XQ ? act_lds_bytes(Kp) : 0) +
+                         (WK > 1 ? pool_cap * WK * 4 : 0);
+    if (smem > 65536 - 64) return hipErrorNotSupported;
+    hipLaunchKernelGGL((k_gemv_dyn<FMT, UPL, WK, NL, XQ>), dim3((unsigned)grid), dim3(DWG),
+                       (unsigned)smem, st, (const uint8_t*)a.w, (int)a.N, U, US, (int)(a.K / 32),
+                       row_bytes_of(FMT, a.K), buf_bytes, a.q, a.d, a.s, a.y, ai);
+    return hipGetLastError();
+}
+
+template <int FMT, int UPL, int WK, bool XQ>
+static hipError_t launch_dyn_wk(const GemvArgs& a, int U, const SliceGeom& g, hipStream_t st,
+                                const ActIn& ai) {
+    const int buf_bytes = 16 * g.nchunk + 16;
+    const int nl = (g.nchunk + 63) / 64;
+    if (nl <= 2) return launch_dyn_cfg<FMT, UPL, WK, 2, XQ>(a, ai, U, g.US, buf_bytes, st);
+    if (nl <= 3) return launch_dyn_cfg<FMT, UPL, WK, 3, XQ>(a, ai, U, g.US, buf_bytes, st);
+    if (nl <= 4) return launch_dyn_cfg<FMT, UPL, WK, 4, XQ>(a, ai, U, g.US, buf_bytes, st);
+    return hipErrorNotSupported;
+}
+
+// Matrices with at least this many rows per compute unit take the
+// dynamic-row kernel (where it fits).  Measured on MI355X: it ends the
+// 128256-row lm_head 2-3 us sooner (62.4 vs 64.8 us), but runs the
+// 28672 x 4096 gate|up product 1.2-1.4 us slower than two 4-wave workgroups
+// per unit with fixed shares, and the 4096-row down product no faster.
+constexpr int kDynRowsPerCu = 256;
+
 template <int FMT, bool SW, bool XQ>
 static hipError_t launch_lds_fmt(const GemvArgs& a, int U, const SliceGeom& g, hipStream_t st,
                                  const SwigluOut& so, const ActIn& ai) {
+    if constexpr (!SW) {
+        if (a.N >= (int64_t)kDynRowsPerCu * cu_count()) {
+            hipError_t e = hipErrorNotSupported;
+            if (U > 256) e = launch_dyn_wk<FMT, 2, 4, XQ>(a, U, g, st, ai);
+            else if (U > 128) e = launch_dyn_wk<FMT, 1, 4, XQ>(a, U, g, st, ai);
+            else if (U > 64) e = launch_dyn_wk<FMT, 1, 2, XQ>(a, U, g, st, ai);
+            else e = launch_dyn_wk<FMT, 1, 1, XQ>(a, U, g, st, ai);
+            if (e != hipErrorNotSupported) return e;
+        }
+    }
     if (U > 256) return launch_lds_wk<FMT, 2, 4, SW, XQ>(a, U, g, st, so, ai);
     if (U > 128) return launch_lds_wk<FMT, 1, 4, SW, XQ>(a, U, g, st, so, ai);
     if (U > 64) return launch_lds_wk<FMT, 1, 2, SW, XQ>(a, U, g, st, so, ai);

@@ -129,3 +129,42 @@ def test_config3_lm_head_q6_k(qg):
         dots = block_dots(qg, "q6_k", wd, N, K, act[0], r0, nr)
         ref = oracle.block_dots("q6_k", c["w"], N, K, q, rows=(r0, nr))
         assert np.array_equal(dots, ref)
+
+
+# Matrices with at least 256 rows per compute unit (65536 on MI355X) take the
+# dynamic-row kernel: one 8-wave workgroup per compute unit whose waves pull
+# rows from a counter in LDS.  Tall, ragged shapes (N not a multiple of its 8-row
+# groups) for every format and split-K width, checked on sampled rows (the
+# first and last 64 and a seeded spread) and, with the activation quantised
+# in the launch, against the two-call path bit for bit.
+DYN_SHAPES = [("q4_0", 2304), ("q4_k", 2304), ("q6_k", 2304), ("q8_0", 2304), ("q6_k_r8", 2304),
+              ("q4_k", 4864), ("q6_k", 4864), ("q4_k", 8448), ("q6_k_r8", 8448),
+              ("q4_0", 16640)]
+
+
+@pytest.mark.parametrize("fmt,K", DYN_SHAPES)
+def test_dynamic_row_kernel(qg, fmt, K):
+    N = 65600 + 3
+    g = np.random.default_rng(K + len(fmt))
+    base = "q6_k" if fmt == "q6_k_r8" else fmt
+    w = synth.weights(base, g, N, K)
+    x, _ = synth.activation(g, 1, K)
+    act = quantize(qg, x)
+    q, d, s = act_host(*act)
+    wd = dev(w)
+    if fmt == "q6_k_r8":
+        wr = torch.empty((N, qg.q6_k_r8_row_bytes(K)), dtype=torch.uint8, device="cuda:0")
+        qg.qgemv_q6_k_repack(wd, N, K, wr)
+        wd = wr
+    say("dynamic-row gemv", fmt, N, K)
+    y = gemv(qg, fmt, wd, N, K, act)
+    assert np.all(np.isfinite(y))
+    rows = sample_rows(N, 1500, seed=K)
+    y_ref, T = oracle_rows(base, w, N, K, q, d, s, rows)
+    check_y(y[rows], y_ref, T, f"dynamic-row {fmt} N={N} K={K}")
+    # the same product with x quantised in the launch
+    xd = dev(np.ascontiguousarray(x.reshape(-1), dtype=np.float32))
+    q2, d2, s2 = qg.act_buffers(1, K, "cuda:0")
+    y2 = torch.full((N,), float("nan"), device="cuda:0")
+    qg.qgemv_quantize_gemv(qg.FMT_ID[fmt], wd, N, K, xd, q2, d2, s2, y2)
+    assert np.array_equal(host(y2).view(np.uint32), y.view(np.uint32))
