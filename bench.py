@@ -336,18 +336,23 @@ def small_m_profile(qg, torch, np, synth, dev):
 
 
 def time_kernel(torch, fn, iters, R):
-    """Average microseconds of fn(i) over iters launches (events around the loop)."""
-    for i in range(3):
-        fn(i % R)
-    torch.cuda.synchronize()
-    a = torch.cuda.Event(enable_timing=True)
-    b = torch.cuda.Event(enable_timing=True)
-    a.record()
+    """Microseconds per launch of fn(i): the best of three windows of `iters`
+    back-to-back launches (events around each window), after `iters` warm-up
+    launches."""
     for i in range(iters):
         fn(i % R)
-    b.record()
     torch.cuda.synchronize()
-    return a.elapsed_time(b) * 1e3 / iters
+    best = float("inf")
+    for _ in range(3):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(iters):
+            fn(i % R)
+        b.record()
+        torch.cuda.synchronize()
+        best = min(best, a.elapsed_time(b) * 1e3 / iters)
+    return best
 
 
 def graph_time(torch, calls, reps=20):
