@@ -433,10 +433,12 @@ def graph_config0(qg, torch, np, dev, c0, copies):
             "calls_per_s": round(1e6 / per), "replay_equals_eager": same}
 
 
-def graph_config1(qg, torch, np, dev, c1, layers, fused=False):
-    """One config-1 layer (3 activation quantisations + 7 Q4_K GEMVs, or with
-    `fused` 7 GEMVs that quantise their own input) per rotated weight copy,
-    `layers` layers in one graph."""
+def graph_config1(qg, torch, np, dev, c1, layers, fused=False, grouped=False):
+    """One config-1 layer per rotated weight copy, `layers` layers in one
+    graph: 3 activation quantisations + 7 Q4_K GEMVs; with `fused`, 7 GEMVs
+    that quantise their own input; with `grouped`, 4 launches in the order a
+    decode layer's dependencies allow -- q|k|v, o, gate|up (qgemv_quantize_multi
+    where matrices share an input), down."""
     mats = c1["mats"]
     wl = {n: [torch.from_numpy(m["w"]).to(dev)] for n, m in mats.items()}
     for n in wl:
@@ -451,6 +453,15 @@ def graph_config1(qg, torch, np, dev, c1, layers, fused=False):
     ys = {n: torch.empty(m["N"], dtype=torch.float32, device=dev) for n, m in mats.items()}
 
     def layer(c):
+        if grouped:
+            calls = []
+            for names in (("q", "k", "v"), ("o",), ("gate", "up"), ("down",)):
+                m0 = mats[names[0]]
+                x, _, a = xs[m0["x"].tobytes()]
+                calls.append(lambda names=names, m0=m0, x=x, a=a: qg.qgemv_quantize_multi(
+                    qg.QGEMV_FMT_Q4_K, [wl[n][c] for n in names], [mats[n]["N"] for n in names],
+                    m0["K"], x, *a, [ys[n] for n in names]))
+            return calls
         if fused:
             calls = []
             for n, m in mats.items():
@@ -583,7 +594,9 @@ def extras(qg, torch, np, synth, dev, R, c2, c3, args):
                                 "weight_GBps": round(8386560 / layer_us / 1e3, 1),
                                 "graph": graph_config1(qg, torch, np, dev, c1, 64),
                                 "graph_quantize_in_launch": graph_config1(qg, torch, np, dev, c1, 64,
-                                                                          fused=True)}
+                                                                          fused=True),
+                                "graph_grouped_4_launches": graph_config1(qg, torch, np, dev, c1, 64,
+                                                                          grouped=True)}
 
     # config 4: small-M Q4_K 14336 x 4096
     c4 = synth.config4()

@@ -35,6 +35,7 @@ QGEMV_FMT_Q4_0, QGEMV_FMT_Q4_K, QGEMV_FMT_Q6_K, QGEMV_FMT_Q8_0 = 0, 1, 2, 3
 QGEMV_FMT_Q6_K_R8 = 4
 QGEMV_VARIANT_AUTO, QGEMV_VARIANT_DOT4, QGEMV_VARIANT_MFMA = 0, 1, 2
 QGEMV_K_MAX = 32768
+QGEMV_MULTI_MAX = 8
 QGEMV_M_MAX = 64
 
 # Every extern "C" symbol that include/qgemv.h declares.
@@ -44,7 +45,7 @@ EXPORTS = [
     "qgemv_q6_k_repack", "qgemv_q6_k_r8",
     "qgemm_q4_k_small_m", "qgemm_q6_k_small_m", "qgemm_q4_0_small_m",
     "qgemv_silu_mul_quantize", "qgemv_q4_k_swiglu_quantize",
-    "qgemv_quantize_gemv", "qgemv_quantize_q4_k_swiglu",
+    "qgemv_quantize_gemv", "qgemv_quantize_q4_k_swiglu", "qgemv_multi", "qgemv_quantize_multi",
     "qgemv_block_dots",
 ]
 
@@ -74,6 +75,10 @@ _lib.qgemv_quantize_q4_k_swiglu.argtypes = [_P, _I64, _I64, _P, _P, _P, _P, _P, 
                                             _P]
 _lib.qgemv_quantize_gemv.restype = _I
 _lib.qgemv_quantize_gemv.argtypes = [_I, _P, _I64, _I64, _P, _P, _P, _P, _P, _P]
+_lib.qgemv_multi.restype = _I
+_lib.qgemv_multi.argtypes = [_I, _I, _P, _P, _I64, _P, _P, _P, _P, _P]
+_lib.qgemv_quantize_multi.restype = _I
+_lib.qgemv_quantize_multi.argtypes = [_I, _I, _P, _P, _I64, _P, _P, _P, _P, _P, _P]
 _lib.qgemv_block_dots.restype = _I
 _lib.qgemv_block_dots.argtypes = [_I, _P, _I64, _I64, _I64, _I64, _P, _P, _P]
 
@@ -217,6 +222,30 @@ def qgemv_quantize_q4_k_swiglu(w, N, K, x, q, d, s, q_out, d_out, s_out, gu=None
 def qgemv_quantize_gemv(fmt, w, N, K, x, q, d, s, y, stream=None):
     return _check(_lib.qgemv_quantize_gemv(fmt, _ptr(w), N, K, _ptr(x), _ptr(q), _ptr(d), _ptr(s),
                                            _ptr(y), _stream(stream)), "qgemv_quantize_gemv")
+
+
+def _multi_arrays(ws, ns, ys):
+    if not (len(ws) == len(ns) == len(ys)):
+        raise ValueError("ws, ns and ys must have the same length")
+    c = len(ws)
+    wa = (ctypes.c_void_p * max(c, 1))(*[_ptr(t) for t in ws])
+    na = (ctypes.c_int64 * max(c, 1))(*[int(v) for v in ns])
+    ya = (ctypes.c_void_p * max(c, 1))(*[_ptr(t) for t in ys])
+    return c, wa, na, ya
+
+
+def qgemv_multi(fmt, ws, ns, K, q, d, s, ys, stream=None):
+    """Several GEMVs (lists ws, ns, ys of one length) on one activation."""
+    c, wa, na, ya = _multi_arrays(ws, ns, ys)
+    return _check(_lib.qgemv_multi(fmt, c, wa, na, K, _ptr(q), _ptr(d), _ptr(s), ya,
+                                   _stream(stream)), "qgemv_multi")
+
+
+def qgemv_quantize_multi(fmt, ws, ns, K, x, q, d, s, ys, stream=None):
+    c, wa, na, ya = _multi_arrays(ws, ns, ys)
+    return _check(_lib.qgemv_quantize_multi(fmt, c, wa, na, K, _ptr(x), _ptr(q), _ptr(d),
+                                            _ptr(s), ya, _stream(stream)),
+                  "qgemv_quantize_multi")
 
 
 def qgemv_block_dots(fmt, w, N, K, row0, nrows, q, dots, stream=None):

@@ -289,14 +289,50 @@ constexpr int SEGP = 64;  // passes whose split-K partial sums are buffered in L
 // this long (the LDS-streaming kernel takes longer ones).
 constexpr int kXqShortKp = 2048;
 
-template <int FMT, int LPR, int UPL, int WK, bool XQ>
+// MULTI: the rows are those of several matrices (mr), each with its own
+// weights and output; row r of the combined range is row r - start[m] of
+// matrix m (selected without indexing the argument arrays by lane).
+template <int FMT, int LPR, int UPL, int WK, bool XQ, bool MULTI>
 __global__ __launch_bounds__(WG) void k_gemv(const uint8_t* __restrict__ w, int N, int U,
                                               int nbw, int row_bytes,
                                               const int8_t* __restrict__ q,
                                               const uint16_t* __restrict__ d,
                                               const int32_t* __restrict__ s,
-                                              float* __restrict__ y, const ActIn ai) {
+                                              float* __restrict__ y, const ActIn ai,
+                                              const MultiRows mr) {
     static_assert(WK == 1 || LPR == 64, "split-K needs whole waves per row");
+    static_assert(!MULTI || WK == 1, "several matrices: whole rows per lane group");
+    // matrix m of combined row r, its row pointer and output
+    auto mat_of = [&](int64_t r) {
+        int m = 0;
+#pragma unroll
+        for (int k = 1; k < kMultiMax; k++) m += (k < mr.count && r >= mr.start[k]) ? 1 : 0;
+        return m;
+    };
+    auto row_ptr = [&](int64_t r) -> const uint8_t* {
+        if constexpr (!MULTI) return w + r * (int64_t)row_bytes;
+        const int m = mat_of(r);
+        const uint8_t* base = static_cast<const uint8_t*>(mr.w[0]);
+        int start = mr.start[0];
+#pragma unroll
+        for (int k = 1; k < kMultiMax; k++) {
+            base = m == k ? static_cast<const uint8_t*>(mr.w[k]) : base;
+            start = m == k ? mr.start[k] : start;
+        }
+        return base + (r - start) * (int64_t)row_bytes;
+    };
+    auto out_ptr = [&](int64_t r) -> float* {
+        if constexpr (!MULTI) return y + r;
+        const int m = mat_of(r);
+        float* base = mr.y[0];
+        int start = mr.start[0];
+#pragma unroll
+        for (int k = 1; k < kMultiMax; k++) {
+            base = m == k ? mr.y[k] : base;
+            start = m == k ? mr.start[k] : start;
+        }
+        return base + (r - start);
+    };
     constexpr int RPW = 64 / LPR;
     constexpr int NRG = 4 / WK;
     constexpr int RPP = NRG * RPW;  // rows per workgroup pass (one row group)
@@ -340,7 +376,7 @@ __global__ __launch_bounds__(WG) void k_gemv(const uint8_t* __restrict__ w, int 
     // branch, so the compiler waits for exactly the loads a row needs while
     // the next row's loads stay in flight.
     auto load_row = [&](WT (&wv)[UPL], int64_t row) {
-        const uint8_t* rp = w + min(row, (int64_t)N - 1) * (int64_t)row_bytes;
+        const uint8_t* rp = row_ptr(min(row, (int64_t)N - 1));
 #pragma unroll
         for (int i = 0; i < UPL; i++) UnitT::load(rp, uu[i], 2 * uu[i] + 1 < nbw, wv[i]);
     };
@@ -357,7 +393,7 @@ __global__ __launch_bounds__(WG) void k_gemv(const uint8_t* __restrict__ w, int 
     };
     auto finish_row = [&](float acc, int64_t row, int pl) {
         if (li == LPR - 1 && row < N) {
-            if constexpr (WK == 1) y[row] = acc;
+            if constexpr (WK == 1) *out_ptr(row) = acc;
             else part[(pl * RPP + my_off) * WK + kq] = acc;
         }
     };
@@ -1004,7 +1040,7 @@ static int units_of(int fmt, int64_t K) {
 
 // Workgroups of one kernel instantiation that fit on the device at once
 // (occupancy x compute units), cached per device.
-template <int FMT, int LPR, int UPL, int WK, bool XQ = false>
+template <int FMT, int LPR, int UPL, int WK, bool XQ = false, bool MULTI = false>
 static int resident_workgroups() {
     static std::atomic<int> cache[64];
     int dev = 0;
@@ -1012,7 +1048,8 @@ static int resident_workgroups() {
     int v = cache[dev].load(std::memory_order_relaxed);
     if (v > 0) return v;
     int per_cu = 0, cus = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_gemv<FMT, LPR, UPL, WK, XQ>, WG, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_gemv<FMT, LPR, UPL, WK, XQ, MULTI>,
+                                                     WG, 0) !=
             hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         per_cu <= 0 || cus <= 0) {
@@ -1024,19 +1061,19 @@ static int resident_workgroups() {
     return v;
 }
 
-template <int FMT, int LPR, int UPL, int WK, bool XQ = false>
+template <int FMT, int LPR, int UPL, int WK, bool XQ = false, bool MULTI = false>
 static hipError_t launch_gemv_cfg(const GemvArgs& a, int U, hipStream_t st,
-                                  const ActIn& ai = ActIn{}) {
+                                  const ActIn& ai = ActIn{}, const MultiRows& mr = MultiRows{}) {
     constexpr int RPP = (4 / WK) * (64 / LPR);
     const int64_t ngroups = (a.N + RPP - 1) / RPP;
     // as many workgroups as fit at once, then evened out so that every
     // workgroup gets the same number of passes (to within one)
-    const int64_t resident = resident_workgroups<FMT, LPR, UPL, WK, XQ>();
+    const int64_t resident = resident_workgroups<FMT, LPR, UPL, WK, XQ, MULTI>();
     const int64_t passes = (ngroups + resident - 1) / resident;
     const int64_t grid = (ngroups + passes - 1) / passes;
-    hipLaunchKernelGGL((k_gemv<FMT, LPR, UPL, WK, XQ>), dim3((unsigned)grid), dim3(WG), 0, st,
-                       (const uint8_t*)a.w, (int)a.N, U, (int)(a.K / 32), row_bytes_of(FMT, a.K),
-                       a.q, a.d, a.s, a.y, ai);
+    hipLaunchKernelGGL((k_gemv<FMT, LPR, UPL, WK, XQ, MULTI>), dim3((unsigned)grid), dim3(WG), 0,
+                       st, (const uint8_t*)a.w, (int)a.N, U, (int)(a.K / 32),
+                       row_bytes_of(FMT, a.K), a.q, a.d, a.s, a.y, ai, mr);
     return hipGetLastError();
 }
 
@@ -1284,6 +1321,69 @@ hipError_t launch_quantize_q4k_swiglu(const GemvArgs& a, const SwigluOut& so, co
     const SliceGeom g = slice_geom<FMT>(a.K, U, lds_wk(U));
     if (!lds_slice_fits<FMT>(g, act_lds_bytes(Kp))) return hipErrorInvalidValue;
     return launch_lds_fmt<FMT, true, true>(a, U, g, st, so, ai);
+}
+
+// Several matrices sharing one activation row: one launch of the
+// lanes-per-row kernel over their combined rows (rows of at most 32 units),
+// else one launch per matrix.
+template <int FMT, bool XQ>
+static hipError_t launch_multi_fmt(const MultiRows& mr, int64_t K, const int8_t* q,
+                                   const uint16_t* d, const int32_t* s, const ActIn& ai,
+                                   hipStream_t st) {
+    const int U = units_of(FMT, K);
+    const int Kp = (int)((K + 255) / 256 * 256);
+    const int64_t total = mr.start[mr.count];
+    if (U <= 32 && (!XQ || Kp <= kXqShortKp)) {
+        const GemvArgs a{nullptr, total, K, q, d, s, nullptr};
+        if (U > 16) return launch_gemv_cfg<FMT, 32, 1, 1, XQ, true>(a, U, st, ai, mr);
+        if (U > 8) return launch_gemv_cfg<FMT, 16, 1, 1, XQ, true>(a, U, st, ai, mr);
+        if (U > 4) return launch_gemv_cfg<FMT, 8, 1, 1, XQ, true>(a, U, st, ai, mr);
+        return launch_gemv_cfg<FMT, 4, 1, 1, XQ, true>(a, U, st, ai, mr);
+    }
+    // one launch per matrix; with XQ the first quantises x and writes the
+    // codes, which the others read
+    for (int i = 0; i < mr.count; i++) {
+        const int64_t n = mr.start[i + 1] - mr.start[i];
+        if (n == 0) continue;
+        hipError_t e;
+        if (XQ && i == 0) {
+            const GemvArgs a{mr.w[i], n, K, ai.q, ai.d, ai.s, mr.y[i]};
+            e = launch_quantize_gemv(FMT, a, ai, st);
+        } else {
+            const GemvArgs a{mr.w[i], n, K, XQ ? ai.q : q, XQ ? ai.d : d, XQ ? ai.s : s, mr.y[i]};
+            e = launch_gemv(FMT, a, st);
+        }
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_multi(int fmt, const MultiRows& mr, int64_t K, const int8_t* q,
+                        const uint16_t* d, const int32_t* s, hipStream_t st) {
+    switch (fmt) {
+    case QGEMV_FMT_Q4_0: return launch_multi_fmt<QGEMV_FMT_Q4_0, false>(mr, K, q, d, s, {}, st);
+    case QGEMV_FMT_Q4_K: return launch_multi_fmt<QGEMV_FMT_Q4_K, false>(mr, K, q, d, s, {}, st);
+    case QGEMV_FMT_Q6_K: return launch_multi_fmt<QGEMV_FMT_Q6_K, false>(mr, K, q, d, s, {}, st);
+    case QGEMV_FMT_Q6_K_R8:
+        return launch_multi_fmt<QGEMV_FMT_Q6_K_R8, false>(mr, K, q, d, s, {}, st);
+    default: return launch_multi_fmt<QGEMV_FMT_Q8_0, false>(mr, K, q, d, s, {}, st);
+    }
+}
+
+hipError_t launch_quantize_multi(int fmt, const MultiRows& mr, int64_t K, const ActIn& ai,
+                                 hipStream_t st) {
+    switch (fmt) {
+    case QGEMV_FMT_Q4_0:
+        return launch_multi_fmt<QGEMV_FMT_Q4_0, true>(mr, K, nullptr, nullptr, nullptr, ai, st);
+    case QGEMV_FMT_Q4_K:
+        return launch_multi_fmt<QGEMV_FMT_Q4_K, true>(mr, K, nullptr, nullptr, nullptr, ai, st);
+    case QGEMV_FMT_Q6_K:
+        return launch_multi_fmt<QGEMV_FMT_Q6_K, true>(mr, K, nullptr, nullptr, nullptr, ai, st);
+    case QGEMV_FMT_Q6_K_R8:
+        return launch_multi_fmt<QGEMV_FMT_Q6_K_R8, true>(mr, K, nullptr, nullptr, nullptr, ai, st);
+    default:
+        return launch_multi_fmt<QGEMV_FMT_Q8_0, true>(mr, K, nullptr, nullptr, nullptr, ai, st);
+    }
 }
 
 hipError_t launch_gemv(int fmt, const GemvArgs& a, hipStream_t st) {

@@ -18,6 +18,8 @@
 #include "qgemv.h"
 #include "qgemv_launch.h"
 
+static_assert(QGEMV_MULTI_MAX == qgemv::kMultiMax, "one limit for the multi-matrix entries");
+
 namespace {
 
 thread_local char g_last_error[256] = "";
@@ -171,6 +173,67 @@ qgemv_status swiglu_common(const char* name, const void* w, int64_t N, int64_t K
     return launched(qgemv::launch_quantize_q4k_swiglu(a, so, ai, (hipStream_t)stream), name);
 }
 
+// Gates shared by the two multi-matrix entries; x == NULL for the one whose
+// activation codes are given (q, d, s inputs), else q, d, s are outputs.
+qgemv_status multi_common(const char* name, int fmt, int count, const void* const* w,
+                          const int64_t* n, int64_t K, const float* x, const int8_t* q,
+                          const uint16_t* d, const int32_t* s, float* const* y,
+                          qgemv_stream_t stream) {
+    if (count < 0) return fail(QGEMV_E_SHAPE, "%s: count = %d is negative", name, count);
+    if (count == 0) return ok();
+    if (!w || !n || !y) return fail(QGEMV_E_NULL, "%s: NULL pointer argument", name);
+    int64_t total = 0;
+    for (int i = 0; i < count; i++) {
+        if (n[i] < 0)
+            return fail(QGEMV_E_SHAPE, "%s: n[%d] = %lld is negative", name, i, (long long)n[i]);
+        total += n[i];
+        if (total > INT32_MAX)
+            return fail(QGEMV_E_SHAPE, "%s: %lld rows in all exceed 2^31-1", name,
+                        (long long)total);
+    }
+    if (total == 0) return ok();
+    if (!q || !d || !s) return fail(QGEMV_E_NULL, "%s: NULL pointer argument", name);
+    for (int i = 0; i < count; i++)
+        if (n[i] > 0 && (!w[i] || !y[i]))
+            return fail(QGEMV_E_NULL, "%s: NULL weights or output of matrix %d", name, i);
+    qgemv_status st = check_k(K);
+    if (st != QGEMV_OK) return st;
+    if (fmt < QGEMV_FMT_Q4_0 || fmt > QGEMV_FMT_Q6_K_R8)
+        return fail(QGEMV_E_UNSUPPORTED, "%s: unknown format %d", name, fmt);
+    if (count > QGEMV_MULTI_MAX)
+        return fail(QGEMV_E_UNSUPPORTED, "%s: count = %d exceeds QGEMV_MULTI_MAX = %d", name,
+                    count, QGEMV_MULTI_MAX);
+    if (K > QGEMV_K_MAX)
+        return fail(QGEMV_E_UNSUPPORTED, "%s: K = %lld exceeds QGEMV_K_MAX = %d", name,
+                    (long long)K, QGEMV_K_MAX);
+    for (int i = 0; i < count; i++) {
+        if (n[i] > 0 && !aligned(w[i], 16))
+            return fail(QGEMV_E_ALIGN, "%s: weights of matrix %d must be 16-byte aligned", name, i);
+        if (n[i] > 0 && !aligned(y[i], 4))
+            return fail(QGEMV_E_ALIGN, "%s: output of matrix %d must be 4-byte aligned", name, i);
+    }
+    if (x && !aligned(x, 16)) return fail(QGEMV_E_ALIGN, "%s: x must be 16-byte aligned", name);
+    if ((st = check_act_align(q, d, s)) != QGEMV_OK) return st;
+    if ((st = check_device()) != QGEMV_OK) return st;
+    qgemv::MultiRows mr{};
+    mr.count = count;
+    mr.start[0] = 0;
+    for (int i = 0; i < count; i++) {
+        mr.start[i + 1] = mr.start[i] + (int)n[i];
+        mr.w[i] = w[i];
+        mr.y[i] = y[i];
+    }
+    for (int i = count; i < qgemv::kMultiMax; i++) {
+        mr.start[i + 1] = mr.start[count];
+        mr.w[i] = nullptr;
+        mr.y[i] = nullptr;
+    }
+    if (!x) return launched(qgemv::launch_multi(fmt, mr, K, q, d, s, (hipStream_t)stream), name);
+    const qgemv::ActIn ai{x, const_cast<int8_t*>(q), const_cast<uint16_t*>(d),
+                          const_cast<int32_t*>(s)};
+    return launched(qgemv::launch_quantize_multi(fmt, mr, K, ai, (hipStream_t)stream), name);
+}
+
 }  // namespace
 
 extern "C" {
@@ -194,7 +257,8 @@ const char* qgemv_build_info(void) {
     return "libqgemv abi=1 arch=gfx950 formats=q4_0,q4_k,q6_k,q8_0,q6_k_r8(repacked) act=int8/32+fp16+int32sum "
            "gemv=v_dot4_i32_i8,lds-row-stream,lds-dynamic-rows,lanes-per-row{4,8,16,32,64} "
            "small_m=q4_k{dot4,mfma_i8_16x16x32},q6_k/q4_0{gemv_rows,mfma_i8_16x16x32} "
-           "fused=q4_k_swiglu_quantize,quantize_gemv,quantize_q4_k_swiglu K_max=32768 M_max=64";
+           "fused=q4_k_swiglu_quantize,quantize_gemv,quantize_q4_k_swiglu multi=multi,quantize_multi(<=8) "
+           "K_max=32768 M_max=64";
 }
 
 const char* qgemv_last_error(void) { return g_last_error; }
@@ -343,6 +407,20 @@ qgemv_status qgemv_quantize_q4_k_swiglu(const void* w, int64_t N, int64_t K, con
     const char* name = "qgemv_quantize_q4_k_swiglu";
     if (N > 0 && !x) return fail(QGEMV_E_NULL, "%s: NULL pointer argument", name);
     return swiglu_common(name, w, N, K, x, q, d, s, q_out, d_out, s_out, gu, h, stream);
+}
+
+qgemv_status qgemv_multi(int fmt, int count, const void* const* w, const int64_t* n, int64_t K,
+                         const int8_t* q, const uint16_t* d, const int32_t* s, float* const* y,
+                         qgemv_stream_t stream) {
+    return multi_common("qgemv_multi", fmt, count, w, n, K, nullptr, q, d, s, y, stream);
+}
+
+qgemv_status qgemv_quantize_multi(int fmt, int count, const void* const* w, const int64_t* n,
+                                  int64_t K, const float* x, int8_t* q, uint16_t* d, int32_t* s,
+                                  float* const* y, qgemv_stream_t stream) {
+    const char* name = "qgemv_quantize_multi";
+    if (count > 0 && !x) return fail(QGEMV_E_NULL, "%s: NULL pointer argument", name);
+    return multi_common(name, fmt, count, w, n, K, x, q, d, s, y, stream);
 }
 
 qgemv_status qgemv_block_dots(int fmt, const void* w, int64_t N, int64_t K, int64_t row0,

@@ -42,7 +42,24 @@ struct ActIn {
     int32_t* s;
 };
 
+// Several matrices of one format and K that share one activation row, seen
+// as one range of rows: matrix i holds rows start[i] .. start[i + 1] - 1.
+constexpr int kMultiMax = 8;
+struct MultiRows {
+    int count;
+    int start[kMultiMax + 1];
+    const void* w[kMultiMax];
+    float* y[kMultiMax];
+};
+
 hipError_t launch_gemv(int fmt, const GemvArgs& a, hipStream_t st);
+// The GEMVs of mr on one activation row (q, d, s), in one launch where the
+// rows take the lanes-per-row kernel, else one launch per matrix.
+hipError_t launch_multi(int fmt, const MultiRows& mr, int64_t K, const int8_t* q,
+                        const uint16_t* d, const int32_t* s, hipStream_t st);
+// The same with the activation quantised from ai.x in the launch.
+hipError_t launch_quantize_multi(int fmt, const MultiRows& mr, int64_t K, const ActIn& ai,
+                                 hipStream_t st);
 // launch_quantize_act on ai then launch_gemv on its codes, in one launch
 // where the rows take the LDS-streaming kernel (else in those two launches)
 hipError_t launch_quantize_gemv(int fmt, const GemvArgs& a, const ActIn& ai, hipStream_t st);

@@ -65,6 +65,8 @@ extern "C" {
 
 /* Largest K accepted by the GEMV and small-M entry points in this build. */
 #define QGEMV_K_MAX 32768
+/* Most matrices one qgemv_multi / qgemv_quantize_multi call takes. */
+#define QGEMV_MULTI_MAX 8
 /* Largest M accepted by qgemm_q4_k_small_m. */
 #define QGEMV_M_MAX 64
 
@@ -247,6 +249,30 @@ qgemv_status qgemv_q6_k_r8(const void* w_r, int64_t N, int64_t K, const int8_t* 
 qgemv_status qgemv_quantize_gemv(int fmt, const void* w, int64_t N, int64_t K,
                                  const float* x, int8_t* q, uint16_t* d, int32_t* s,
                                  float* y, qgemv_stream_t stream);
+
+/* Several GEMVs on one activation row in one launch (the q/k/v projections,
+ * or gate and up stored apart: "Running an LLM on VKNN", Performance: every
+ * launch besides the matmuls is overhead; llambda.lisp README, Features:
+ * row-parallel GEMV with isolated writes).  count matrices of one format
+ * fmt and one K: w[i] (device, 16-byte aligned) holds n[i] rows, y[i]
+ * (device, fp32 [n[i]]) receives their products with the activation q, d, s
+ * (qgemv_quantize_act, same K).  y[i] equals the format's GEMV of matrix i
+ * bit for bit.  w, n, y are host arrays of count entries, read during the
+ * call only.  0 <= count <= QGEMV_MULTI_MAX (larger: QGEMV_E_UNSUPPORTED);
+ * count == 0 or all n[i] == 0 is a no-op; n[i] < 0: QGEMV_E_SHAPE.  Rows of
+ * at most 32 units of 64 weights (K <= 2048) go out as one launch over the
+ * combined rows; longer rows take one launch per matrix.  Other gates and
+ * errors as for the format's GEMV. */
+qgemv_status qgemv_multi(int fmt, int count, const void* const* w, const int64_t* n,
+                         int64_t K, const int8_t* q, const uint16_t* d, const int32_t* s,
+                         float* const* y, qgemv_stream_t stream);
+/* qgemv_multi with the activation quantised from fp32 x [K] (16-byte
+ * aligned) in the same launch: equal, bit for bit, to qgemv_quantize_act
+ * into q, d, s followed by qgemv_multi; q, d, s receive the codes. */
+qgemv_status qgemv_quantize_multi(int fmt, int count, const void* const* w,
+                                  const int64_t* n, int64_t K, const float* x, int8_t* q,
+                                  uint16_t* d, int32_t* s, float* const* y,
+                                  qgemv_stream_t stream);
 
 /* Validation: the int32 block dots of weight rows [row0, row0+nrows) against
  * one activation row q [Kp], computed by the same device code as the GEMV

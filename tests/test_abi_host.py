@@ -164,6 +164,44 @@ def test_gates_quantize_fused_entries():
                    S) == qg.QGEMV_OK
 
 
+def test_gates_multi_entries():
+    """qgemv_multi / qgemv_quantize_multi: count, NULL arrays and members,
+    negative rows, format, limits and alignment, before any device work."""
+    import ctypes
+    qg = _lib()
+    S = 0
+    P = ctypes.c_void_p
+    def arrays(ws, ns, ys):
+        c = len(ws)
+        return (c, (P * max(c, 1))(*ws), (ctypes.c_int64 * max(c, 1))(*ns), (P * max(c, 1))(*ys))
+    c, w, n, y = arrays([A, A], [10, 20], [A, A])
+    M = "qgemv_multi"          # fmt, count, w, n, K, q, d, s, y, stream
+    assert _status(M, 1, c, w, n, 256, A, A, A, y, S) != qg.QGEMV_E_NULL
+    assert _status(M, 1, -1, w, n, 256, A, A, A, y, S) == qg.QGEMV_E_SHAPE
+    assert _status(M, 1, 0, None, None, 256, None, None, None, None, S) == qg.QGEMV_OK
+    assert _status(M, 1, c, None, n, 256, A, A, A, y, S) == qg.QGEMV_E_NULL
+    assert _status(M, 1, c, w, n, 256, None, A, A, y, S) == qg.QGEMV_E_NULL
+    c2, w2, n2, y2 = arrays([A, None], [10, 20], [A, A])
+    assert _status(M, 1, c2, w2, n2, 256, A, A, A, y2, S) == qg.QGEMV_E_NULL
+    c3, w3, n3, y3 = arrays([A, None], [10, 0], [A, None])       # empty member: no pointers needed
+    assert _status(M, 1, c3, w3, n3, 48, A, A, A, y3, S) == qg.QGEMV_E_SHAPE
+    c4, w4, n4, y4 = arrays([A, A], [10, -2], [A, A])
+    assert _status(M, 1, c4, w4, n4, 256, A, A, A, y4, S) == qg.QGEMV_E_SHAPE
+    c5, w5, n5, y5 = arrays([A] * 9, [1] * 9, [A] * 9)
+    assert _status(M, 1, c5, w5, n5, 256, A, A, A, y5, S) == qg.QGEMV_E_UNSUPPORTED
+    assert _status(M, 9, c, w, n, 256, A, A, A, y, S) == qg.QGEMV_E_UNSUPPORTED
+    assert _status(M, 1, c, w, n, 65536, A, A, A, y, S) == qg.QGEMV_E_UNSUPPORTED
+    c6, w6, n6, y6 = arrays([A, A + 8], [10, 20], [A, A])
+    assert _status(M, 1, c6, w6, n6, 256, A, A, A, y6, S) == qg.QGEMV_E_ALIGN
+    c7, w7, n7, y7 = arrays([A, A], [10, 20], [A, A + 2])
+    assert _status(M, 1, c7, w7, n7, 256, A, A, A, y7, S) == qg.QGEMV_E_ALIGN
+    assert _status(M, 1, c, w, n, 256, A + 4, A, A, y, S) == qg.QGEMV_E_ALIGN
+    XM = "qgemv_quantize_multi"   # fmt, count, w, n, K, x, q, d, s, y, stream
+    assert _status(XM, 1, c, w, n, 256, None, A, A, A, y, S) == qg.QGEMV_E_NULL
+    assert _status(XM, 1, c, w, n, 256, A + 4, A, A, A, y, S) == qg.QGEMV_E_ALIGN
+    assert _status(XM, 1, 0, None, None, 256, None, None, None, None, None, S) == qg.QGEMV_OK
+
+
 def test_gate_order_null_before_shape_before_align():
     qg = _lib()
     # a NULL pointer wins over a bad K and a misaligned pointer
