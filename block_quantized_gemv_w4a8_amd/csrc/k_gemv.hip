@@ -539,6 +539,93 @@ __host__ __device__ inline int unit_byte(int u) {
     return u * 68;
 }
 
+// One wave's slice of every row in the LDS-staged kernels (k_gemv_lds,
+// k_gemv_dyn): units u_lo .. u_hi - 1 of a row, lane i taking units
+// u_lo + i, u_lo + i + 64, ..., their activation held in registers; the
+// slice's bytes sbeg .. sbeg + slen - 1 of a row move through the wave's LDS
+// buffers as 16-byte chunks on a grid aligned to 16-byte global addresses
+// (lane i fetches chunks i, i + 64, ...; the last one shifted back to end at
+// the slice end, so no load leaves the row).  Lanes past the slice repeat its
+// last unit (every load unconditional and in bounds) and drop its term.
+template <int FMT, int UPL, int NL, bool NT>
+struct SliceStream {
+    using UnitT = Unit<FMT>;
+    using WT = typename UnitT::W;
+    using UL = UnitLds<FMT>;
+    int lane, u_lo, u_hi, sbeg, slen, nbw;
+    ActReg<FMT> A[UPL];
+    int ul[UPL];
+    bool ok[UPL], has1[UPL];
+
+    __device__ __forceinline__ SliceStream(int lane_, int U, int US, int kq, int nbw_,
+                                           int row_bytes)
+        : lane(lane_), u_lo(kq * US), u_hi(min(U, kq * US + US)), nbw(nbw_) {
+        sbeg = unit_byte<FMT>(u_lo);
+        slen = min(unit_byte<FMT>(u_hi), row_bytes) - sbeg;
+    }
+    // the activation of the lane's units (from global memory or LDS)
+    __device__ __forceinline__ void load_act(const int8_t* q, const uint16_t* d,
+                                             const int32_t* s) {
+#pragma unroll
+        for (int i = 0; i < UPL; i++) {
+            const int u = u_lo + lane + 64 * i;
+            ok[i] = u < u_hi;
+            const int uc = ok[i] ? u : u_hi - 1;
+            A[i].load(q, d, s, uc);
+            ul[i] = uc - u_lo;
+            has1[i] = 2 * uc + 1 < nbw;
+        }
+    }
+    // offset (from the aligned chunk base) of this lane's k-th chunk
+    __device__ __forceinline__ int chunk_off(int k, int delta) const {
+        return min(16 * (lane + 64 * k), delta + slen - 16);
+    }
+    // Issue the loads of the slice of the row at rowp; returns the slice's
+    // offset from the 16-byte-aligned address below it.
+    __device__ __forceinline__ int stage(u32x4 (&R)[NL], const uint8_t* rowp) const {
+        const uint8_t* a = rowp + sbeg;
+        const int delta = (int)((uintptr_t)a & 15);
+        const uint8_t* ab = a - delta;
+#pragma unroll
+        for (int k = 0; k < NL; k++) R[k] = ld16_stream<NT>(ab + chunk_off(k, delta));
+        return delta;
+    }
+    // Park a staged slice in the wave's LDS buffer (in the row's byte order).
+    __device__ __forceinline__ void commit(const u32x4 (&R)[NL], int delta, uint8_t* buf) const {
+#pragma unroll
+        for (int k = 0; k < NL; k++) st16(buf + chunk_off(k, delta), R[k]);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+    // The slice's dot with the activation, reduced over the wave (valid in
+    // lane 63).
+    __device__ __forceinline__ float dot(const uint8_t* buf, int delta) const {
+        float acc = 0.0f;
+#pragma unroll
+        for (int i = 0; i < UPL; i++) {
+            WT wv;
+            UL::load(buf, delta, ul[i], has1[i], wv);
+            const float t = UnitT::term(wv, A[i], u_lo + ul[i], nbw);
+            acc += ok[i] ? t : 0.0f;
+        }
+        return group_sum<64>(acc);
+    }
+};
+
+// The activation quantised in the launch (XQ): the workgroup quantises x
+// into LDS (aq, ad, as), every lane loads its units' activation from there,
+// and workgroup 0 writes the codes out.  Called by every thread.
+template <int NTH, class SS>
+__device__ __forceinline__ void xq_prologue(SS& ss, const ActIn& ai, int nbw, int Kp,
+                                            const f32x4 (&xv)[4], int8_t* aq, uint16_t* ad,
+                                            int32_t* as) {
+    quantize_row_lds<NTH>(ai.x, 32 * nbw, Kp, xv, aq, ad, as);
+    __syncthreads();
+    ss.load_act(aq, ad, as);
+    if (blockIdx.x == 0) xq_write_out<NTH>(ai, Kp, aq, ad, as);
+}
+
 // LDS-streaming GEMV (whole waves per row, LPR = 64).  Same work split as
 // k_gemv, but a wave brings its slice of a row in with fully coalesced loads
 // -- lane i fetches the 16-byte chunk i, i + 64, ... of the slice, on a chunk
@@ -574,32 +661,11 @@ __global__ __launch_bounds__(WG) void k_gemv_lds(const uint8_t* __restrict__ w, 
     constexpr int RPP = 4 / WK;
     __shared__ float part[SEGP * RPP * WK];
     __shared__ float hseg[SW ? 32 * (SEGP * RPP / 64) : 1];   // SW: h of a segment's blocks
-    using UnitT = Unit<FMT>;
-    using WT = typename UnitT::W;
-    using UL = UnitLds<FMT>;
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int kq = wave % WK, rg = wave / WK;
-    const int u_lo = kq * US;
-    const int u_hi = min(U, u_lo + US);
-    const int sbeg = unit_byte<FMT>(u_lo);
-    const int slen = min(unit_byte<FMT>(u_hi), row_bytes) - sbeg;
-
-    ActReg<FMT> A[UPL];
-    int ul[UPL];
-    bool ok[UPL], has1[UPL];
-    auto load_act = [&](const int8_t* aq, const uint16_t* ad, const int32_t* as) {
-#pragma unroll
-        for (int i = 0; i < UPL; i++) {
-            const int u = u_lo + lane + LPR * i;
-            ok[i] = u < u_hi;
-            const int uc = ok[i] ? u : u_hi - 1;
-            A[i].load(aq, ad, as, uc);
-            ul[i] = uc - u_lo;
-            has1[i] = 2 * uc + 1 < nbw;
-        }
-    };
-    if constexpr (!XQ) load_act(q, d, s);
+    SliceStream<FMT, UPL, NL, NT> ss(lane, U, US, kq, nbw, row_bytes);
+    if constexpr (!XQ) ss.load_act(q, d, s);
     // XQ: the activation row, quantised in this workgroup, after the slice buffers
     const int Kp = (32 * nbw + 255) / 256 * 256;
     int8_t* const aq = reinterpret_cast<int8_t*>(lds + 8 * buf_bytes);
@@ -636,36 +702,11 @@ __global__ __launch_bounds__(WG) void k_gemv_lds(const uint8_t* __restrict__ w, 
             }
         }
     }
-    // offset (from the aligned chunk base) of this lane's k-th chunk
-    auto chunk_off = [&](int k, int delta) { return min(16 * (lane + 64 * k), delta + slen - 16); };
-    // Issue the loads of a row's slice; returns the slice's offset from the
-    // 16-byte-aligned address below it.
     auto stage = [&](u32x4 (&R)[NL], int64_t row) {
-        const uint8_t* a = w + min(row, (int64_t)N - 1) * (int64_t)row_bytes + sbeg;
-        const int delta = (int)((uintptr_t)a & 15);
-        const uint8_t* ab = a - delta;
-#pragma unroll
-        for (int k = 0; k < NL; k++) R[k] = ld16_stream<NT>(ab + chunk_off(k, delta));
-        return delta;
+        return ss.stage(R, w + min(row, (int64_t)N - 1) * (int64_t)row_bytes);
     };
-    auto commit = [&](const u32x4 (&R)[NL], int delta, uint8_t* buf) {
-#pragma unroll
-        for (int k = 0; k < NL; k++) st16(buf + chunk_off(k, delta), R[k]);
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    };
-    auto dot_row = [&](const uint8_t* buf, int delta) {
-        float acc = 0.0f;
-#pragma unroll
-        for (int i = 0; i < UPL; i++) {
-            WT wv;
-            UL::load(buf, delta, ul[i], has1[i], wv);
-            const float t = UnitT::term(wv, A[i], u_lo + ul[i], nbw);
-            acc += ok[i] ? t : 0.0f;
-        }
-        return group_sum<LPR>(acc);
-    };
+    auto commit = [&](const u32x4 (&R)[NL], int delta, uint8_t* buf) { ss.commit(R, delta, buf); };
+    auto dot_row = [&](const uint8_t* buf, int delta) { return ss.dot(buf, delta); };
     auto finish_row = [&](float acc, int pl) {
         if (lane == LPR - 1) part[(pl * RPP + rg) * WK + kq] = acc;
     };
@@ -690,20 +731,7 @@ __global__ __launch_bounds__(WG) void k_gemv_lds(const uint8_t* __restrict__ w, 
             __builtin_amdgcn_sched_barrier(0);
             db = stage(Rb, row_of(p0 + 2));
             __builtin_amdgcn_sched_barrier(0);
-            if (xq) {
-                quantize_row_lds(ai.x, 32 * nbw, Kp, xv, aq, ad, as);
-                __syncthreads();
-                load_act(aq, ad, as);
-                if (blockIdx.x == 0) {
-                    for (int t = threadIdx.x; t < Kp / 16; t += WG)
-                        *reinterpret_cast<u32x4*>(ai.q + 16 * t) =
-                            *reinterpret_cast<const u32x4*>(aq + 16 * t);
-                    for (int t = threadIdx.x; t < Kp / 32; t += WG) {
-                        ai.d[t] = ad[t];
-                        ai.s[t] = as[t];
-                    }
-                }
-            }
+            if (xq) xq_prologue<WG>(ss, ai, nbw, Kp, xv, aq, ad, as);
             commit(Rc, dc, buf0);
             d0 = dc;
         }
@@ -797,17 +825,10 @@ __global__ __launch_bounds__(DWG) void k_gemv_dyn(const uint8_t* __restrict__ w,
     static_assert(DW % WK == 0, "whole waves per slice");
     extern __shared__ __align__(16) uint8_t lds[];
     __shared__ int cnt[WK];
-    constexpr int LPR = 64;
-    using UnitT = Unit<FMT>;
-    using WT = typename UnitT::W;
-    using UL = UnitLds<FMT>;
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int kq = wave % WK;
-    const int u_lo = kq * US;
-    const int u_hi = min(U, u_lo + US);
-    const int sbeg = unit_byte<FMT>(u_lo);
-    const int slen = min(unit_byte<FMT>(u_hi), row_bytes) - sbeg;
+    SliceStream<FMT, UPL, NL, true> ss(lane, U, US, kq, nbw, row_bytes);
 
     // this workgroup's rows; indices past them (and rows past N) map to row
     // N - 1, whose bytes the prefetch then reads from cache
@@ -818,21 +839,7 @@ __global__ __launch_bounds__(DWG) void k_gemv_dyn(const uint8_t* __restrict__ w,
     auto row_of = [&](int i) { return i < pool_n ? min(row_raw(i), N - 1) : N - 1; };
 
     if (threadIdx.x < WK) cnt[threadIdx.x] = 0;
-    ActReg<FMT> A[UPL];
-    int ul[UPL];
-    bool ok[UPL], has1[UPL];
-    auto load_act = [&](const int8_t* aq, const uint16_t* ad, const int32_t* as) {
-#pragma unroll
-        for (int i = 0; i < UPL; i++) {
-            const int u = u_lo + lane + LPR * i;
-            ok[i] = u < u_hi;
-            const int uc = ok[i] ? u : u_hi - 1;
-            A[i].load(aq, ad, as, uc);
-            ul[i] = uc - u_lo;
-            has1[i] = 2 * uc + 1 < nbw;
-        }
-    };
-    if constexpr (!XQ) load_act(q, d, s);
+    if constexpr (!XQ) ss.load_act(q, d, s);
     const int Kp = (32 * nbw + 255) / 256 * 256;
     int8_t* const aq = reinterpret_cast<int8_t*>(lds + 2 * DW * buf_bytes);
     uint16_t* const ad = reinterpret_cast<uint16_t*>(lds + 2 * DW * buf_bytes + Kp);
@@ -853,35 +860,13 @@ __global__ __launch_bounds__(DWG) void k_gemv_dyn(const uint8_t* __restrict__ w,
     };
     auto take = [&](int v) { return __builtin_amdgcn_readfirstlane(v); };
     auto grab = [&]() { return take(grab_issue()); };
-    auto chunk_off = [&](int k, int delta) { return min(16 * (lane + 64 * k), delta + slen - 16); };
     auto stage = [&](u32x4 (&R)[NL], int row) {
-        const uint8_t* a = w + (int64_t)row * row_bytes + sbeg;
-        const int delta = (int)((uintptr_t)a & 15);
-        const uint8_t* ab = a - delta;
-#pragma unroll
-        for (int k = 0; k < NL; k++) R[k] = ld16_stream<true>(ab + chunk_off(k, delta));
-        return delta;
+        return ss.stage(R, w + (int64_t)row * row_bytes);
     };
-    auto commit = [&](const u32x4 (&R)[NL], int delta, uint8_t* buf) {
-#pragma unroll
-        for (int k = 0; k < NL; k++) st16(buf + chunk_off(k, delta), R[k]);
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    };
-    auto dot_row = [&](const uint8_t* buf, int delta) {
-        float acc = 0.0f;
-#pragma unroll
-        for (int i = 0; i < UPL; i++) {
-            WT wv;
-            UL::load(buf, delta, ul[i], has1[i], wv);
-            const float t = UnitT::term(wv, A[i], u_lo + ul[i], nbw);
-            acc += ok[i] ? t : 0.0f;
-        }
-        return group_sum<LPR>(acc);
-    };
+    auto commit = [&](const u32x4 (&R)[NL], int delta, uint8_t* buf) { ss.commit(R, delta, buf); };
+    auto dot_row = [&](const uint8_t* buf, int delta) { return ss.dot(buf, delta); };
     auto finish_row = [&](float acc, int i) {
-        if (lane == LPR - 1 && i < pool_n && row_raw(i) < N) {
+        if (lane == 63 && i < pool_n && row_raw(i) < N) {
             if constexpr (WK == 1) y[row_raw(i)] = acc;
             else part[i * WK + kq] = acc;
         }
@@ -905,12 +890,7 @@ __global__ __launch_bounds__(DWG) void k_gemv_dyn(const uint8_t* __restrict__ w,
         ib = grab();
         db = stage(Rb, row_of(ib));
         __builtin_amdgcn_sched_barrier(0);
-        if (XQ) {
-            quantize_row_lds<DWG>(ai.x, 32 * nbw, Kp, xv, aq, ad, as);
-            __syncthreads();
-            load_act(aq, ad, as);
-            if (b == 0) xq_write_out<DWG>(ai, Kp, aq, ad, as);
-        }
+        if (XQ) xq_prologue<DWG>(ss, ai, nbw, Kp, xv, aq, ad, as);
         commit(Rc, dc, buf0);
         d0 = dc;
         i0 = ic;
