@@ -61,7 +61,8 @@ hipError_t launch_multi(int fmt, const MultiRows& mr, int64_t K, const int8_t* q
 hipError_t launch_quantize_multi(int fmt, const MultiRows& mr, int64_t K, const ActIn& ai,
                                  hipStream_t st);
 // launch_quantize_act on ai then launch_gemv on its codes, in one launch
-// where the rows take the LDS-streaming kernel (else in those two launches)
+// where the kernel's LDS also holds the quantised row (else in those two
+// launches)
 hipError_t launch_quantize_gemv(int fmt, const GemvArgs& a, const ActIn& ai, hipStream_t st);
 hipError_t launch_q6k_repack(const void* w, int64_t N, int64_t K, void* wr, hipStream_t st);
 hipError_t launch_q4k_swiglu(const GemvArgs& a, const SwigluOut& so, hipStream_t st);

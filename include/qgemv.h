@@ -241,11 +241,12 @@ qgemv_status qgemv_q6_k_r8(const void* w_r, int64_t N, int64_t K, const int8_t* 
  * Performance: every launch besides the matmuls is overhead; "Backends and
  * hardware", section "CPU": the activation is quantised once per matmul).
  * x: fp32 [K], 16-byte aligned; q [Kp], d [Kp/32], s [Kp/32] receive the
- * codes of x; y: fp32 [N].  Rows of more than 32 units of 64 weights are
- * served by one launch in which every workgroup quantises x into its own LDS
- * while its first weight rows load; shorter rows take the two launches.
- * Other arguments, limits and errors as for the format's GEMV; x must not
- * overlap any output. */
+ * codes of x; y: fp32 [N].  One launch, in which every workgroup quantises
+ * x into its own LDS while its first weight rows load -- except where the
+ * staged rows and the quantised x would not fit a workgroup's LDS (the
+ * longest rows, e.g. K = 32768 for Q4_K and Q6_K), which take the two
+ * launches.  Other arguments, limits and errors as for the format's GEMV; x
+ * must not overlap any output. */
 qgemv_status qgemv_quantize_gemv(int fmt, const void* w, int64_t N, int64_t K,
                                  const float* x, int8_t* q, uint16_t* d, int32_t* s,
                                  float* y, qgemv_stream_t stream);
