@@ -611,6 +611,24 @@ struct SliceStream {
         }
         return group_sum<64>(acc);
     }
+    // Two rows' dots (two independent chains for the scheduler to
+    // interleave); each is formed exactly as dot() forms it.
+    __device__ __forceinline__ void dot2(const uint8_t* buf0, int delta0, const uint8_t* buf1,
+                                         int delta1, float& s0, float& s1) const {
+        float acc0 = 0.0f, acc1 = 0.0f;
+#pragma unroll
+        for (int i = 0; i < UPL; i++) {
+            WT w0, w1;
+            UL::load(buf0, delta0, ul[i], has1[i], w0);
+            UL::load(buf1, delta1, ul[i], has1[i], w1);
+            const float t0 = UnitT::term(w0, A[i], u_lo + ul[i], nbw);
+            const float t1 = UnitT::term(w1, A[i], u_lo + ul[i], nbw);
+            acc0 += ok[i] ? t0 : 0.0f;
+            acc1 += ok[i] ? t1 : 0.0f;
+        }
+        s0 = group_sum<64>(acc0);
+        s1 = group_sum<64>(acc1);
+    }
 };
 
 // The activation quantised in the launch (XQ): the workgroup quantises x
@@ -624,6 +642,66 @@ __device__ __forceinline__ void xq_prologue(SS& ss, const ActIn& ai, int nbw, in
     __syncthreads();
     ss.load_act(aq, ad, as);
     if (blockIdx.x == 0) xq_write_out<NTH>(ai, Kp, aq, ad, as);
+}
+
+// SwiGLU outputs of the fused gate|up product (SW).  Workgroup 0 zeroes the
+// activation blocks between nh and the next multiple of 256.
+template <int NTH>
+__device__ __forceinline__ void swiglu_zero_tail(const SwigluOut& so) {
+    const int64_t nhb = so.nh / 32, nbo = (so.nh + 255) / 256 * 8;
+    for (int64_t t = threadIdx.x; t < (nbo - nhb) * 8; t += NTH) {
+        const int64_t b = nhb + t / 8;
+        *reinterpret_cast<uint32_t*>(so.q + 32 * b + 4 * (t % 8)) = 0u;
+        if (t % 8 == 0) {
+            so.d[b] = 0;
+            so.s[b] = 0;
+        }
+    }
+}
+
+// The output blocks hb0 + j * stride (j < nblk) of the fused product: row l
+// of block j (gate rows l < 32, up rows l >= 32) is parked in part at
+// (64 j + l) * WK + slice, its WK slices added in slice order.  One thread per
+// value forms h = silu(g) * u into hseg, then 8 lanes per block quantise it
+// as the next product's activation block (the same device functions as
+// k_silu_mul_quantize); [gate | up] and h are stored only where asked for.
+// Called by every thread of the workgroup once part is complete.
+template <int NTH, int WK>
+__device__ __forceinline__ void swiglu_epilogue(const float* part, float* hseg, int nblk,
+                                                int64_t hb0, int64_t stride,
+                                                const SwigluOut& so) {
+    for (int t = threadIdx.x; t < 32 * nblk; t += NTH) {
+        const int j = t >> 5, i = t & 31;
+        const int64_t hb = hb0 + j * stride;
+        float g = part[(64 * j + i) * WK], u = part[(64 * j + 32 + i) * WK];
+#pragma unroll
+        for (int kk = 1; kk < WK; kk++) {
+            g += part[(64 * j + i) * WK + kk];
+            u += part[(64 * j + 32 + i) * WK + kk];
+        }
+        const float hv = silu_mul(g, u);
+        hseg[t] = hv;
+        if (so.gu) {
+            so.gu[32 * hb + i] = g;
+            so.gu[so.nh + 32 * hb + i] = u;
+        }
+        if (so.h) so.h[32 * hb + i] = hv;
+    }
+    __syncthreads();
+    // whole aligned groups of 8 lanes take part (8 * nblk is a multiple of 8)
+    for (int t = threadIdx.x; t < 8 * nblk; t += NTH) {
+        const int j = t >> 3, sub = t & 7;
+        const int64_t hb = hb0 + j * stride;
+        float v[4];
+#pragma unroll
+        for (int k = 0; k < 4; k++) v[k] = hseg[32 * j + 4 * sub + k];
+        const QBlock r = quantize_block8(v);
+        *reinterpret_cast<uint32_t*>(so.q + 32 * hb + 4 * sub) = r.packed;
+        if (sub == 0) {
+            so.d[hb] = (uint16_t)r.dbits;
+            so.s[hb] = r.sum;
+        }
+    }
 }
 
 // LDS-streaming GEMV (whole waves per row, LPR = 64).  Same work split as
@@ -643,11 +721,8 @@ __device__ __forceinline__ void xq_prologue(SS& ss, const ActIn& ai, int nbw, in
 // 0 .. nh-1 then up rows nh .. 2nh-1 (N = 2nh).  A workgroup walks whole
 // output blocks of 32: block b is gate rows 32b .. 32b+31 and up rows
 // nh+32b .. nh+32b+31, so the 64 row results of a block end up parked in the
-// workgroup's LDS together.  At the end of a segment, 8 lanes per block form
-// h = silu(g) * u and quantise it as the next product's activation block b
-// (the same device functions as k_silu_mul_quantize); the [gate | up] and h
-// values are stored only where asked for.  Workgroup 0 also zeroes the
-// activation blocks between nh and the next multiple of 256.
+// workgroup's LDS together, and at the end of a segment swiglu_epilogue turns
+// them into the next product's activation blocks.
 template <int FMT, int UPL, int WK, int NL, bool NT, bool SW, bool XQ>
 __global__ __launch_bounds__(WG) void k_gemv_lds(const uint8_t* __restrict__ w, int N, int U,
                                                   int US, int nbw, int row_bytes, int buf_bytes,
@@ -690,18 +765,7 @@ __global__ __launch_bounds__(WG) void k_gemv_lds(const uint8_t* __restrict__ w, 
         const int l = (int)(p % GPB) * RPP + rg;   // 0..31 gate, 32..63 up
         return l < 32 ? 32 * hb + l : so.nh + 32 * hb + (l - 32);
     };
-    if (SW && blockIdx.x == 0) {
-        // activation blocks past nh, up to the next multiple of 256: zero
-        const int64_t nbo = (so.nh + 255) / 256 * 8;
-        for (int64_t t = threadIdx.x; t < (nbo - nhb) * 8; t += WG) {
-            const int64_t b = nhb + t / 8;
-            *reinterpret_cast<uint32_t*>(so.q + 32 * b + 4 * (t % 8)) = 0u;
-            if (t % 8 == 0) {
-                so.d[b] = 0;
-                so.s[b] = 0;
-            }
-        }
-    }
+    if (SW && blockIdx.x == 0) swiglu_zero_tail<WG>(so);
     auto stage = [&](u32x4 (&R)[NL], int64_t row) {
         return ss.stage(R, w + min(row, (int64_t)N - 1) * (int64_t)row_bytes);
     };
@@ -759,41 +823,8 @@ __global__ __launch_bounds__(WG) void k_gemv_lds(const uint8_t* __restrict__ w, 
                 }
             }
         } else {
-            // row l of the segment's output block j is part[(64 j + l) * WK + kq];
-            // one thread per value forms h, then 8 lanes per block quantise it
-            const int nblk = np / GPB;
-            const int t = threadIdx.x;
-            if (t < 32 * nblk) {
-                const int j = t >> 5, i = t & 31;
-                const int64_t hb = blockIdx.x + (p0 / GPB + j) * G;
-                float g = part[(64 * j + i) * WK], u = part[(64 * j + 32 + i) * WK];
-#pragma unroll
-                for (int kk = 1; kk < WK; kk++) {
-                    g += part[(64 * j + i) * WK + kk];
-                    u += part[(64 * j + 32 + i) * WK + kk];
-                }
-                const float hv = silu_mul(g, u);
-                hseg[t] = hv;
-                if (so.gu) {
-                    so.gu[32 * hb + i] = g;
-                    so.gu[so.nh + 32 * hb + i] = u;
-                }
-                if (so.h) so.h[32 * hb + i] = hv;
-            }
-            __syncthreads();
-            if (t < 8 * nblk) {
-                const int j = t >> 3, sub = t & 7;
-                const int64_t hb = blockIdx.x + (p0 / GPB + j) * G;
-                float v[4];
-#pragma unroll
-                for (int k = 0; k < 4; k++) v[k] = hseg[32 * j + 4 * sub + k];
-                const QBlock r = quantize_block8(v);
-                *reinterpret_cast<uint32_t*>(so.q + 32 * hb + 4 * sub) = r.packed;
-                if (sub == 0) {
-                    so.d[hb] = (uint16_t)r.dbits;
-                    so.s[hb] = r.sum;
-                }
-            }
+            // row l of the segment's output block j is part[(64 j + l) * WK + kq]
+            swiglu_epilogue<WG, WK>(part, hseg, np / GPB, blockIdx.x + (p0 / GPB) * G, G, so);
         }
         __syncthreads();
     }
@@ -811,17 +842,27 @@ __global__ __launch_bounds__(WG) void k_gemv_lds(const uint8_t* __restrict__ w, 
 // slices of a row has its own counter (the waves holding that slice's
 // activation pull from it) and the slices' partial sums meet in LDS, added
 // in slice order as in k_gemv_lds, so every output has the same bits.
+//
+// SW (the fused gate|up product, as in k_gemv_lds): a workgroup owns the
+// output blocks b, b + G, b + 2G, ... (64 rows each, gate then up); every row
+// result goes to LDS and swiglu_epilogue forms and quantises h once all of
+// them are in.  With two 4-wave workgroups per unit and whole blocks each,
+// the younger workgroup of a unit ran ~4 us behind its twin (and 448 blocks
+// do not split evenly over 512 workgroups); here the unit's 8 waves share
+// its one or two blocks until the last row.
 constexpr int DW = 8;           // waves of a dynamic-row workgroup
 constexpr int DWG = 64 * DW;    // its threads
-constexpr int DRG = 8;          // rows per row group of the static split
+constexpr int DRG = 8;          // rows per row group of the static split (even: rows go in pairs)
+static_assert(DRG % 2 == 0, "pairs of rows stay inside a row group");
 
-template <int FMT, int UPL, int WK, int NL, bool XQ>
+template <int FMT, int UPL, int WK, int NL, bool XQ, bool SW, bool PAIRS>
 __global__ __launch_bounds__(DWG) void k_gemv_dyn(const uint8_t* __restrict__ w, int N, int U,
                                                    int US, int nbw, int row_bytes, int buf_bytes,
                                                    const int8_t* __restrict__ q,
                                                    const uint16_t* __restrict__ d,
                                                    const int32_t* __restrict__ s,
-                                                   float* __restrict__ y, const ActIn ai) {
+                                                   float* __restrict__ y, const SwigluOut so,
+                                                   const ActIn ai) {
     static_assert(DW % WK == 0, "whole waves per slice");
     extern __shared__ __align__(16) uint8_t lds[];
     __shared__ int cnt[WK];
@@ -833,12 +874,21 @@ __global__ __launch_bounds__(DWG) void k_gemv_dyn(const uint8_t* __restrict__ w,
     // this workgroup's rows; indices past them (and rows past N) map to row
     // N - 1, whose bytes the prefetch then reads from cache
     const int G = gridDim.x, b = blockIdx.x;
+    const int nhb = SW ? (int)(so.nh / 32) : 0;
+    const int nblk = SW ? (nhb > b ? (nhb - b + G - 1) / G : 0) : 0;   // SW: output blocks
     const int ngr = (N + DRG - 1) / DRG;
-    const int pool_n = ngr > b ? (ngr - b + G - 1) / G * DRG : 0;
-    auto row_raw = [&](int i) { return DRG * (b + (i / DRG) * G) + i % DRG; };
+    const int pool_n = SW ? 64 * nblk : (ngr > b ? (ngr - b + G - 1) / G * DRG : 0);
+    auto row_raw = [&](int i) {
+        if constexpr (SW) {
+            const int hb = b + (i >> 6) * G, l = i & 63;
+            return l < 32 ? 32 * hb + l : (int)so.nh + 32 * hb + (l - 32);
+        }
+        return DRG * (b + (i / DRG) * G) + i % DRG;
+    };
     auto row_of = [&](int i) { return i < pool_n ? min(row_raw(i), N - 1) : N - 1; };
 
     if (threadIdx.x < WK) cnt[threadIdx.x] = 0;
+    if (SW && b == 0) swiglu_zero_tail<DWG>(so);
     if constexpr (!XQ) ss.load_act(q, d, s);
     const int Kp = (32 * nbw + 255) / 256 * 256;
     int8_t* const aq = reinterpret_cast<int8_t*>(lds + 2 * DW * buf_bytes);
@@ -846,6 +896,7 @@ __global__ __launch_bounds__(DWG) void k_gemv_dyn(const uint8_t* __restrict__ w,
     int32_t* const as = reinterpret_cast<int32_t*>(lds + 2 * DW * buf_bytes + Kp + Kp / 16);
     float* const part =
         reinterpret_cast<float*>(lds + 2 * DW * buf_bytes + (XQ ? act_lds_bytes(Kp) : 0));
+    float* const hseg = part + pool_n * WK;   // SW: h of the workgroup's blocks
     uint8_t* buf0 = lds + (2 * wave) * buf_bytes;
     uint8_t* buf1 = buf0 + buf_bytes;
     __syncthreads();   // the counters are zero
@@ -867,55 +918,121 @@ __global__ __launch_bounds__(DWG) void k_gemv_dyn(const uint8_t* __restrict__ w,
     auto dot_row = [&](const uint8_t* buf, int delta) { return ss.dot(buf, delta); };
     auto finish_row = [&](float acc, int i) {
         if (lane == 63 && i < pool_n && row_raw(i) < N) {
-            if constexpr (WK == 1) y[row_raw(i)] = acc;
+            if constexpr (WK == 1 && !SW) y[row_raw(i)] = acc;
             else part[i * WK + kq] = acc;
         }
     };
 
-    u32x4 Ra[NL], Rb[NL];
-    int ia, ib, i0, d0, d1, da, db;
-    {
-        // three rows requested before the first is committed (XQ: after the
-        // loads of x; the rows stream in while the workgroup quantises x)
-        f32x4 xv[4];
-        if (XQ) xq_load<DWG>(ai.x, 32 * nbw, 0, xv);
-        __builtin_amdgcn_sched_barrier(0);
-        u32x4 Rc[NL];
-        const int ic = grab();
-        const int dc = stage(Rc, row_of(ic));
-        __builtin_amdgcn_sched_barrier(0);
-        ia = grab();
-        da = stage(Ra, row_of(ia));
-        __builtin_amdgcn_sched_barrier(0);
-        ib = grab();
-        db = stage(Rb, row_of(ib));
-        __builtin_amdgcn_sched_barrier(0);
-        if (XQ) xq_prologue<DWG>(ss, ai, nbw, Kp, xv, aq, ad, as);
-        commit(Rc, dc, buf0);
-        d0 = dc;
-        i0 = ic;
+    if constexpr (PAIRS) {
+        // rows go in pairs of consecutive indices (one LDS atomic per pair;
+        // pools and their row groups have even sizes, so a pair never
+        // straddles the end of the pool); two pairs are in flight while a
+        // third is computed, its two dots interleaved
+        auto grab2_issue = [&]() {
+            int v = 0;
+            if (lane == 0) v = atomicAdd(&cnt[kq], 2);
+            return v;
+        };
+        u32x4 A0[NL], B0[NL], A1[NL], B1[NL];
+        int j0, j1, dA0, dB0, dA1, dB1;
+        {
+            // four rows requested before the first is committed (XQ: after
+            // the loads of x; the rows stream in while x is quantised)
+            f32x4 xv[4];
+            if (XQ) xq_load<DWG>(ai.x, 32 * nbw, 0, xv);
+            __builtin_amdgcn_sched_barrier(0);
+            j0 = take(grab2_issue());
+            dA0 = stage(A0, row_of(j0));
+            dB0 = stage(B0, row_of(j0 + 1));
+            __builtin_amdgcn_sched_barrier(0);
+            j1 = take(grab2_issue());
+            dA1 = stage(A1, row_of(j1));
+            dB1 = stage(B1, row_of(j1 + 1));
+            __builtin_amdgcn_sched_barrier(0);
+            if (XQ) xq_prologue<DWG>(ss, ai, nbw, Kp, xv, aq, ad, as);
+        }
+        int tn = grab2_issue();   // the pair after j1, in flight
+        // a wave's indices increase, so once one is past the pool all later are
+        while (j0 < pool_n) {
+            commit(A0, dA0, buf0);
+            commit(B0, dB0, buf1);
+            const int c0 = j0, e0 = dA0, f0 = dB0;
+            j0 = take(tn);
+            tn = grab2_issue();
+            dA0 = stage(A0, row_of(j0));
+            dB0 = stage(B0, row_of(j0 + 1));
+            __builtin_amdgcn_sched_barrier(0);
+            {
+                float s0, s1;
+                ss.dot2(buf0, e0, buf1, f0, s0, s1);
+                finish_row(s0, c0);
+                finish_row(s1, c0 + 1);
+            }
+            if (j1 >= pool_n) break;
+            commit(A1, dA1, buf0);
+            commit(B1, dB1, buf1);
+            const int c1 = j1, e1 = dA1, f1 = dB1;
+            j1 = take(tn);
+            tn = grab2_issue();
+            dA1 = stage(A1, row_of(j1));
+            dB1 = stage(B1, row_of(j1 + 1));
+            __builtin_amdgcn_sched_barrier(0);
+            {
+                float s0, s1;
+                ss.dot2(buf0, e1, buf1, f1, s0, s1);
+                finish_row(s0, c1);
+                finish_row(s1, c1 + 1);
+            }
+        }
+    } else {
+        u32x4 Ra[NL], Rb[NL];
+        int ia, ib, i0, d0, d1, da, db;
+        {
+            // three rows requested before the first is committed (XQ: after the
+            // loads of x; the rows stream in while the workgroup quantises x)
+            f32x4 xv[4];
+            if (XQ) xq_load<DWG>(ai.x, 32 * nbw, 0, xv);
+            __builtin_amdgcn_sched_barrier(0);
+            u32x4 Rc[NL];
+            const int ic = grab();
+            const int dc = stage(Rc, row_of(ic));
+            __builtin_amdgcn_sched_barrier(0);
+            ia = grab();
+            da = stage(Ra, row_of(ia));
+            __builtin_amdgcn_sched_barrier(0);
+            ib = grab();
+            db = stage(Rb, row_of(ib));
+            __builtin_amdgcn_sched_barrier(0);
+            if (XQ) xq_prologue<DWG>(ss, ai, nbw, Kp, xv, aq, ad, as);
+            commit(Rc, dc, buf0);
+            d0 = dc;
+            i0 = ic;
+        }
+        int tn = grab_issue();   // the index after ib, in flight
+        // a wave's indices increase, so once one is past the pool all later are
+        while (i0 < pool_n) {
+            finish_row(dot_row(buf0, d0), i0);
+            commit(Ra, da, buf1);
+            d1 = da;
+            const int i1 = ia;
+            ia = take(tn);
+            tn = grab_issue();
+            da = stage(Ra, row_of(ia));
+            __builtin_amdgcn_sched_barrier(0);
+            if (i1 < pool_n) finish_row(dot_row(buf1, d1), i1);
+            commit(Rb, db, buf0);
+            d0 = db;
+            i0 = ib;
+            ib = take(tn);
+            tn = grab_issue();
+            db = stage(Rb, row_of(ib));
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
-    int tn = grab_issue();   // the index after ib, in flight
-    // a wave's indices increase, so once one is past the pool all later are
-    while (i0 < pool_n) {
-        finish_row(dot_row(buf0, d0), i0);
-        commit(Ra, da, buf1);
-        d1 = da;
-        const int i1 = ia;
-        ia = take(tn);
-        tn = grab_issue();
-        da = stage(Ra, row_of(ia));
-        __builtin_amdgcn_sched_barrier(0);
-        if (i1 < pool_n) finish_row(dot_row(buf1, d1), i1);
-        commit(Rb, db, buf0);
-        d0 = db;
-        i0 = ib;
-        ib = take(tn);
-        tn = grab_issue();
-        db = stage(Rb, row_of(ib));
-        __builtin_amdgcn_sched_barrier(0);
-    }
-    if constexpr (WK > 1) {
+    if constexpr (SW) {
+        __syncthreads();
+        swiglu_epilogue<DWG, WK>(part, hseg, nblk, b, G, so);
+    } else if constexpr (WK > 1) {
         __syncthreads();
         for (int i = threadIdx.x; i < pool_n; i += DWG) {
             if (row_raw(i) < N) {
@@ -1184,31 +1301,48 @@ static int cu_count() {
 // The dynamic-row kernel: one workgroup per compute unit.  Returns
 // hipErrorNotSupported (nothing launched) where its slice buffers, the
 // activation row and the partial sums would not fit in 64 KB of LDS.
-template <int FMT, int UPL, int WK, int NL, bool XQ>
-static hipError_t launch_dyn_cfg(const GemvArgs& a, const ActIn& ai, int U, int US, int buf_bytes,
-                                 hipStream_t st) {
+// Slices of at most this many bytes go through the dynamic-row kernel two
+// rows at a time per wave (four rows in flight instead of two).  Measured on
+// MI355X: the 2304-byte rows of the fused gate|up product ran ~1 us faster
+// in pairs; the 3360-byte rows of the lm_head ran ~2.5 us slower (eight waves
+// with two of its rows in flight each already keep ~54 KB per unit in
+// flight).
+constexpr int kDynPairMaxSlice = 3072;
+
+template <int FMT, int UPL, int WK, int NL, bool XQ, bool SW>
+static hipError_t launch_dyn_cfg(const GemvArgs& a, const SwigluOut& so, const ActIn& ai, int U,
+                                 int US, int buf_bytes, hipStream_t st) {
     const int cus = cu_count();
-    const int64_t ngr = (a.N + DRG - 1) / DRG;
-    const int64_t grid = ngr < cus ? ngr : cus;
-    const int64_t pool_cap = (ngr + grid - 1) / grid * DRG;
+    // work items: row groups of DRG, or (SW) output blocks of 64 rows
+    const int64_t items = SW ? so.nh / 32 : (a.N + DRG - 1) / DRG;
+    const int64_t grid = items < cus ? items : cus;
+    const int64_t per_wg = (items + grid - 1) / grid;
+    const int64_t pool_cap = per_wg * (SW ? 64 : DRG);
     const int Kp = (int)((a.K + 255) / 256 * 256);
     const int64_t smem = 2 * DW * (int64_t)buf_bytes + (XQ ? act_lds_bytes(Kp) : 0) +
-                         (WK > 1 ? pool_cap * WK * 4 : 0);
+                         (WK > 1 || SW ? pool_cap * WK * 4 : 0) + (SW ? per_wg * 32 * 4 : 0);
     if (smem > 65536 - 64) return hipErrorNotSupported;
-    hipLaunchKernelGGL((k_gemv_dyn<FMT, UPL, WK, NL, XQ>), dim3((unsigned)grid), dim3(DWG),
-                       (unsigned)smem, st, (const uint8_t*)a.w, (int)a.N, U, US, (int)(a.K / 32),
-                       row_bytes_of(FMT, a.K), buf_bytes, a.q, a.d, a.s, a.y, ai);
+    if (buf_bytes - 32 <= kDynPairMaxSlice)
+        hipLaunchKernelGGL((k_gemv_dyn<FMT, UPL, WK, NL, XQ, SW, true>), dim3((unsigned)grid),
+                           dim3(DWG), (unsigned)smem, st, (const uint8_t*)a.w, (int)a.N, U, US,
+                           (int)(a.K / 32), row_bytes_of(FMT, a.K), buf_bytes, a.q, a.d, a.s, a.y,
+                           so, ai);
+    else
+        hipLaunchKernelGGL((k_gemv_dyn<FMT, UPL, WK, NL, XQ, SW, false>), dim3((unsigned)grid),
+                           dim3(DWG), (unsigned)smem, st, (const uint8_t*)a.w, (int)a.N, U, US,
+                           (int)(a.K / 32), row_bytes_of(FMT, a.K), buf_bytes, a.q, a.d, a.s, a.y,
+                           so, ai);
     return hipGetLastError();
 }
 
-template <int FMT, int UPL, int WK, bool XQ>
+template <int FMT, int UPL, int WK, bool XQ, bool SW>
 static hipError_t launch_dyn_wk(const GemvArgs& a, int U, const SliceGeom& g, hipStream_t st,
-                                const ActIn& ai) {
+                                const SwigluOut& so, const ActIn& ai) {
     const int buf_bytes = 16 * g.nchunk + 16;
     const int nl = (g.nchunk + 63) / 64;
-    if (nl <= 2) return launch_dyn_cfg<FMT, UPL, WK, 2, XQ>(a, ai, U, g.US, buf_bytes, st);
-    if (nl <= 3) return launch_dyn_cfg<FMT, UPL, WK, 3, XQ>(a, ai, U, g.US, buf_bytes, st);
-    if (nl <= 4) return launch_dyn_cfg<FMT, UPL, WK, 4, XQ>(a, ai, U, g.US, buf_bytes, st);
+    if (nl <= 2) return launch_dyn_cfg<FMT, UPL, WK, 2, XQ, SW>(a, so, ai, U, g.US, buf_bytes, st);
+    if (nl <= 3) return launch_dyn_cfg<FMT, UPL, WK, 3, XQ, SW>(a, so, ai, U, g.US, buf_bytes, st);
+    if (nl <= 4) return launch_dyn_cfg<FMT, UPL, WK, 4, XQ, SW>(a, so, ai, U, g.US, buf_bytes, st);
     return hipErrorNotSupported;
 }
 
@@ -1222,15 +1356,15 @@ constexpr int kDynRowsPerCu = 256;
 template <int FMT, bool SW, bool XQ>
 static hipError_t launch_lds_fmt(const GemvArgs& a, int U, const SliceGeom& g, hipStream_t st,
                                  const SwigluOut& so, const ActIn& ai) {
-    if constexpr (!SW) {
-        if (a.N >= (int64_t)kDynRowsPerCu * cu_count()) {
-            hipError_t e = hipErrorNotSupported;
-            if (U > 256) e = launch_dyn_wk<FMT, 2, 4, XQ>(a, U, g, st, ai);
-            else if (U > 128) e = launch_dyn_wk<FMT, 1, 4, XQ>(a, U, g, st, ai);
-            else if (U > 64) e = launch_dyn_wk<FMT, 1, 2, XQ>(a, U, g, st, ai);
-            else e = launch_dyn_wk<FMT, 1, 1, XQ>(a, U, g, st, ai);
-            if (e != hipErrorNotSupported) return e;
-        }
+    // the fused gate|up product always tries the dynamic-row kernel (whole
+    // output blocks per unit, shared by its 8 waves)
+    if (SW || a.N >= (int64_t)kDynRowsPerCu * cu_count()) {
+        hipError_t e = hipErrorNotSupported;
+        if (U > 256) e = launch_dyn_wk<FMT, 2, 4, XQ, SW>(a, U, g, st, so, ai);
+        else if (U > 128) e = launch_dyn_wk<FMT, 1, 4, XQ, SW>(a, U, g, st, so, ai);
+        else if (U > 64) e = launch_dyn_wk<FMT, 1, 2, XQ, SW>(a, U, g, st, so, ai);
+        else e = launch_dyn_wk<FMT, 1, 1, XQ, SW>(a, U, g, st, so, ai);
+        if (e != hipErrorNotSupported) return e;
     }
     if (U > 256) return launch_lds_wk<FMT, 2, 4, SW, XQ>(a, U, g, st, so, ai);
     if (U > 128) return launch_lds_wk<FMT, 1, 4, SW, XQ>(a, U, g, st, so, ai);

@@ -77,21 +77,43 @@ __device__ __forceinline__ QBlockL<L> quantize_block(const float (&v)[32 / L]) {
         // |x / d32| <= 127.01 -- of the correctly rounded quotient, so both
         // round to the same integer unless the product lies within 2^-13 of a
         // boundary k + 1/2 (where rint's ties-to-even would also differ from
-        // rounding half away).  There, and when 1 / d32 would leave the
-        // normal range, the lane divides instead.  Either way q is the
-        // rounding of the correctly rounded quotient.
+        // rounding half away).  Such a value (about one in 4096), or every
+        // value of a block whose 1 / d32 would leave the normal range, is
+        // divided instead.  A lane almost never holds two such values, so the
+        // one it holds is selected, divided once and put back, in straight-
+        // line code (taken branches around each value's division cost a wave
+        // ~0.7 us); lanes with more go through every value.  Either way q is
+        // the rounding of the correctly rounded quotient.
+        constexpr float kBand = 0.5f - 0x1p-13f;
         const float rcp = __builtin_amdgcn_rcpf(d32);
-        bool divide = !(d32 >= 0x1p-120f && d32 <= 0x1p120f);
-        float qf[V];
+        const bool ranged = d32 >= 0x1p-120f && d32 <= 0x1p120f;
+        float qf[V], y[V];
+        float far = 0.0f;   // largest distance to the nearest integer
 #pragma unroll
         for (int k = 0; k < V; k++) {
-            const float y = v[k] * rcp;
-            qf[k] = __builtin_rintf(y);
-            divide |= fabsf(y - qf[k]) >= 0.5f - 0x1p-13f;   // an exact difference
+            y[k] = v[k] * rcp;
+            qf[k] = __builtin_rintf(y[k]);
+            far = fmaxf(far, fabsf(y[k] - qf[k]));   // an exact difference
         }
-        if (divide) {
+        if (!ranged || far >= kBand) {
+            bool f[V];
+            int nflag = 0;
+            float vs = 0.0f;
 #pragma unroll
-            for (int k = 0; k < V; k++) qf[k] = roundf(v[k] / d32);
+            for (int k = 0; k < V; k++) {
+                f[k] = !ranged || fabsf(y[k] - qf[k]) >= kBand;
+                nflag += f[k] ? 1 : 0;
+                vs = f[k] ? v[k] : vs;
+            }
+            if (nflag == 1) {
+                const float qd = roundf(vs / d32);
+#pragma unroll
+                for (int k = 0; k < V; k++) qf[k] = f[k] ? qd : qf[k];
+            } else {
+#pragma unroll
+                for (int k = 0; k < V; k++)
+                    if (f[k]) qf[k] = roundf(v[k] / d32);
+            }
         }
 #pragma unroll
         for (int k = 0; k < V; k++) {

@@ -154,7 +154,7 @@ def swiglu_fused_x(qg, wd, N, K, xd):
 
 
 @pytest.mark.parametrize("N,K", [(32, 256), (96, 896), (320, 4096), (64, 4864), (544, 1024),
-                                 (160, 14336)])
+                                 (160, 14336), (8256, 2048), (24736, 512)])
 def test_quantize_swiglu_shapes(qg, N, K):
     g = np.random.default_rng(N * 11 + K)
     w = synth.q4_k_weights(g, 2 * N, K)

@@ -69,8 +69,10 @@ def check_against_oracle(w, N, K, act, out, gu, h):
     assert np.array_equal(so.reshape(-1), rs.reshape(-1))
 
 
+# N = 8256 and 24736 give a workgroup of the dynamic-row kernel two and up
+# to four output blocks (one unit per 256 blocks), with a ragged remainder
 @pytest.mark.parametrize("N,K", [(32, 256), (96, 896), (320, 4096), (64, 4864), (160, 32768),
-                                 (544, 1024), (1056, 2048)])
+                                 (544, 1024), (1056, 2048), (8256, 2048), (24736, 512)])
 def test_fused_shapes(qg, N, K):
     g = np.random.default_rng(N * 7 + K)
     w = synth.q4_k_weights(g, 2 * N, K)
