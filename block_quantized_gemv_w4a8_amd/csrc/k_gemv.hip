@@ -131,39 +131,52 @@ struct ActReg<QGEMV_FMT_Q8_0> {
 
 // An fp32 activation row quantised by the whole workgroup into LDS: codes
 // aq [Kp], fp16 scale bits ad [Kp/32] and code sums as [Kp/32], blocks past K
-// zero.  The block quantiser is the one of k_quantize_act with 2 lanes per
-// block of 32 (16 consecutive values each) instead of 8: max and sum are
-// exact, so the bits are the same, and the per-block work (max, scale, sum)
-// is shared by 16 values per lane.  One pass covers 128 blocks; each load's
-// address is clamped into x and half-blocks past K are masked to zero.  The
-// first pass's loads are issued by the caller (xq_load) ahead of its weight
-// loads.
+// zero.  The block quantiser is the one of k_quantize_act with XqLanes<NTH>
+// lanes per block of 32 (2 for 256 threads, 4 for 512: 16 or 8 consecutive
+// values each) instead of 8: max and sum are exact, so the bits are the
+// same, and the per-block work (max, scale, sum) is shared by the lane's
+// values.  One pass covers NTH / XqLanes blocks (128 at both sizes, so every
+// thread has values at K = 4096); each load's address is clamped into x and
+// lane parts past K are masked to zero.  The first pass's loads are issued by
+// the caller (xq_load) ahead of its weight loads.
+template <int NTH>
+constexpr int XqLanes = NTH >= 512 ? 4 : 2;
+template <int NTH>
+constexpr int XqLoads = 32 / XqLanes<NTH> / 4;   // f32x4 loads per lane and pass
+
 template <int NTH = WG>
 __device__ __forceinline__ void xq_load(const float* __restrict__ x, int K, int b0,
-                                        f32x4 (&v)[4]) {
-    const int e = 32 * (b0 + (threadIdx.x >> 1)) + 16 * (threadIdx.x & 1);
+                                        f32x4 (&v)[XqLoads<NTH>]) {
+    constexpr int L = XqLanes<NTH>;
+    const int e = 32 * (b0 + (int)threadIdx.x / L) + (32 / L) * ((int)threadIdx.x % L);
 #pragma unroll
-    for (int k = 0; k < 4; k++) v[k] = *reinterpret_cast<const f32x4*>(x + min(e + 4 * k, K - 4));
+    for (int k = 0; k < XqLoads<NTH>; k++)
+        v[k] = *reinterpret_cast<const f32x4*>(x + min(e + 4 * k, K - 4));
 }
 
 template <int NTH = WG>
-__device__ __forceinline__ void xq_batch(const f32x4 (&v)[4], int K, int nb, int b0, int8_t* aq,
-                                         uint16_t* ad, int32_t* as) {
-    const int b = b0 + (threadIdx.x >> 1), half = threadIdx.x & 1;
-    const int e = 32 * b + 16 * half;
+__device__ __forceinline__ void xq_batch(const f32x4 (&v)[XqLoads<NTH>], int K, int nb, int b0,
+                                         int8_t* aq, uint16_t* ad, int32_t* as) {
+    constexpr int L = XqLanes<NTH>, V = 32 / L;
+    const int b = b0 + (int)threadIdx.x / L, part = (int)threadIdx.x % L;
+    const int e = 32 * b + V * part;
     const bool in = e < K;
-    float vv[16];
+    float vv[V];
 #pragma unroll
-    for (int k = 0; k < 4; k++) {
+    for (int k = 0; k < V / 4; k++) {
         vv[4 * k] = in ? v[k].x : 0.0f;
         vv[4 * k + 1] = in ? v[k].y : 0.0f;
         vv[4 * k + 2] = in ? v[k].z : 0.0f;
         vv[4 * k + 3] = in ? v[k].w : 0.0f;
     }
-    const QBlockL<2> r = quantize_block<2>(vv);
+    const QBlockL<L> r = quantize_block<L>(vv);
     if (b < nb) {
-        *reinterpret_cast<u32x4*>(aq + e) = u32x4{r.packed[0], r.packed[1], r.packed[2], r.packed[3]};
-        if (half == 0) {
+        if constexpr (L == 2)
+            *reinterpret_cast<u32x4*>(aq + e) =
+                u32x4{r.packed[0], r.packed[1], r.packed[2], r.packed[3]};
+        else
+            *reinterpret_cast<uint2*>(aq + e) = uint2{r.packed[0], r.packed[1]};
+        if (part == 0) {
             ad[b] = (uint16_t)r.dbits;
             as[b] = r.sum;
         }
@@ -172,13 +185,13 @@ __device__ __forceinline__ void xq_batch(const f32x4 (&v)[4], int K, int nb, int
 
 template <int NTH = WG>
 __device__ __forceinline__ void quantize_row_lds(const float* __restrict__ x, int K, int Kp,
-                                                 const f32x4 (&first)[4], int8_t* aq,
+                                                 const f32x4 (&first)[XqLoads<NTH>], int8_t* aq,
                                                  uint16_t* ad, int32_t* as) {
     const int nb = Kp / 32;
-    constexpr int BATCH = NTH / 2;   // blocks per pass
+    constexpr int BATCH = NTH / XqLanes<NTH>;   // blocks per pass
     xq_batch<NTH>(first, K, nb, 0, aq, ad, as);
     for (int b0 = BATCH; b0 < nb; b0 += BATCH) {
-        f32x4 v[4];
+        f32x4 v[XqLoads<NTH>];
         xq_load<NTH>(x, K, b0, v);
         xq_batch<NTH>(v, K, nb, b0, aq, ad, as);
     }
@@ -407,7 +420,7 @@ __global__ __launch_bounds__(WG) void k_gemv(const uint8_t* __restrict__ w, int 
         if constexpr (XQ) {
             if (p0 == 0) {
                 // the first row's weights are on their way; quantise x
-                f32x4 xv[4];
+                f32x4 xv[XqLoads<WG>];
                 xq_load(ai.x, 32 * nbw, 0, xv);
                 quantize_row_lds(ai.x, 32 * nbw, Kp, xv, aq, ad, as);
                 __syncthreads();
@@ -636,8 +649,8 @@ struct SliceStream {
 // and workgroup 0 writes the codes out.  Called by every thread.
 template <int NTH, class SS>
 __device__ __forceinline__ void xq_prologue(SS& ss, const ActIn& ai, int nbw, int Kp,
-                                            const f32x4 (&xv)[4], int8_t* aq, uint16_t* ad,
-                                            int32_t* as) {
+                                            const f32x4 (&xv)[XqLoads<NTH>], int8_t* aq,
+                                            uint16_t* ad, int32_t* as) {
     quantize_row_lds<NTH>(ai.x, 32 * nbw, Kp, xv, aq, ad, as);
     __syncthreads();
     ss.load_act(aq, ad, as);
@@ -785,7 +798,7 @@ __global__ __launch_bounds__(WG) void k_gemv_lds(const uint8_t* __restrict__ w, 
             // the loads of x, which is what the waves wait for first; the
             // rows stream in while the workgroup quantises x)
             const bool xq = XQ && p0 == 0;
-            f32x4 xv[4];
+            f32x4 xv[XqLoads<WG>];
             if (xq) xq_load(ai.x, 32 * nbw, 0, xv);
             __builtin_amdgcn_sched_barrier(0);
             u32x4 Rc[NL];
@@ -938,7 +951,7 @@ __global__ __launch_bounds__(DWG) void k_gemv_dyn(const uint8_t* __restrict__ w,
         {
             // four rows requested before the first is committed (XQ: after
             // the loads of x; the rows stream in while x is quantised)
-            f32x4 xv[4];
+            f32x4 xv[XqLoads<DWG>];
             if (XQ) xq_load<DWG>(ai.x, 32 * nbw, 0, xv);
             __builtin_amdgcn_sched_barrier(0);
             j0 = take(grab2_issue());
@@ -990,7 +1003,7 @@ __global__ __launch_bounds__(DWG) void k_gemv_dyn(const uint8_t* __restrict__ w,
         {
             // three rows requested before the first is committed (XQ: after the
             // loads of x; the rows stream in while the workgroup quantises x)
-            f32x4 xv[4];
+            f32x4 xv[XqLoads<DWG>];
             if (XQ) xq_load<DWG>(ai.x, 32 * nbw, 0, xv);
             __builtin_amdgcn_sched_barrier(0);
             u32x4 Rc[NL];
