@@ -307,7 +307,7 @@ constexpr int kXqShortKp = 2048;
 // matrix m (selected without indexing the argument arrays by lane).
 template <int FMT, int LPR, int UPL, int WK, bool XQ, bool MULTI>
 __global__ __launch_bounds__(WG) void k_gemv(const uint8_t* __restrict__ w, int N, int U,
-                                              int nbw, int row_bytes,
+                                              int US, int nbw, int row_bytes,
                                               const int8_t* __restrict__ q,
                                               const uint16_t* __restrict__ d,
                                               const int32_t* __restrict__ s,
@@ -356,7 +356,6 @@ __global__ __launch_bounds__(WG) void k_gemv(const uint8_t* __restrict__ w, int 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int kq = wave % WK, rg = wave / WK;
     const int li = lane % LPR, sub = lane / LPR;
-    const int US = (U + WK - 1) / WK;
     const int u_lo = kq * US;
     const int u_hi = min(U, u_lo + US);
 
@@ -1150,6 +1149,18 @@ static int units_of(int fmt, int64_t K) {
 
 // Workgroups of one kernel instantiation that fit on the device at once
 // (occupancy x compute units), cached per device.
+// Units per split-K slice, the same in every kernel so that a row's slice
+// sums, and so its bits, do not depend on the kernel: slices of the K-quant
+// formats start at super-block boundaries, those of the repacked Q6_K at
+// tile boundaries.
+template <int FMT>
+static int slice_units(int U, int WK) {
+    int us = (U + WK - 1) / WK;
+    if (FMT == QGEMV_FMT_Q4_K || FMT == QGEMV_FMT_Q6_K) us = (us + 3) / 4 * 4;
+    if (FMT == QGEMV_FMT_Q6_K_R8) us = (us + 31) / 32 * 32;
+    return us;
+}
+
 template <int FMT, int LPR, int UPL, int WK, bool XQ = false, bool MULTI = false>
 static int resident_workgroups() {
     static std::atomic<int> cache[64];
@@ -1158,9 +1169,8 @@ static int resident_workgroups() {
     int v = cache[dev].load(std::memory_order_relaxed);
     if (v > 0) return v;
     int per_cu = 0, cus = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_gemv<FMT, LPR, UPL, WK, XQ, MULTI>,
-                                                     WG, 0) !=
-            hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, k_gemv<FMT, LPR, UPL, WK, XQ, MULTI>, WG, 0) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         per_cu <= 0 || cus <= 0) {
         (void)hipGetLastError();
@@ -1182,8 +1192,8 @@ static hipError_t launch_gemv_cfg(const GemvArgs& a, int U, hipStream_t st,
     const int64_t passes = (ngroups + resident - 1) / resident;
     const int64_t grid = (ngroups + passes - 1) / passes;
     hipLaunchKernelGGL((k_gemv<FMT, LPR, UPL, WK, XQ, MULTI>), dim3((unsigned)grid), dim3(WG), 0,
-                       st, (const uint8_t*)a.w, (int)a.N, U, (int)(a.K / 32),
-                       row_bytes_of(FMT, a.K), a.q, a.d, a.s, a.y, ai, mr);
+                       st, (const uint8_t*)a.w, (int)a.N, U, slice_units<FMT>(U, WK),
+                       (int)(a.K / 32), row_bytes_of(FMT, a.K), a.q, a.d, a.s, a.y, ai, mr);
     return hipGetLastError();
 }
 
@@ -1248,12 +1258,9 @@ struct SliceGeom {
 
 template <int FMT>
 static SliceGeom slice_geom(int64_t K, int U, int WK) {
-    const bool kq = (FMT == QGEMV_FMT_Q4_K || FMT == QGEMV_FMT_Q6_K);
     const int rb = row_bytes_of(FMT, K);
     SliceGeom g;
-    g.US = (U + WK - 1) / WK;
-    if (kq) g.US = (g.US + 3) / 4 * 4;  // slices start at super-block boundaries
-    if (FMT == QGEMV_FMT_Q6_K_R8) g.US = (g.US + 31) / 32 * 32;  // ... at tile boundaries
+    g.US = slice_units<FMT>(U, WK);
     g.nchunk = 0;
     for (int k = 0; k < WK; k++) {
         const int lo = k * g.US;
@@ -1385,9 +1392,21 @@ static hipError_t launch_lds_fmt(const GemvArgs& a, int U, const SliceGeom& g, h
     return launch_lds_wk<FMT, 1, 1, SW, XQ>(a, U, g, st, so, ai);
 }
 
+// Repacked Q6_K rows of 129 to 256 units (split-K over 4 waves) that are too
+// few to take the dynamic-row kernel go through the direct-load kernel: the
+// repacked fields load per lane as aligned 16-byte pieces, and as many
+// workgroups as fit keep the units busy.  Measured on MI355X (the 4096 x
+// 14336 down product in the decode step, same box): 11.2-11.3 us against
+// 11.8-11.9 us through LDS (same slices, same bits); with a third row buffer
+// (two rows in flight) 12.7 us.
+constexpr bool kDirectR8Long = true;
+
 template <int FMT>
 static hipError_t launch_gemv_fmt(const GemvArgs& a, hipStream_t st) {
     const int U = units_of(FMT, a.K);
+    if (FMT == QGEMV_FMT_Q6_K_R8 && kDirectR8Long && U > 128 && U <= 256 &&
+        a.N < (int64_t)kDynRowsPerCu * cu_count())
+        return launch_gemv_cfg<FMT, 64, 1, 4>(a, U, st);
     if (kLdsStream && U > 32) {
         const SliceGeom g = slice_geom<FMT>(a.K, U, lds_wk(U));
         if (lds_slice_fits<FMT>(g)) return launch_lds_fmt<FMT, false, false>(a, U, g, st, {}, {});
