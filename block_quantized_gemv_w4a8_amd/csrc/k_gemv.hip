@@ -844,7 +844,8 @@ __global__ __launch_bounds__(WG) void k_gemv_lds(const uint8_t* __restrict__ w, 
 
 // Dynamic-row LDS-streaming GEMV: one workgroup of DW = 8 waves per compute
 // unit, the same per-row work as k_gemv_lds, but the rows of a workgroup are
-// handed to its waves one at a time from a counter in LDS.  With two
+// handed to its waves from a counter in LDS, one at a time or (PAIRS, short
+// slices) two consecutive ones, whose dots are computed together.  With two
 // 4-wave workgroups per compute unit and a fixed share each, the workgroup
 // dispatched first ran 16-36% faster than its co-resident twin (its waves
 // are older and win the issue arbitration), and the unit finished with the
@@ -864,7 +865,7 @@ __global__ __launch_bounds__(WG) void k_gemv_lds(const uint8_t* __restrict__ w, 
 // its one or two blocks until the last row.
 constexpr int DW = 8;           // waves of a dynamic-row workgroup
 constexpr int DWG = 64 * DW;    // its threads
-constexpr int DRG = 8;          // rows per row group of the static split (even: rows go in pairs)
+constexpr int DRG = 8;          // rows per row group of the static split
 static_assert(DRG % 2 == 0, "pairs of rows stay inside a row group");
 
 template <int FMT, int UPL, int WK, int NL, bool XQ, bool SW, bool PAIRS>
