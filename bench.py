@@ -35,6 +35,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+SMALL_M_LIST = (1, 2, 4, 8, 16, 24, 32, 48, 64)
 METRIC = "quantized GEMV weight GB/s and % of HBM peak at Llama-3-8B shapes, 1 GPU"
 WORKLOAD = ("llama3.1-8b decode step, batch 1: ffn gate|up q4_k 28672x4096 with fused "
             "silu*up requant -> down q6_k 4096x14336, then lm_head q6_k 128256x4096 "
@@ -319,31 +320,33 @@ def main():
 
 
 def small_m_profile(qg, torch, np, synth, dev):
-    """The small-M MFMA products alone, for rocprofv3 counter passes."""
+    """The small-M products alone (both variants, every M of SMALL_M_LIST,
+    20 calls each, in this order), for rocprofv3 counter passes."""
     g = np.random.default_rng(4)
     for fmt, N, K in (("q4_k", 14336, 4096), ("q6_k", 4096, 14336)):
         w = torch.from_numpy(synth.weights(fmt, g, N, K)).to(dev)
         x64, _ = synth.activation(g, 64, K)
-        for M in (8, 64):
+        for M in SMALL_M_LIST:
             q, d, s = qg.act_buffers(M, K, dev)
             qg.qgemv_quantize_act(torch.from_numpy(np.ascontiguousarray(x64[:M])).to(dev), M, K, K,
                                   q, d, s)
             y = torch.empty((M, N), dtype=torch.float32, device=dev)
-            for _ in range(20):
-                qg.SMALL_M[fmt](w, N, K, M, q, d, s, y, qg.QGEMV_VARIANT_MFMA)
-            torch.cuda.synchronize()
+            for v in (qg.QGEMV_VARIANT_DOT4, qg.QGEMV_VARIANT_MFMA):
+                for _ in range(20):
+                    qg.SMALL_M[fmt](w, N, K, M, q, d, s, y, v)
+                torch.cuda.synchronize()
             log(f"[small-m-profile] {fmt} {N}x{K} M={M} done")
 
 
-def time_kernel(torch, fn, iters, R):
-    """Microseconds per launch of fn(i): the best of three windows of `iters`
+def kernel_stats(torch, fn, iters, R, windows=5):
+    """Microseconds per launch of fn(i) over `windows` windows of `iters`
     back-to-back launches (events around each window), after `iters` warm-up
-    launches."""
+    launches: median, min and max of the windows."""
     for i in range(iters):
         fn(i % R)
     torch.cuda.synchronize()
-    best = float("inf")
-    for _ in range(3):
+    per = []
+    for _ in range(windows):
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
         a.record()
@@ -351,8 +354,15 @@ def time_kernel(torch, fn, iters, R):
             fn(i % R)
         b.record()
         torch.cuda.synchronize()
-        best = min(best, a.elapsed_time(b) * 1e3 / iters)
-    return best
+        per.append(a.elapsed_time(b) * 1e3 / iters)
+    per.sort()
+    return {"us": round(per[len(per) // 2], 2), "us_min": round(per[0], 2),
+            "us_max": round(per[-1], 2)}
+
+
+def time_kernel(torch, fn, iters, R):
+    """The median of kernel_stats (microseconds per launch)."""
+    return kernel_stats(torch, fn, iters, R)["us"]
 
 
 def graph_time(torch, calls, reps=20):
@@ -513,11 +523,13 @@ def extras(qg, torch, np, synth, dev, R, c2, c3, args):
         qg.qgemv_quantize_act(torch.from_numpy(x).to(dev), 1, K, K, q, d, s)
         y = torch.empty(N, dtype=torch.float32, device=dev)
         f = qg.GEMV[fmt]
-        us = time_kernel(torch, lambda c: f(ws[c], N, K, q, d, s, y), 100, copies)
+        st = kernel_stats(torch, lambda c: f(ws[c], N, K, q, d, s, y), 100, copies)
+        us = st["us"]
         wb = synth.logical_bytes(fmt.replace("_r8", ""), N, K)
         del ws
-        return {"us": round(us, 2), "weight_GBps": round(wb / us / 1e3, 1),
-                "hbm_frac": round(wb / us / 1e3 / HBM_PEAK_GBPS, 4), "calls_per_s": round(1e6 / us)}
+        return {**st, "weight_GBps": round(wb / us / 1e3, 1),
+                "hbm_frac": round(wb / us / 1e3 / HBM_PEAK_GBPS, 4), "calls_per_s": round(1e6 / us),
+                "weight_copies_rotated": copies}
 
     ex["gate_up_q4_k_28672x4096"] = gemv_case("q4_k", c2["w_gu"], Ngu, Kgu, c2["x"], 8)
     # the same product with SiLU*up and the requantisation fused in (one launch)
@@ -605,7 +617,7 @@ def extras(qg, torch, np, synth, dev, R, c2, c3, args):
     for _ in range(15):
         w4.append(w4[0].clone())
     sm = {}
-    for M in (1, 2, 4, 8, 16, 32, 64):
+    for M in SMALL_M_LIST:
         xm = torch.from_numpy(np.ascontiguousarray(c4["x64"][:M])).to(dev)
         qm, dm, smm = qg.act_buffers(M, K4, dev)
         qg.qgemv_quantize_act(xm, M, K4, K4, qm, dm, smm)
@@ -627,7 +639,17 @@ def extras(qg, torch, np, synth, dev, R, c2, c3, args):
         # int8 MACs of the product over the measured time, against the dense int8 peak
         sm[f"M{M}_mfma_int8_TOPS"] = round(2 * M * N4 * K4 / sm[f"M{M}_mfma_us"] / 1e6, 1)
     sm["crossover_M_mfma_faster_from"] = next(
-        (M for M in (1, 2, 4, 8, 16, 32, 64) if sm[f"M{M}_mfma_us"] < sm[f"M{M}_dot4_us"]), None)
+        (M for M in SMALL_M_LIST if sm[f"M{M}_mfma_us"] < sm[f"M{M}_dot4_us"]), None)
+    # one weight copy read again and again (33 MB stays in the Infinity Cache):
+    # the cache-resident figure, labelled as such
+    for M in (8, 64):
+        xm = torch.from_numpy(np.ascontiguousarray(c4["x64"][:M])).to(dev)
+        qm, dm, smm = qg.act_buffers(M, K4, dev)
+        qg.qgemv_quantize_act(xm, M, K4, K4, qm, dm, smm)
+        ym = torch.empty((M, N4), dtype=torch.float32, device=dev)
+        sm[f"M{M}_mfma_cache_resident_single_copy_us"] = round(time_kernel(
+            torch, lambda c: qg.qgemm_q4_k_small_m(w4[0], N4, K4, M, qm, dm, smm, ym,
+                                                   qg.QGEMV_VARIANT_MFMA), 50, 1), 2)
     ex["config4_small_m_q4_k_14336x4096"] = sm
     del w4
 
@@ -640,7 +662,7 @@ def extras(qg, torch, np, synth, dev, R, c2, c3, args):
         w6.append(w6[0].clone())
     x6, _ = synth.activation(g6, 64, K6)
     sm6 = {}
-    for M in (1, 2, 4, 8, 16, 32, 64):
+    for M in SMALL_M_LIST:
         xm = torch.from_numpy(np.ascontiguousarray(x6[:M])).to(dev)
         qm, dm, smm = qg.act_buffers(M, K6, dev)
         qg.qgemv_quantize_act(xm, M, K6, K6, qm, dm, smm)
@@ -654,8 +676,7 @@ def extras(qg, torch, np, synth, dev, R, c2, c3, args):
         sm6[f"M{M}_mfma_weight_GBps"] = round(wb6 / sm6[f"M{M}_mfma_us"] / 1e3, 1)
         sm6[f"M{M}_mfma_int8_TOPS"] = round(2 * M * N6 * K6 / sm6[f"M{M}_mfma_us"] / 1e6, 1)
     sm6["crossover_M_mfma_faster_from"] = next(
-        (M for M in (1, 2, 4, 8, 16, 32, 64) if sm6[f"M{M}_mfma_us"] < sm6[f"M{M}_gemv_rows_us"]),
-        None)
+        (M for M in SMALL_M_LIST if sm6[f"M{M}_mfma_us"] < sm6[f"M{M}_gemv_rows_us"]), None)
     ex["small_m_q6_k_4096x14336"] = sm6
     del w6
 
