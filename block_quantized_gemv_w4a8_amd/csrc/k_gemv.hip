@@ -565,6 +565,7 @@ struct SliceStream {
     using WT = typename UnitT::W;
     using UL = UnitLds<FMT>;
     int lane, u_lo, u_hi, sbeg, slen, nbw;
+    bool empty;   // a slice past the row's last unit (see the constructor)
     ActReg<FMT> A[UPL];
     int ul[UPL];
     bool ok[UPL], has1[UPL];
@@ -572,6 +573,18 @@ struct SliceStream {
     __device__ __forceinline__ SliceStream(int lane_, int U, int US, int kq, int nbw_,
                                            int row_bytes)
         : lane(lane_), u_lo(kq * US), u_hi(min(U, kq * US + US)), nbw(nbw_) {
+        // Slices start at tile boundaries for the repacked Q6_K, so the last
+        // of WK slices can lie wholly past the row (e.g. 132 units over
+        // slices of 64).  Such a slice streams the row's last tile instead
+        // (whole tiles: unit_byte addresses only tile starts; its loads stay
+        // inside the row and fit the slice buffers) and contributes nothing.
+        empty = u_hi <= u_lo;
+        if (empty) {
+            constexpr int UG = FMT == QGEMV_FMT_Q6_K_R8 ? 32
+                               : (FMT == QGEMV_FMT_Q4_K || FMT == QGEMV_FMT_Q6_K) ? 4 : 1;
+            u_lo = (U - 1) / UG * UG;
+            u_hi = U;
+        }
         sbeg = unit_byte<FMT>(u_lo);
         slen = min(unit_byte<FMT>(u_hi), row_bytes) - sbeg;
     }
@@ -581,7 +594,7 @@ struct SliceStream {
 #pragma unroll
         for (int i = 0; i < UPL; i++) {
             const int u = u_lo + lane + 64 * i;
-            ok[i] = u < u_hi;
+            ok[i] = !empty && u < u_hi;
             const int uc = ok[i] ? u : u_hi - 1;
             A[i].load(q, d, s, uc);
             ul[i] = uc - u_lo;

@@ -53,8 +53,11 @@ def test_repack_bytes(qg, N, K):
     assert np.array_equal(wr, repack_reference(w.reshape(N, -1), N, K))
 
 
+# K = 8448 (132 units) and 16640 (260 units): split-K slices start at tile
+# boundaries, so the last of the four slices holds no unit of the row
 @pytest.mark.parametrize("N,K", [(1, 256), (37, 896), (130, 2304), (300, 4096), (129, 8192),
-                                 (64, 14336), (33, 32768), (1000, 1024)])
+                                 (64, 14336), (33, 32768), (1000, 1024), (70, 8448),
+                                 (129, 16640)])
 def test_r8_gemv_against_oracle(qg, N, K):
     g = np.random.default_rng(N + 3 * K)
     w = synth.q6_k_weights(g, N, K)

@@ -70,7 +70,8 @@ SHAPES = {
     "q6_k": [(1, 256), (65, 1024), (257, 2304), (64, 4096), (33, 4384), (17, 14336),
              (3, 32768)],
     "q8_0": [(3, 96), (65, 896), (64, 4096), (33, 4864), (17, 14336)],
-    "q6_k_r8": [(65, 1024), (64, 4096), (33, 4864), (17, 14336), (3, 32768)],
+    "q6_k_r8": [(65, 1024), (64, 4096), (33, 4864), (9, 8448), (17, 14336), (5, 16640),
+                (3, 32768)],
 }
 
 
