@@ -126,8 +126,9 @@ def main():
                     help="bracket every n-th lm_head launch of the timed steps with HIP events "
                          "(each pair costs ~20 us of step time, so they are sampled)")
     ap.add_argument("--small-m-profile", action="store_true",
-                    help="only run the small-M MFMA products (Q4_K 14336x4096, Q6_K 4096x14336 "
-                         "at M = 8 and 64), 20 calls each, for counter collection")
+                    help="only run the small-M products (Q4_K 14336x4096, Q6_K 4096x14336; "
+                         "both variants at every M of SMALL_M_LIST), 20 calls each, for "
+                         "counter collection")
     ap.add_argument("--native-q6k", action="store_true",
                     help="run the Q6_K GEMVs on the on-disk layout instead of the repacked one")
     ap.add_argument("--unfused", action="store_true",
