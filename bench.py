@@ -235,8 +235,10 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    K = args.steps
-    P = max(1, args.event_every)
+    K = max(1, args.steps)
+    # every P-th step's lm_head is bracketed by events (at least one when
+    # fewer than P steps are timed)
+    P = max(1, min(args.event_every, K))
     evs = [HipTimer() if i % P == P - 1 else None for i in range(K)]
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
