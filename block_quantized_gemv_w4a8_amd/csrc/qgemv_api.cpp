@@ -2,7 +2,7 @@
 // kernel launches.  No allocation, no host synchronisation, no copies.
 //
 // Every entry point runs its gates in the same order -- NULL pointers,
-// shapes, limits of this build, alignment, device -- and returns at the first
+// shapes, limits of this library, alignment, device -- and returns at the first
 // failure without launching anything, so a failed call never leaves a partial
 // result (colibri GPU backends, "Eligibility gates" and "Failure invariant").
 // A refusal names its reason through qgemv_last_error() ("Backends and
@@ -57,7 +57,7 @@ qgemv_status check_device() {
         state = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
         g_dev_ok[dev].store(state, std::memory_order_relaxed);
         if (state == 2)
-            return fail(QGEMV_E_DEVICE, "device %d is %s, this build targets gfx950", dev,
+            return fail(QGEMV_E_DEVICE, "device %d is %s, this library targets gfx950", dev,
                         prop.gcnArchName);
     }
     if (state == 2) return fail(QGEMV_E_DEVICE, "device %d is not gfx950", dev);
@@ -245,7 +245,7 @@ const char* qgemv_status_str(int status) {
     case QGEMV_OK: return "QGEMV_OK";
     case QGEMV_E_NULL: return "QGEMV_E_NULL: a required pointer is NULL";
     case QGEMV_E_SHAPE: return "QGEMV_E_SHAPE: invalid size or stride";
-    case QGEMV_E_UNSUPPORTED: return "QGEMV_E_UNSUPPORTED: valid but declined by this build";
+    case QGEMV_E_UNSUPPORTED: return "QGEMV_E_UNSUPPORTED: valid but declined by this library";
     case QGEMV_E_ALIGN: return "QGEMV_E_ALIGN: misaligned pointer";
     case QGEMV_E_DEVICE: return "QGEMV_E_DEVICE: no usable gfx950 device";
     case QGEMV_E_LAUNCH: return "QGEMV_E_LAUNCH: kernel launch failed";
@@ -274,7 +274,7 @@ qgemv_status qgemv_quantize_act(const float* x, int64_t M, int64_t K, int64_t ld
         return fail(QGEMV_E_SHAPE, "qgemv_quantize_act: ldx = %lld < K = %lld", (long long)ldx,
                     (long long)K);
     if (M > (int64_t)1 << 31 || ldx > (int64_t)1 << 40 || K > (int64_t)1 << 31)
-        return fail(QGEMV_E_UNSUPPORTED, "qgemv_quantize_act: sizes beyond this build's range");
+        return fail(QGEMV_E_UNSUPPORTED, "qgemv_quantize_act: sizes beyond this library's range");
     const int64_t Kp = (K + 255) / 256 * 256;
     if (M * (Kp / 32) * 8 / 256 >= ((int64_t)1 << 31))
         return fail(QGEMV_E_UNSUPPORTED, "qgemv_quantize_act: M*K too large for one launch");

@@ -36,7 +36,7 @@
  *
  * Conventions shared by every entry point:
  *   - Argument gates run in a fixed order, cheapest first, and the first
- *     failure returns: NULL pointers, then shapes, then limits of this build,
+ *     failure returns: NULL pointers, then shapes, then limits of this library,
  *     then alignment, then the device (colibri GPU backends, "Eligibility
  *     gates": every gate returns).  On any error nothing is launched and no
  *     output is written (same page, "Failure invariant": a failure is never a
@@ -63,7 +63,7 @@ extern "C" {
 
 #define QGEMV_ABI_VERSION 1
 
-/* Largest K accepted by the GEMV and small-M entry points in this build. */
+/* Largest K accepted by the GEMV and small-M entry points in this library. */
 #define QGEMV_K_MAX 32768
 /* Most matrices one qgemv_multi / qgemv_quantize_multi call takes. */
 #define QGEMV_MULTI_MAX 8
@@ -76,7 +76,7 @@ typedef enum {
     QGEMV_OK = 0,
     QGEMV_E_NULL = 1,        /* a required pointer is NULL */
     QGEMV_E_SHAPE = 2,       /* negative size, K not a positive multiple of 32, ldx < K, ... */
-    QGEMV_E_UNSUPPORTED = 3, /* valid but declined by this build (K > QGEMV_K_MAX, M > QGEMV_M_MAX, bad enum) */
+    QGEMV_E_UNSUPPORTED = 3, /* valid but declined by this library (K > QGEMV_K_MAX, M > QGEMV_M_MAX, bad enum) */
     QGEMV_E_ALIGN = 4,       /* w, q not 16-byte aligned; d 2-byte; x, s, y, h, gu, dots 4-byte
                                 (x 16-byte for the products that quantise it) */
     QGEMV_E_DEVICE = 5,      /* no current HIP device, or it is not gfx950 */

@@ -93,7 +93,7 @@ def test_gates_null_shape_limits_align():
     assert _status("qgemm_q4_k_small_m", None, 5, 256, 0, None, None, None, None, 0, S) == qg.QGEMV_OK
     assert _status("qgemv_block_dots", 2, None, 4, 256, 4, 0, None, None, S) == qg.QGEMV_OK
     assert _status(SW, None, 0, 256, None, None, None, None, None, None, None, None, S) == qg.QGEMV_OK
-    # limits of this build
+    # limits of this library
     assert _status("qgemv_q6_k", A, 10, 65536, A, A, A, A, S) == qg.QGEMV_E_UNSUPPORTED
     assert _status("qgemm_q4_k_small_m", A, 8, 256, 65, A, A, A, A, 1, S) == qg.QGEMV_E_UNSUPPORTED
     assert _status("qgemm_q4_k_small_m", A, 8, 256, 4, A, A, A, A, 9, S) == qg.QGEMV_E_UNSUPPORTED
