@@ -1410,7 +1410,7 @@ static hipError_t launch_lds_fmt(const GemvArgs& a, int U, const SliceGeom& g, h
 // few to take the dynamic-row kernel go through the direct-load kernel: the
 // repacked fields load per lane as aligned 16-byte pieces, and as many
 // workgroups as fit keep the units busy.  Measured on MI355X (the 4096 x
-// 14336 down product in the decode step, same box): 11.2-11.3 us against
+// 14336 down product in the decode step, same GPU and process): 11.2-11.3 us against
 // 11.8-11.9 us through LDS (same slices, same bits); with a third row buffer
 // (two rows in flight) 12.7 us.
 constexpr bool kDirectR8Long = true;
