@@ -51,10 +51,13 @@ def log(*a):
 
 
 class HipTimer:
-    """A pair of HIP events recorded without the system-scope fence
+    """Two pairs of HIP events created without the system-scope fence
     (hipEventDisableSystemFence): the default fence writes back and
     invalidates the caches at every record, which opens a gap of several
-    microseconds in the queue and lands inside the bracketed interval."""
+    microseconds in the queue.  Pair 0 brackets a launch on its stream (it
+    also takes in the queue gap before the kernel); pair 1 is handed to
+    qgemv_time_next_launch, so that the kernel itself records it at its start
+    and end."""
     FLAGS = 0x20000000  # hipEventDisableSystemFence
 
     def __init__(self):
@@ -68,7 +71,7 @@ class HipTimer:
                                                  ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
         self.ev = []
-        for _ in range(2):
+        for _ in range(4):
             e = ctypes.c_void_p()
             if self.hip.hipEventCreateWithFlags(ctypes.byref(e), self.FLAGS) != 0:
                 raise RuntimeError("hipEventCreateWithFlags failed")
@@ -78,10 +81,14 @@ class HipTimer:
         if self.hip.hipEventRecord(self.ev[k], stream_handle) != 0:
             raise RuntimeError("hipEventRecord failed")
 
-    def elapsed_ms(self):
+    def kernel_events(self):
+        return self.ev[2], self.ev[3]
+
+    def elapsed_ms(self, pair=0):
+        a, b = self.ev[2 * pair], self.ev[2 * pair + 1]
         ms = self.ct.c_float()
-        self.hip.hipEventSynchronize(self.ev[1])
-        if self.hip.hipEventElapsedTime(self.ct.byref(ms), self.ev[0], self.ev[1]) != 0:
+        self.hip.hipEventSynchronize(b)
+        if self.hip.hipEventElapsedTime(self.ct.byref(ms), a, b) != 0:
             raise RuntimeError("hipEventElapsedTime failed")
         return ms.value
 
@@ -223,6 +230,7 @@ def main():
             qg.qgemv_quantize_act(x_head, 1, Kh, Kh, q3, d3, s3, stream=sh)
         if ev is not None:
             ev.record(0, sh)
+            qg.qgemv_time_next_launch(*ev.kernel_events())
         if sep_quant:
             gemv_q6(w_hd[c], Nh, Kh, q3, d3, s3, logits, stream=sh)
         else:
@@ -254,11 +262,15 @@ def main():
     wall_ms = (w1 - w0) * 1e3
     ms_per_step = max(gpu_ms, wall_ms) / K
     value = step_wbytes / (ms_per_step * 1e-3) / 1e9
-    head_us = [e.elapsed_ms() * 1e3 for e in evs if e is not None]
+    # the lm_head kernel's own start/end events (qgemv_time_next_launch), and
+    # the bracket recorded on the stream around the same launch
+    head_us = [e.elapsed_ms(1) * 1e3 for e in evs if e is not None]
+    bracket_us = [e.elapsed_ms(0) * 1e3 for e in evs if e is not None]
     head_avg_us = float(np.mean(head_us))
+    bracket_avg_us = float(np.mean(bracket_us))
     log(f"[bench] step {ms_per_step * 1e3:.1f} us (events {gpu_ms / K * 1e3:.1f}, wall "
-        f"{wall_ms / K * 1e3:.1f}); lm_head avg {head_avg_us:.2f} us over {len(head_us)} "
-        f"event-bracketed launches")
+        f"{wall_ms / K * 1e3:.1f}); lm_head kernel avg {head_avg_us:.2f} us over "
+        f"{len(head_us)} timed launches (stream bracket {bracket_avg_us:.2f} us)")
 
     # dominant kernel roofline: algorithmic bytes per launch of the lm_head GEMV
     # = N rows x (row weight bytes + 4 B output) + one activation row (codes,
@@ -279,6 +291,8 @@ def main():
                             "(qgemv_quantize_gemv)")),
                 "avg_us": round(head_avg_us, 2),
                 "timed_launches": len(head_us),
+                "timing": "kernel start/end events (qgemv_time_next_launch)",
+                "stream_bracket_avg_us": round(bracket_avg_us, 2),
                 "alg_bytes_per_launch": head_alg}
 
     extra = {}

@@ -41,6 +41,7 @@ QGEMV_M_MAX = 64
 # Every extern "C" symbol that include/qgemv.h declares.
 EXPORTS = [
     "qgemv_abi_version", "qgemv_status_str", "qgemv_build_info", "qgemv_last_error",
+    "qgemv_time_next_launch",
     "qgemv_quantize_act", "qgemv_q4_0", "qgemv_q4_k", "qgemv_q6_k", "qgemv_q8_0",
     "qgemv_q6_k_repack", "qgemv_q6_k_r8",
     "qgemm_q4_k_small_m", "qgemm_q6_k_small_m", "qgemm_q4_0_small_m",
@@ -58,6 +59,7 @@ _lib.qgemv_build_info.restype = ctypes.c_char_p
 _lib.qgemv_build_info.argtypes = []
 _lib.qgemv_last_error.restype = ctypes.c_char_p
 _lib.qgemv_last_error.argtypes = []
+_lib.qgemv_time_next_launch.argtypes = [_P, _P]
 _lib.qgemv_quantize_act.restype = _I
 _lib.qgemv_quantize_act.argtypes = [_P, _I64, _I64, _I64, _P, _P, _P, _P]
 for _n in ("qgemv_q4_0", "qgemv_q4_k", "qgemv_q6_k", "qgemv_q8_0", "qgemv_q6_k_r8"):
@@ -132,6 +134,16 @@ def qgemv_build_info() -> str:
 
 def qgemv_last_error() -> str:
     return _lib.qgemv_last_error().decode()
+
+
+def _handle(e):
+    return e.value if isinstance(e, ctypes.c_void_p) else e
+
+
+def qgemv_time_next_launch(start=None, stop=None):
+    """start, stop: hipEvent_t handles (int or ctypes.c_void_p) or None."""
+    return _check(_lib.qgemv_time_next_launch(_handle(start), _handle(stop)),
+                  "qgemv_time_next_launch")
 
 
 def qgemv_quantize_act(x, M, K, ldx, q, d, s, stream=None):

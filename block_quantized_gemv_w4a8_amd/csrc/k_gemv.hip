@@ -1205,9 +1205,9 @@ static hipError_t launch_gemv_cfg(const GemvArgs& a, int U, hipStream_t st,
     const int64_t resident = resident_workgroups<FMT, LPR, UPL, WK, XQ, MULTI>();
     const int64_t passes = (ngroups + resident - 1) / resident;
     const int64_t grid = (ngroups + passes - 1) / passes;
-    hipLaunchKernelGGL((k_gemv<FMT, LPR, UPL, WK, XQ, MULTI>), dim3((unsigned)grid), dim3(WG), 0,
-                       st, (const uint8_t*)a.w, (int)a.N, U, slice_units<FMT>(U, WK),
-                       (int)(a.K / 32), row_bytes_of(FMT, a.K), a.q, a.d, a.s, a.y, ai, mr);
+    launch_kernel((k_gemv<FMT, LPR, UPL, WK, XQ, MULTI>), dim3((unsigned)grid), dim3(WG), 0,
+                  st, (const uint8_t*)a.w, (int)a.N, U, slice_units<FMT>(U, WK),
+                  (int)(a.K / 32), row_bytes_of(FMT, a.K), a.q, a.d, a.s, a.y, ai, mr);
     return hipGetLastError();
 }
 
@@ -1258,9 +1258,9 @@ static hipError_t launch_lds_cfg(const GemvArgs& a, const SwigluOut& so, const A
         resident = (int64_t)kLdsWgPerCu * cus;
     const int64_t passes = (items + resident - 1) / resident;
     const int64_t grid = (items + passes - 1) / passes;
-    hipLaunchKernelGGL((k_gemv_lds<FMT, UPL, WK, NL, kStreamNT, SW, XQ>), dim3((unsigned)grid),
-                       dim3(WG), smem, st, (const uint8_t*)a.w, (int)a.N, U, US, (int)(a.K / 32),
-                       row_bytes_of(FMT, a.K), buf_bytes, a.q, a.d, a.s, a.y, so, ai);
+    launch_kernel((k_gemv_lds<FMT, UPL, WK, NL, kStreamNT, SW, XQ>), dim3((unsigned)grid),
+                  dim3(WG), smem, st, (const uint8_t*)a.w, (int)a.N, U, US, (int)(a.K / 32),
+                  row_bytes_of(FMT, a.K), buf_bytes, a.q, a.d, a.s, a.y, so, ai);
     return hipGetLastError();
 }
 
@@ -1357,15 +1357,15 @@ static hipError_t launch_dyn_cfg(const GemvArgs& a, const SwigluOut& so, const A
                          (WK > 1 || SW ? pool_cap * WK * 4 : 0) + (SW ? per_wg * 32 * 4 : 0);
     if (smem > 65536 - 64) return hipErrorNotSupported;
     if (buf_bytes - 32 <= kDynPairMaxSlice)
-        hipLaunchKernelGGL((k_gemv_dyn<FMT, UPL, WK, NL, XQ, SW, true>), dim3((unsigned)grid),
-                           dim3(DWG), (unsigned)smem, st, (const uint8_t*)a.w, (int)a.N, U, US,
-                           (int)(a.K / 32), row_bytes_of(FMT, a.K), buf_bytes, a.q, a.d, a.s, a.y,
-                           so, ai);
+        launch_kernel((k_gemv_dyn<FMT, UPL, WK, NL, XQ, SW, true>), dim3((unsigned)grid),
+                      dim3(DWG), (unsigned)smem, st, (const uint8_t*)a.w, (int)a.N, U, US,
+                      (int)(a.K / 32), row_bytes_of(FMT, a.K), buf_bytes, a.q, a.d, a.s, a.y,
+                      so, ai);
     else
-        hipLaunchKernelGGL((k_gemv_dyn<FMT, UPL, WK, NL, XQ, SW, false>), dim3((unsigned)grid),
-                           dim3(DWG), (unsigned)smem, st, (const uint8_t*)a.w, (int)a.N, U, US,
-                           (int)(a.K / 32), row_bytes_of(FMT, a.K), buf_bytes, a.q, a.d, a.s, a.y,
-                           so, ai);
+        launch_kernel((k_gemv_dyn<FMT, UPL, WK, NL, XQ, SW, false>), dim3((unsigned)grid),
+                      dim3(DWG), (unsigned)smem, st, (const uint8_t*)a.w, (int)a.N, U, US,
+                      (int)(a.K / 32), row_bytes_of(FMT, a.K), buf_bytes, a.q, a.d, a.s, a.y,
+                      so, ai);
     return hipGetLastError();
 }
 
@@ -1602,8 +1602,8 @@ hipError_t launch_q6k_repack(const void* w, int64_t N, int64_t K, void* wr, hipS
     const int ntile = (nsb + Q6K::TILE_SB - 1) / Q6K::TILE_SB;
     const int64_t threads = N * ntile * Q6K::TILE_SB;
     const int64_t grid = (threads + WG - 1) / WG;
-    hipLaunchKernelGGL(k_q6k_repack, dim3((unsigned)grid), dim3(WG), 0, st, (const uint8_t*)w, N,
-                       nsb, (int64_t)nsb * 210, ntile, (uint8_t*)wr);
+    launch_kernel(k_q6k_repack, dim3((unsigned)grid), dim3(WG), 0, st, (const uint8_t*)w, N,
+                  nsb, (int64_t)nsb * 210, ntile, (uint8_t*)wr);
     return hipGetLastError();
 }
 
@@ -1619,24 +1619,24 @@ hipError_t launch_block_dots(int fmt, const void* w, int64_t K, int64_t row0, in
     const uint8_t* wp = (const uint8_t*)w;
     switch (fmt) {
     case QGEMV_FMT_Q4_0:
-        hipLaunchKernelGGL(k_block_dots<QGEMV_FMT_Q4_0>, dim3((unsigned)grid), dim3(WG), 0, st,
-                           wp, row0, nrows, U, nbw, rb, nblk, q, dots);
+        launch_kernel(k_block_dots<QGEMV_FMT_Q4_0>, dim3((unsigned)grid), dim3(WG), 0, st,
+                      wp, row0, nrows, U, nbw, rb, nblk, q, dots);
         break;
     case QGEMV_FMT_Q4_K:
-        hipLaunchKernelGGL(k_block_dots<QGEMV_FMT_Q4_K>, dim3((unsigned)grid), dim3(WG), 0, st,
-                           wp, row0, nrows, U, nbw, rb, nblk, q, dots);
+        launch_kernel(k_block_dots<QGEMV_FMT_Q4_K>, dim3((unsigned)grid), dim3(WG), 0, st,
+                      wp, row0, nrows, U, nbw, rb, nblk, q, dots);
         break;
     case QGEMV_FMT_Q6_K:
-        hipLaunchKernelGGL(k_block_dots<QGEMV_FMT_Q6_K>, dim3((unsigned)grid), dim3(WG), 0, st,
-                           wp, row0, nrows, U, nbw, rb, nblk, q, dots);
+        launch_kernel(k_block_dots<QGEMV_FMT_Q6_K>, dim3((unsigned)grid), dim3(WG), 0, st,
+                      wp, row0, nrows, U, nbw, rb, nblk, q, dots);
         break;
     case QGEMV_FMT_Q6_K_R8:
-        hipLaunchKernelGGL(k_block_dots<QGEMV_FMT_Q6_K_R8>, dim3((unsigned)grid), dim3(WG), 0,
-                           st, wp, row0, nrows, U, nbw, rb, nblk, q, dots);
+        launch_kernel(k_block_dots<QGEMV_FMT_Q6_K_R8>, dim3((unsigned)grid), dim3(WG), 0,
+                      st, wp, row0, nrows, U, nbw, rb, nblk, q, dots);
         break;
     default:
-        hipLaunchKernelGGL(k_block_dots<QGEMV_FMT_Q8_0>, dim3((unsigned)grid), dim3(WG), 0, st,
-                           wp, row0, nrows, U, nbw, rb, nblk, q, dots);
+        launch_kernel(k_block_dots<QGEMV_FMT_Q8_0>, dim3((unsigned)grid), dim3(WG), 0, st,
+                      wp, row0, nrows, U, nbw, rb, nblk, q, dots);
         break;
     }
     return hipGetLastError();

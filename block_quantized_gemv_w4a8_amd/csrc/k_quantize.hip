@@ -79,8 +79,8 @@ hipError_t launch_quantize_act(const float* x, int64_t M, int64_t K, int64_t ldx
     const int64_t Kp = (K + 255) / 256 * 256;
     const int64_t threads = M * (Kp / 32) * 8;
     const int64_t grid = (threads + QWG - 1) / QWG;
-    hipLaunchKernelGGL(k_quantize_act, dim3((unsigned)grid), dim3(QWG), 0, st, x, M, K, ldx, Kp,
-                       q, d, s);
+    launch_kernel(k_quantize_act, dim3((unsigned)grid), dim3(QWG), 0, st, x, M, K, ldx, Kp,
+                  q, d, s);
     return hipGetLastError();
 }
 
@@ -89,8 +89,8 @@ hipError_t launch_silu_mul_quantize(const float* gu, int64_t N, int8_t* q, uint1
     const int64_t Kp = (N + 255) / 256 * 256;
     const int64_t threads = (Kp / 32) * 8;
     const int64_t grid = (threads + QWG - 1) / QWG;
-    hipLaunchKernelGGL(k_silu_mul_quantize, dim3((unsigned)grid), dim3(QWG), 0, st, gu, N, Kp, q,
-                       d, s, h);
+    launch_kernel(k_silu_mul_quantize, dim3((unsigned)grid), dim3(QWG), 0, st, gu, N, Kp, q,
+                  d, s, h);
     return hipGetLastError();
 }
 

@@ -625,9 +625,9 @@ static hipError_t launch_mfma_cfg(const void* w, int64_t N, int64_t K, int64_t M
                                   hipStream_t st) {
     const int Kp = (int)((K + 255) / 256 * 256);
     const int64_t grid = (N + 16 * RT - 1) / (16 * RT);
-    hipLaunchKernelGGL((k_small_m_mfma<FMT, MT, RT, KS, KP, MS, G, R>), dim3((unsigned)grid),
-                       dim3(64 * RT * KS * KP * MS), 0, st, (const uint8_t*)w, (int)N, (int)K,
-                       Kp, (int)M, q, d, s, y);
+    launch_kernel((k_small_m_mfma<FMT, MT, RT, KS, KP, MS, G, R>), dim3((unsigned)grid),
+                  dim3(64 * RT * KS * KP * MS), 0, st, (const uint8_t*)w, (int)N, (int)K,
+                  Kp, (int)M, q, d, s, y);
     return hipGetLastError();
 }
 
@@ -679,9 +679,9 @@ static hipError_t launch_dot4(const void* w, int64_t N, int64_t K, int64_t M, co
     const int64_t gx = (passes + R - 1) / R;
     const int64_t gy = (M + MT - 1) / MT;
     const int smem = MT * small_m_row_smem(Kp);
-    hipLaunchKernelGGL((k_small_m_dot4<MT, LPR>), dim3((unsigned)gx, (unsigned)gy), dim3(SWG),
-                       smem, st, (const uint8_t*)w, (int)N, Kp, U, Kp / 256 * 144, (int)M, q, d,
-                       s, y, R);
+    launch_kernel((k_small_m_dot4<MT, LPR>), dim3((unsigned)gx, (unsigned)gy), dim3(SWG),
+                  smem, st, (const uint8_t*)w, (int)N, Kp, U, Kp / 256 * 144, (int)M, q, d,
+                  s, y, R);
     return hipGetLastError();
 }
 

@@ -236,6 +236,13 @@ qgemv_status multi_common(const char* name, int fmt, int count, const void* cons
 
 }  // namespace
 
+namespace qgemv {
+LaunchTimer& next_launch_timer() {
+    static thread_local LaunchTimer t;
+    return t;
+}
+}  // namespace qgemv
+
 extern "C" {
 
 int qgemv_abi_version(void) { return QGEMV_ABI_VERSION; }
@@ -262,6 +269,11 @@ const char* qgemv_build_info(void) {
 }
 
 const char* qgemv_last_error(void) { return g_last_error; }
+
+qgemv_status qgemv_time_next_launch(void* start, void* stop) {
+    qgemv::next_launch_timer() = {(hipEvent_t)start, (hipEvent_t)stop};
+    return QGEMV_OK;
+}
 
 qgemv_status qgemv_quantize_act(const float* x, int64_t M, int64_t K, int64_t ldx, int8_t* q,
                                 uint16_t* d, int32_t* s, qgemv_stream_t stream) {

@@ -3,12 +3,38 @@
 // already passed every gate of the public entry points.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "qgemv.h"
 
 namespace qgemv {
+
+// Events that the next kernel launched from this host thread records at its
+// start and end (set by qgemv_time_next_launch; both NULL when disarmed).
+struct LaunchTimer {
+    hipEvent_t start = nullptr;
+    hipEvent_t stop = nullptr;
+};
+LaunchTimer& next_launch_timer();
+
+// Every kernel of the library is launched through here: a plain launch, or,
+// when the calling thread is armed, one that records the timer's events
+// around the kernel and disarms the thread.
+template <typename... KArgs, typename... Args>
+inline void launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, unsigned smem,
+                          hipStream_t st, Args... args) {
+    LaunchTimer& t = next_launch_timer();
+    if (t.start || t.stop) {
+        const LaunchTimer use = t;
+        t = LaunchTimer{};
+        hipExtLaunchKernelGGL(kernel, grid, block, smem, st, use.start, use.stop, 0u,
+                              static_cast<KArgs>(args)...);
+    } else {
+        kernel<<<grid, block, smem, st>>>(static_cast<KArgs>(args)...);
+    }
+}
 
 struct GemvArgs {
     const void* w;

@@ -46,8 +46,9 @@
  *     host<->device copy and no allocation, so calls can be captured into a
  *     HIP graph.  Faults inside a kernel surface at the caller's next
  *     synchronisation, as usual for HIP.
- *   - The library keeps no per-call state: concurrent calls on different
- *     streams are safe as long as their output buffers do not overlap.
+ *   - The library keeps no per-call state (only the thread-local error text
+ *     and timing setting below): concurrent calls on different streams are
+ *     safe as long as their output buffers do not overlap.
  *     Inputs and outputs of one call must not alias.
  *   - An empty problem (N == 0 or M == 0) returns QGEMV_OK without launching.
  *   - Results are deterministic: the same inputs give bit-identical outputs.
@@ -106,6 +107,19 @@ const char* qgemv_build_info(void);
 /* Reason for the most recent non-OK status returned to the calling thread
  * (thread-local, overwritten by the next failing call; "" if none). */
 const char* qgemv_last_error(void);
+
+/* Kernel timing, a measurement aid that no product formula needs.  Arms the
+ * calling host thread so that the next kernel this library launches from
+ * that thread records `start` (a hipEvent_t, or NULL) when the kernel begins
+ * and `stop` (a hipEvent_t, or NULL) when it ends.  hipEventElapsedTime
+ * (start, stop) is then that kernel's own duration, without the time the
+ * stream spent on earlier work or between launches.  The events are created
+ * and destroyed by the caller and must outlive the timed launch.  One launch
+ * consumes the setting: an entry point that launches several kernels times
+ * its first; a call that returns an error before launching leaves it armed.
+ * qgemv_time_next_launch(NULL, NULL) disarms.  Only this thread-local pair
+ * is stored; returns QGEMV_OK. */
+qgemv_status qgemv_time_next_launch(void* start, void* stop);
 
 /* Activation quantisation ("Backends and hardware", section "CPU": quantised
  * to int8 once per matmul).  x: fp32 [M][ldx] with K valid columns

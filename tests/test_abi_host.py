@@ -54,6 +54,13 @@ def test_version_and_strings():
     assert "gfx950" in info and "q6_k" in info
 
 
+def test_time_next_launch_arms_and_disarms_without_a_device():
+    # only a thread-local pair is stored: no HIP call, so no device needed
+    qg = _lib()
+    assert qg.qgemv_time_next_launch(0x1000, 0x2000) == 0
+    assert qg.qgemv_time_next_launch(None, None) == 0
+
+
 # Fake device addresses: only ever passed where an earlier gate must refuse.
 A = 0x7F0000000000  # 256-byte aligned
 
