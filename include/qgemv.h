@@ -117,8 +117,9 @@ const char* qgemv_last_error(void);
  * and destroyed by the caller and must outlive the timed launch.  One launch
  * consumes the setting: an entry point that launches several kernels times
  * its first; a call that returns an error before launching leaves it armed.
- * qgemv_time_next_launch(NULL, NULL) disarms.  Only this thread-local pair
- * is stored; returns QGEMV_OK. */
+ * qgemv_time_next_launch(NULL, NULL) disarms.  Meant for eager launches:
+ * disarm before capturing a stream into a HIP graph.  Only this thread-local
+ * pair is stored; returns QGEMV_OK. */
 qgemv_status qgemv_time_next_launch(void* start, void* stop);
 
 /* Activation quantisation ("Backends and hardware", section "CPU": quantised
