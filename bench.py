@@ -670,6 +670,23 @@ def extras(qg, torch, np, synth, dev, R, c2, c3, args):
     ex["config4_small_m_q4_k_14336x4096"] = sm
     del w4
 
+    # the other weight formats at the gate/up shape (Q8_0 and Q4_0 GEMVs)
+    gf = np.random.default_rng(13)
+    xf, _ = synth.activation(gf, 1, 4096)
+    ex["q8_0_14336x4096"] = gemv_case("q8_0", synth.q8_0_weights(gf, 14336, 4096), 14336,
+                                      4096, xf, 8)
+    ex["q4_0_14336x4096"] = gemv_case("q4_0", synth.q4_0_weights(gf, 14336, 4096), 14336,
+                                      4096, xf, 16)
+
+    # the one-time load repack of the lm_head weights (Q6_K -> Q6_K_R8)
+    wh = torch.from_numpy(c3["w"]).to(dev)
+    whr = torch.empty((Nh, qg.q6_k_r8_row_bytes(Kh)), dtype=torch.uint8, device=dev)
+    us = time_kernel(torch, lambda c: qg.qgemv_q6_k_repack(wh, Nh, Kh, whr), 5, 1)
+    wb = synth.logical_bytes("q6_k", Nh, Kh)
+    ex["q6_k_repack_128256x4096"] = {"us": round(us, 2),
+                                     "read_plus_write_GBps": round(2 * wb / us / 1e3, 1)}
+    del wh, whr
+
     # the prefill chunk through the down projection: Q6_K 4096 x 14336
     g6 = np.random.default_rng(11)
     N6, K6 = 4096, 14336
@@ -729,7 +746,61 @@ def cpu_baseline(np, synth, c2, c3, seconds, step_wbytes):
     return {"value": round(step_wbytes / per / 1e9, 4), "unit": "GB/s", "cores": 1,
             "kind": "oracle", "ms_per_step": round(per * 1e3, 1),
             "sample": f"{len(times)} whole steps of the same workload, single thread, "
-                      f"median step time"}
+                      f"median step time",
+            "per_kernel": oracle_rates(np, synth, c2, c3)}
+
+
+def oracle_rates(np, synth, c2, c3, seconds=0.3):
+    """The oracle beside each per-kernel GPU figure of `extra`: the same
+    shapes, on a bounded sample of weight rows (the first 512, or 64 for the
+    small-M products), each repeated for at least `seconds`; single thread."""
+    import oracle
+    g = np.random.default_rng(23)
+    out = {}
+
+    def per_call(fn):
+        n, t0 = 0, time.perf_counter()
+        while True:
+            fn()
+            n += 1
+            t = time.perf_counter() - t0
+            if t >= seconds:
+                return t / n
+
+    def gemv_rate(name, fmt, w, N, K, x, S=512):
+        q, d, s = oracle.quantize_act(x)
+        t = per_call(lambda: oracle.gemv(fmt, w, N, K, q, d, s, rows=(0, S)))
+        out[name] = {"weight_GBps": round(synth.logical_bytes(fmt, S, K) / t / 1e9, 4),
+                     "sample_rows": S}
+
+    def gemm_rate(name, fmt, w, N, K, x, S=64):
+        q, d, s = oracle.quantize_act(x)
+        t = per_call(lambda: oracle.gemm(fmt, w, N, K, q, d, s, rows=(0, S)))
+        M = x.shape[0]
+        out[name] = {"weight_GBps": round(synth.logical_bytes(fmt, S, K) / t / 1e9, 4),
+                     "int8_GOPS": round(2 * M * S * K / t / 1e9, 4), "sample_rows": S}
+
+    hx = np.random.default_rng(0).standard_normal((1, c2["K_down"])).astype(np.float32)
+    gemv_rate("gate_up_q4_k_28672x4096", "q4_k", c2["w_gu"], c2["N_gu"], c2["K_gu"], c2["x"])
+    gemv_rate("down_q6_k_4096x14336", "q6_k", c2["w_down"], c2["N_down"], c2["K_down"], hx)
+    gemv_rate("lm_head_q6_k_128256x4096", "q6_k", c3["w"], c3["N"], c3["K"], c3["x"])
+    x4k, _ = synth.activation(g, 1, 4096)
+    gemv_rate("q8_0_14336x4096", "q8_0", synth.q8_0_weights(g, 512, 4096), 512, 4096, x4k)
+    gemv_rate("q4_0_14336x4096", "q4_0", synth.q4_0_weights(g, 512, 4096), 512, 4096, x4k)
+    out["quantize_act_4096_us"] = round(per_call(lambda: oracle.quantize_act(c2["x"])) * 1e6, 1)
+    gu = g.standard_normal(2 * c2["K_down"]).astype(np.float32)
+    out["silu_mul_quantize_14336_us"] = round(per_call(lambda: oracle.quantize_act(
+        oracle.silu_mul(gu).astype(np.float32)[None])) * 1e6, 1)
+    w4 = synth.q4_k_weights(g, 64, 4096)
+    x64, _ = synth.activation(g, 64, 4096)
+    w6 = synth.q6_k_weights(g, 64, 14336)
+    x64b, _ = synth.activation(g, 64, 14336)
+    for M in (8, 64):
+        gemm_rate(f"small_m_q4_k_14336x4096_M{M}", "q4_k", w4, 64, 4096,
+                  np.ascontiguousarray(x64[:M]))
+        gemm_rate(f"small_m_q6_k_4096x14336_M{M}", "q6_k", w6, 64, 14336,
+                  np.ascontiguousarray(x64b[:M]))
+    return out
 
 
 if __name__ == "__main__":
