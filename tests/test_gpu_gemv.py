@@ -131,6 +131,28 @@ def test_config3_lm_head_q6_k(qg):
         assert np.array_equal(dots, ref)
 
 
+# Q8_0 and Q4_0 at the gate/up shape (14336 x 4096), as the benchmark times
+# them: sampled rows against the oracle, block dots bit-exact at both ends.
+@pytest.mark.parametrize("fmt", ["q8_0", "q4_0"])
+def test_gate_up_shape_q8_0_q4_0(qg, fmt):
+    N, K = 14336, 4096
+    g = np.random.default_rng(13 + len(fmt))
+    w = synth.weights(fmt, g, N, K)
+    x, _ = synth.activation(g, 1, K)
+    say("gate/up shape", fmt, N, K)
+    act = quantize(qg, x)
+    q, d, s = act_host(*act)
+    wd = dev(w)
+    y = gemv(qg, fmt, wd, N, K, act)
+    assert np.all(np.isfinite(y))
+    rows = sample_rows(N, 2048, seed=5)
+    y_ref, T = oracle_rows(fmt, w, N, K, q, d, s, rows)
+    check_y(y[rows], y_ref, T, f"{fmt} {N}x{K} sampled rows")
+    for r0, nr in [(0, 256), (N - 256, 256)]:
+        dots = block_dots(qg, fmt, wd, N, K, act[0], r0, nr)
+        assert np.array_equal(dots, oracle.block_dots(fmt, w, N, K, q, rows=(r0, nr)))
+
+
 # Matrices with at least 256 rows per compute unit (65536 on MI355X) take the
 # dynamic-row kernel: one 8-wave workgroup per compute unit whose waves pull
 # rows from a counter in LDS.  Tall, ragged shapes (N not a multiple of its 8-row
