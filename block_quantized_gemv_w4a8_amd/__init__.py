@@ -103,10 +103,24 @@ def _ptr(t) -> int | None:
     return t.data_ptr()
 
 
+_current_raw_stream = None
+
+
 def _stream(stream) -> int | None:
+    """The hipStream_t of `stream`; None means torch's current stream, read
+    through torch's raw-handle getter where it has one (it skips building a
+    Stream object, a few microseconds per call)."""
+    global _current_raw_stream
     if stream is None:
-        import torch
-        return torch.cuda.current_stream().cuda_stream
+        if _current_raw_stream is None:
+            import torch
+            raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+            get_dev = getattr(torch._C, "_cuda_getDevice", None)
+            if raw is not None and get_dev is not None:
+                _current_raw_stream = lambda: raw(get_dev())
+            else:
+                _current_raw_stream = lambda: torch.cuda.current_stream().cuda_stream
+        return _current_raw_stream()
     if isinstance(stream, int):
         return stream
     return stream.cuda_stream

@@ -55,9 +55,10 @@ def test_repack_bytes(qg, N, K):
 
 # K = 8448 (132 units) and 16640 (260 units): split-K slices start at tile
 # boundaries, so the last of the four slices holds no unit of the row
+# (4096 x 1792: one GPU's K slice of the down product split 8 ways)
 @pytest.mark.parametrize("N,K", [(1, 256), (37, 896), (130, 2304), (300, 4096), (129, 8192),
                                  (64, 14336), (33, 32768), (1000, 1024), (70, 8448),
-                                 (129, 16640)])
+                                 (129, 16640), (4096, 1792)])
 def test_r8_gemv_against_oracle(qg, N, K):
     g = np.random.default_rng(N + 3 * K)
     w = synth.q6_k_weights(g, N, K)

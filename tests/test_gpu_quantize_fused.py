@@ -63,6 +63,7 @@ def two_call_gemv(qg, fmt, wd, N, K, x):
 # rows the one-launch kernel with 1, 2 or 4 waves per row; K % 256 != 0 leaves
 # zero activation blocks past K; K = 32768 exceeds the kernel's LDS with the
 # activation row and falls back as well.
+# Q6_K_R8 16032 x 4096 is one GPU's lm_head rows split 8 ways.
 SHAPES = {
     "q4_0": [(1, 32), (65, 896), (257, 2080), (64, 4096), (33, 4128), (17, 14336), (3, 32768)],
     "q4_k": [(1, 256), (65, 1024), (257, 2304), (64, 4096), (33, 4384), (17, 14336),
@@ -71,7 +72,7 @@ SHAPES = {
              (3, 32768)],
     "q8_0": [(3, 96), (65, 896), (64, 4096), (33, 4864), (17, 14336)],
     "q6_k_r8": [(65, 1024), (64, 4096), (33, 4864), (9, 8448), (17, 14336), (5, 16640),
-                (3, 32768)],
+                (3, 32768), (16032, 4096)],
 }
 
 
@@ -155,7 +156,8 @@ def swiglu_fused_x(qg, wd, N, K, xd):
 
 
 @pytest.mark.parametrize("N,K", [(32, 256), (96, 896), (320, 4096), (64, 4864), (544, 1024),
-                                 (160, 14336), (8256, 2048), (24736, 512)])
+                                 (160, 14336), (8256, 2048), (24736, 512),
+                                 (1792, 4096)])
 def test_quantize_swiglu_shapes(qg, N, K):
     g = np.random.default_rng(N * 11 + K)
     w = synth.q4_k_weights(g, 2 * N, K)

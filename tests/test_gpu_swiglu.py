@@ -71,8 +71,10 @@ def check_against_oracle(w, N, K, act, out, gu, h):
 
 # N = 8256 and 24736 give a workgroup of the dynamic-row kernel two and up
 # to four output blocks (one unit per 256 blocks), with a ragged remainder
+# (N = 1792, K = 4096: one GPU's gate|up rows when the FFN is split 8 ways)
 @pytest.mark.parametrize("N,K", [(32, 256), (96, 896), (320, 4096), (64, 4864), (160, 32768),
-                                 (544, 1024), (1056, 2048), (8256, 2048), (24736, 512)])
+                                 (544, 1024), (1056, 2048), (8256, 2048), (24736, 512),
+                                 (1792, 4096)])
 def test_fused_shapes(qg, N, K):
     g = np.random.default_rng(N * 7 + K)
     w = synth.q4_k_weights(g, 2 * N, K)
