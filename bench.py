@@ -828,7 +828,50 @@ def cpu_baseline(np, synth, c2, c3, seconds, step_wbytes):
             "kind": "oracle", "ms_per_step": round(per * 1e3, 1),
             "sample": f"{len(times)} whole steps of the same workload, single thread, "
                       f"median step time",
+            "parallel": oracle_parallel(np, c2, c3, step_wbytes),
             "per_kernel": oracle_rates(np, synth, c2, c3)}
+
+
+def oracle_parallel(np, c2, c3, step_wbytes, seconds=3.0):
+    """The same whole steps with each GEMV's rows split into equal ranges
+    over host threads (rows are independent; the oracle's C code releases
+    the interpreter lock while it runs), at most 16 threads."""
+    import oracle
+    from concurrent.futures import ThreadPoolExecutor
+    try:
+        T = len(os.sched_getaffinity(0))
+    except AttributeError:
+        T = os.cpu_count() or 1
+    T = max(1, min(16, T))
+    Ngu, Kgu, Nd, Kd = c2["N_gu"], c2["K_gu"], c2["N_down"], c2["K_down"]
+    Nh, Kh = c3["N"], c3["K"]
+
+    def gemv(pool, fmt, w, N, K, q, d, s):
+        b = np.linspace(0, N, T + 1).astype(np.int64)
+        futs = [pool.submit(oracle.gemv, fmt, w, N, K, q, d, s, (int(b[i]), int(b[i + 1] - b[i])))
+                for i in range(T)]
+        return np.concatenate([f.result()[0] for f in futs])
+
+    times = []
+    with ThreadPoolExecutor(T) as pool:
+        t_all = time.perf_counter()
+        while True:
+            t = time.perf_counter()
+            q, d, s = oracle.quantize_act(c2["x"])
+            gu = gemv(pool, "q4_k", c2["w_gu"], Ngu, Kgu, q, d, s)
+            h = oracle.silu_mul(gu.astype(np.float32))
+            q2, d2, s2 = oracle.quantize_act(h.astype(np.float32)[None])
+            gemv(pool, "q6_k", c2["w_down"], Nd, Kd, q2, d2, s2)
+            q3, d3, s3 = oracle.quantize_act(c3["x"])
+            gemv(pool, "q6_k", c3["w"], Nh, Kh, q3, d3, s3)
+            times.append(time.perf_counter() - t)
+            if time.perf_counter() - t_all >= seconds:
+                break
+    per = float(np.median(times))
+    return {"value": round(step_wbytes / per / 1e9, 4), "unit": "GB/s", "cores": T,
+            "ms_per_step": round(per * 1e3, 1),
+            "sample": f"{len(times)} whole steps, each GEMV's rows split over {T} threads, "
+                      f"median step time"}
 
 
 def oracle_rates(np, synth, c2, c3, seconds=0.3):
