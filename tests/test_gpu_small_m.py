@@ -56,6 +56,31 @@ def test_small_m_shapes(qg, fmt, M, N, K):
                 f"small_m {fmt} M={M} N={N} K={K} v={v}")
 
 
+# Wide matrices (at least 512 row tiles of 16: N = 8200 gives 513, the last
+# ragged) take the configurations that share each staged activation over 64
+# or 32 weight rows, one per bucket of M; every output against the oracle.
+WIDE = [("q4_k", 8, 1024), ("q4_k", 20, 1024), ("q4_k", 40, 1024), ("q4_k", 64, 1024),
+        ("q6_k", 8, 1024), ("q6_k", 24, 1024), ("q6_k", 33, 1024), ("q6_k", 64, 1024),
+        ("q4_0", 17, 1056), ("q4_0", 64, 1056)]
+
+
+@pytest.mark.parametrize("fmt,M,K", WIDE)
+def test_small_m_wide_matrices(qg, fmt, M, K):
+    N = 8200
+    g = np.random.default_rng(M * 31 + K + len(fmt))
+    w = WEIGHTS[fmt](g, N, K)
+    x, _ = synth.activation(g, M, K)
+    act = quantize(qg, x)
+    q, d, s = act_host(*act)
+    wd = dev(w)
+    Y_ref, TT = oracle.gemm(fmt, w, N, K, q, d, s)
+    for v in (qg.QGEMV_VARIANT_MFMA, qg.QGEMV_VARIANT_AUTO):
+        say("small_m wide", fmt, M, N, K, "variant", v)
+        Y = small_m(qg, fmt, wd, N, K, act, M, v)
+        check_y(Y.reshape(-1), Y_ref.reshape(-1), TT.reshape(-1),
+                f"small_m wide {fmt} M={M} N={N} K={K} v={v}")
+
+
 def sampled(fmt, w, N, K, act, windows):
     q, d, s = act
     M = q.shape[0]
