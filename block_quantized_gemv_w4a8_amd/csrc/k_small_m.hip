@@ -686,19 +686,17 @@ static hipError_t launch_mfma(const void* w, int64_t N, int64_t K, int64_t M, co
     switch (mt) {
     case 1: return launch_mfma_cfg<FMT, 1, 1, 2, 4, 1, 4, 2>(w, N, K, M, q, d, s, y, st);
     case 2:
-        // Q4_K: each unit's 32-blocks halved over 2 waves: 25.4 against
-        // 29.1 us at M = 24 on 4096 x 14336 (same process); Q6_K no faster
-        if constexpr (FMT == QGEMV_FMT_Q4_K)
+        // Q4_K and Q4_0: each unit's 32-blocks halved over 2 waves: 25.4
+        // against 29.1 us (Q4_K) and 33.8 against 37.7 us (Q4_0) at M = 24 on
+        // 4096 x 14336 (same process); Q6_K no faster
+        if constexpr (FMT != QGEMV_FMT_Q6_K)
             return launch_mfma_cfg<FMT, 2, 1, 2, 2, 2, 2, 2>(w, N, K, M, q, d, s, y, st);
         else
             return launch_mfma_cfg<FMT, 2, 1, 1, 4, 2, 4, 2>(w, N, K, M, q, d, s, y, st);
     case 3:
-        // the same split: Q6_K 57 against 73 us, Q4_K 38 against 46 us at
-        // M = 48 on 4096 x 14336 (same process)
-        if constexpr (FMT != QGEMV_FMT_Q4_0)
-            return launch_mfma_cfg<FMT, 3, 1, 2, 2, 3, 2, 2>(w, N, K, M, q, d, s, y, st);
-        else
-            return launch_mfma_cfg<FMT, 3, 1, 1, 2, 3, 2, 2>(w, N, K, M, q, d, s, y, st);
+        // the same split for every format: at M = 48 on 4096 x 14336, Q6_K
+        // 57 against 73 us, Q4_K 38 against 46 us, Q4_0 48 against 63 us
+        return launch_mfma_cfg<FMT, 3, 1, 2, 2, 3, 2, 2>(w, N, K, M, q, d, s, y, st);
     default: return launch_mfma_cfg<FMT, 4, 1, 1, 2, 4, 2, 2>(w, N, K, M, q, d, s, y, st);
     }
 }
