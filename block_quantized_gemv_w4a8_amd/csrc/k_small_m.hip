@@ -642,15 +642,18 @@ static hipError_t launch_mfma(const void* w, int64_t N, int64_t K, int64_t M, co
                               const uint16_t* d, const int32_t* s, float* y, hipStream_t st) {
     const int mt = (int)((M + 15) / 16);
     const bool wide = (N + 15) / 16 >= kMfmaWideTiles;
-    // <FMT, MT, RT, KS, KP, MS, G, R>.  Wide matrices: 64 weight rows per
-    // workgroup share the staged activation and each wave takes every
-    // activation tile (splitting the tiles there costs more activation
-    // traffic than it gains; Q6_K's larger units leave LDS for 2 row tiles
-    // from MT = 3).  Narrow matrices also split K between waves (at MT = 1
-    // the 4 units of a step and the two halves of each unit's 32-blocks
-    // over 8 waves: 6% faster on Q6_K 4096x14336 than 8 units over 8 waves)
-    // and, from MT = 2, give each wave one activation tile (MS = MT), so a
-    // wave needs the registers of MT = 1 and the chip gets MT times the waves.
+    // <FMT, MT, RT, KS, KP, MS, G, R>.  Wide matrices: 32 (MT = 1) or 64
+    // weight rows per workgroup share the staged activation and each wave
+    // takes every activation tile (splitting the tiles there costs more
+    // activation traffic than it gains; Q6_K's larger units leave LDS for 2
+    // row tiles from MT = 3).  Narrow matrices also split K between waves (at
+    // MT = 1 the 4 units of a step and the two halves of each unit's
+    // 32-blocks over 8 waves: 6% faster on Q6_K 4096x14336 than 8 units over
+    // 8 waves) and, from MT = 2, give each wave one activation tile (MS = MT),
+    // so a wave needs the registers of MT = 1 and the chip gets MT times the
+    // waves.  The per-format choices below were each measured against the
+    // alternative in one process; a bucket of M and a shape fix the
+    // configuration, so the summation order stays fixed per row.
     constexpr int RT34 = FMT == QGEMV_FMT_Q6_K ? 2 : 4;
     if (wide) {
         switch (mt) {
