@@ -725,6 +725,27 @@ def extras(qg, torch, np, synth, dev, R, c2, c3, args):
     ex["small_m_q6_k_4096x14336"] = sm6
     del w6
 
+    # a prefill chunk through the lm_head: Q6_K 128256 x 4096 (a wide matrix)
+    wl = [torch.from_numpy(c3["w"]).to(dev)]
+    wl.append(wl[0].clone())
+    Nl, Kl = c3["N"], c3["K"]
+    xl, _ = synth.activation(np.random.default_rng(12), 64, Kl)
+    sml = {}
+    for M in (8, 64):
+        xm = torch.from_numpy(np.ascontiguousarray(xl[:M])).to(dev)
+        qm, dm, smm = qg.act_buffers(M, Kl, dev)
+        qg.qgemv_quantize_act(xm, M, Kl, Kl, qm, dm, smm)
+        ym = torch.empty((M, Nl), dtype=torch.float32, device=dev)
+        us = time_kernel(torch, lambda c: qg.qgemm_q6_k_small_m(
+            wl[c], Nl, Kl, M, qm, dm, smm, ym, qg.QGEMV_VARIANT_MFMA), 10, 2)
+        wbl = synth.logical_bytes("q6_k", Nl, Kl)
+        sml[f"M{M}_mfma_us"] = round(us, 2)
+        sml[f"M{M}_mfma_weight_GBps"] = round(wbl / us / 1e3, 1)
+        sml[f"M{M}_mfma_int8_TOPS"] = round(2 * M * Nl * Kl / us / 1e6, 1)
+        del ym
+    ex["small_m_q6_k_lm_head_128256x4096"] = sml
+    del wl
+
     # plain device copy: the achievable HBM figure beside the datasheet peak
     a = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
     b = torch.empty_like(a)
