@@ -471,3 +471,118 @@ ALL_PINS = [pin_fp16_decode_exhaustive, pin_fp16_encode_rne, pin_quantize_random
             pin_quantize_closed_forms, pin_unpack_roundtrip, pin_block_dots_brute,
             pin_block_dots_closed_forms, pin_gemv_dequant_brute, pin_gemv_closed_forms,
             pin_quantization_error_bound, pin_gemv_term_sums, pin_gemm_rows, pin_silu_mul]
+
+
+# ------------------------------------------------- literal block layouts ---
+#
+# Blocks built byte by byte, without synth's packers, with the expected fields
+# written out as literals from the layout descriptions of the formats (GGUF
+# block layouts, the reading of "llambda.lisp" README, Features &
+# Architecture: Q4_K_M and Q6_K tensors are read straight from .gguf files).
+# Every byte not named in a probe is zero, so every code not named in the
+# expected map is zero.  Each placement rule (which byte and which bits feed
+# which element) is exercised by at least one probe, so a misreading shared by
+# the packer and the oracle -- which the round-trip pin cannot see -- fails
+# here.
+
+def _block(nbytes, assign):
+    b = np.zeros(nbytes, np.uint8)
+    for k, v in assign.items():
+        b[k] = v
+    return b
+
+
+def _codes(n, nonzero, dtype=np.int64):
+    c = np.zeros(n, dtype)
+    for k, v in nonzero.items():
+        c[k] = v
+    return c
+
+
+# (byte assignments, expected nonzero codes) per format
+Q4_0_PROBES = [
+    ({2 + 3: 0x0B}, {3: 11}),               # qs[3] low nibble -> element 3
+    ({2 + 3: 0x60}, {19: 6}),               # qs[3] high nibble -> element 19
+    ({17: 0xF1}, {15: 1, 31: 15}),          # qs[15] -> elements 15 and 31
+    ({2: 0x7A}, {0: 10, 16: 7}),
+]
+Q8_0_PROBES = [
+    ({2 + 5: 0xFE}, {5: -2}),
+    ({33: 0x7F, 2: 0x81}, {31: 127, 0: -127}),
+]
+Q4_K_PROBES = [
+    ({16: 0x03}, {0: 3}),                   # chunk 0, l = 0, low -> element 0
+    ({16: 0x50}, {32: 5}),                  # chunk 0, l = 0, high -> element 32
+    ({16 + 39: 0x0E}, {71: 14}),            # chunk 1, l = 7, low -> 64 + 7
+    ({16 + 39: 0xB0}, {103: 11}),           # chunk 1, l = 7, high -> 64 + 32 + 7
+    ({16 + 127: 0xF0}, {255: 15}),          # chunk 3, l = 31, high -> 192 + 32 + 31
+    ({16 + 127: 0x09}, {223: 9}),           # chunk 3, l = 31, low -> 192 + 31
+    ({16 + 80: 0x4D}, {144: 13, 176: 4}),   # chunk 2, l = 16
+]
+Q6_K_PROBES = [
+    ({5: 0x0A}, {5: 10}),                   # ql[5] low -> element 5
+    ({5: 0xA0}, {69: 10}),                  # ql[5] high -> element 5 + 64
+    ({37: 0x07}, {37: 7}),                  # ql[37] low -> element 5 + 32
+    ({37: 0x70}, {101: 7}),                 # ql[37] high -> element 5 + 96
+    ({67: 0x0C}, {131: 12}),                # second half: ql[64 + 3] low -> 128 + 3
+    ({99: 0xC0}, {227: 12}),                # ql[64 + 35] high -> 128 + 3 + 96
+    ({128 + 9: 0x02}, {9: 32}),             # qh[9] bits 0-1 -> element 9, code bits 4-5
+    ({128 + 9: 0x0C}, {41: 48}),            # qh[9] bits 2-3 -> element 9 + 32
+    ({128 + 9: 0x10}, {73: 16}),            # qh[9] bits 4-5 -> element 9 + 64
+    ({128 + 9: 0x80}, {105: 32}),           # qh[9] bits 6-7 -> element 9 + 96
+    ({128 + 63: 0x40}, {255: 16}),          # qh[32 + 31] bits 6-7 -> 128 + 31 + 96
+    ({128 + 32: 0x03}, {128: 48}),          # qh[32] bits 0-1 -> element 128
+    ({0: 0x21, 128: 0xE4}, {0: 1, 32: 16, 64: 34, 96: 48}),
+]
+# Q4_K header: d = 0x3555, dmin = 0x2AAA, then the 12 scale bytes of
+#   scales 5, 17, 33, 62, 45, 28, 51, 12 and mins 9, 40, 3, 63, 22, 57, 36, 1:
+#   bytes 0-3: scale j (bits 0-5) | top two bits of scale j+4 (bits 6-7)
+#   bytes 4-7: min j (bits 0-5) | top two bits of min j+4 (bits 6-7)
+#   bytes 8-11: low 4 bits of scale j+4 | low 4 bits of min j+4 << 4
+Q4_K_HEADERS = [
+    ({0: 0x55, 1: 0x35, 2: 0xAA, 3: 0x2A, 4: 0x85, 5: 0x51, 6: 0xE1, 7: 0x3E, 8: 0x49, 9: 0xE8,
+      10: 0x83, 11: 0x3F, 12: 0x6D, 13: 0x9C, 14: 0x43, 15: 0x1C},
+     0x3555, 0x2AAA, [5, 17, 33, 62, 45, 28, 51, 12], [9, 40, 3, 63, 22, 57, 36, 1]),
+    ({4: 0xC0}, 0, 0, [0, 0, 0, 0, 48, 0, 0, 0], [0] * 8),    # top bits of scale 4 only
+    ({11: 0x80}, 0, 0, [0] * 8, [0, 0, 0, 0, 0, 0, 0, 32]),   # top bits of min 7 only
+    ({14: 0x5A}, 0, 0, [0, 0, 0, 0, 0, 0, 10, 0], [0, 0, 0, 0, 0, 0, 5, 0]),
+    ({6: 0x7F}, 0, 0, [0, 0, 63, 0, 0, 0, 16, 0], [0] * 8),   # scale 2 | top bit of scale 6
+]
+Q6_K_SCALES = [0xC0, 0x3F, 0xFF, 0x00, 0x11, 0xDF, 0x05, 0xF8,
+               0x80, 0x7F, 0x01, 0x02, 0xFE, 0x40, 0x9C, 0x2A]
+Q6_K_SCALE_VALUES = [-64, 63, -1, 0, 17, -33, 5, -8, -128, 127, 1, 2, -2, 64, -100, 42]
+
+
+def pin_layout_literal_blocks(lib):
+    for assign, exp in Q4_0_PROBES:
+        codes, d = oracle.unpack_q4_0(_block(18, assign), lib=lib)
+        assert np.array_equal(codes.astype(np.int64), _codes(32, exp)), ("q4_0", assign)
+        assert d == 0
+    codes, d = oracle.unpack_q4_0(_block(18, {0: 0x34, 1: 0x12}), lib=lib)
+    assert d == 0x1234 and not codes.any()
+    for assign, exp in Q8_0_PROBES:
+        codes, d = oracle.unpack_q8_0(_block(34, assign), lib=lib)
+        assert np.array_equal(codes.astype(np.int64), _codes(32, exp)), ("q8_0", assign)
+    codes, d = oracle.unpack_q8_0(_block(34, {0: 0x00, 1: 0x3C}), lib=lib)
+    assert d == 0x3C00 and not codes.any()
+    for assign, exp in Q4_K_PROBES:
+        codes, sc, mn, d, dmin = oracle.unpack_q4_k(_block(144, assign), lib=lib)
+        assert np.array_equal(codes.astype(np.int64), _codes(256, exp)), ("q4_k", assign)
+        assert not sc.any() and not mn.any() and d == 0 and dmin == 0
+    for assign, d_e, dmin_e, sc_e, mn_e in Q4_K_HEADERS:
+        codes, sc, mn, d, dmin = oracle.unpack_q4_k(_block(144, assign), lib=lib)
+        assert not codes.any()
+        assert d == d_e and dmin == dmin_e, ("q4_k header", assign)
+        assert list(sc) == sc_e and list(mn) == mn_e, ("q4_k scales/mins", assign, sc, mn)
+    for assign, exp in Q6_K_PROBES:
+        codes, sc, d = oracle.unpack_q6_k(_block(210, assign), lib=lib)
+        assert np.array_equal(codes.astype(np.int64), _codes(256, exp)), ("q6_k", assign)
+        assert not sc.any() and d == 0
+    hdr = {192 + i: v for i, v in enumerate(Q6_K_SCALES)}
+    hdr.update({208: 0x34, 209: 0x12})
+    codes, sc, d = oracle.unpack_q6_k(_block(210, hdr), lib=lib)
+    assert not codes.any() and d == 0x1234
+    assert list(sc.astype(int)) == Q6_K_SCALE_VALUES
+
+
+ALL_PINS.append(pin_layout_literal_blocks)
