@@ -73,6 +73,8 @@ extern "C" {
 
 typedef void* qgemv_stream_t;
 
+/* Status codes, numbered in the order the gates run (so the limits of this
+ * library, checked before alignment, come before QGEMV_E_ALIGN). */
 typedef enum {
     QGEMV_OK = 0,
     QGEMV_E_NULL = 1,        /* a required pointer is NULL */
@@ -95,13 +97,27 @@ enum {
 enum { QGEMV_VARIANT_AUTO = 0, QGEMV_VARIANT_DOT4 = 1, QGEMV_VARIANT_MFMA = 2 };
 
 /* Returns QGEMV_ABI_VERSION of the loaded library.  A caller built against a
- * different generation must refuse the library as a whole. */
+ * different generation must refuse the library as a whole rather than bind
+ * part of it (colibri GPU backends, the XDNA helper's ABI: a helper is usable
+ * only when it reports the expected ABI generation and exports every entry
+ * point the host requires; binding is all-or-nothing).  No arguments, no
+ * device access, never fails. */
 int qgemv_abi_version(void);
 
-/* Static, never-NULL name of a status code (unknown codes included). */
+/* Static, never-NULL name and one-line meaning of a status code; an unknown
+ * code gives "QGEMV_E_UNKNOWN: ...".  Each refusal has its own status because
+ * each has its own fix (colibri GPU backends, provisioning diagnostics: one
+ * named diagnostic per kind of failure; "Backends and hardware", section
+ * "CUDA": a backend declines with a message naming the reason).  The string
+ * belongs to the library and must not be freed; no device access. */
 const char* qgemv_status_str(int status);
 
-/* Static string: target architecture, formats and kernel variants built in. */
+/* Static string naming what this build carries: ABI generation, target
+ * architecture, weight formats, kernel variants and limits ("Backends and
+ * hardware", section "Environment": the version command prints the kernel
+ * sets, formats and architectures a given build actually carries, the first
+ * thing to check when a number looks wrong).  Owned by the library, never
+ * NULL, no device access. */
 const char* qgemv_build_info(void);
 
 /* Reason for the most recent non-OK status returned to the calling thread
@@ -121,6 +137,19 @@ const char* qgemv_last_error(void);
  * disarm before capturing a stream into a HIP graph.  Only this thread-local
  * pair is stored; returns QGEMV_OK. */
 qgemv_status qgemv_time_next_launch(void* start, void* stop);
+
+/* Measurement aid: reads `bytes` of device memory at buf once, with 16-byte
+ * loads spread over the whole device (wg_per_cu workgroups of 256 threads per
+ * compute unit, 1..32), and discards the data -- the plain streaming read
+ * whose rate the GEMV kernels, bound by streaming their weights, are compared
+ * with ("Running an LLM on VKNN", Performance: the decode step is
+ * weight-memory-bandwidth-bound).  nontemporal != 0 marks the loads
+ * non-temporal.  buf: 16-byte aligned, bytes a positive multiple of 16;
+ * sink: device uint32, written only in the (practically impossible) case
+ * that the folded data equal a fixed constant, so that no load can be
+ * elided.  No allocation; gates and errors as for the GEMVs. */
+qgemv_status qgemv_stream_read(const void* buf, int64_t bytes, int nontemporal,
+                               uint32_t* sink, int wg_per_cu, qgemv_stream_t stream);
 
 /* Activation quantisation ("Backends and hardware", section "CPU": quantised
  * to int8 once per matmul).  x: fp32 [M][ldx] with K valid columns
