@@ -42,7 +42,7 @@ WORKLOAD = ("llama3.1-8b decode step, batch 1: ffn gate|up q4_k 28672x4096 with 
             "(activation quantization inside the gate|up and lm_head launches; "
             "q6_k repacked at load into aligned 8-super-block tiles, same bytes)")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_q6k_lm_head.json")
-KERNEL_SOURCES = ["qgemv_device.h", "qgemv_quant.h", "k_gemv.hip", "k_quantize.hip",
+KERNEL_SOURCES = ["qgemv_device.h", "qgemv_quant.h", "k_gemv.h", "k_gemv.hip", "k_gemv_q6_k_r8.hip", "k_quantize.hip",
                   "qgemv_api.cpp"]
 
 
@@ -132,6 +132,10 @@ def main():
     ap.add_argument("--event-every", type=int, default=30,
                     help="bracket every n-th lm_head launch of the timed steps with HIP events "
                          "(each pair costs ~20 us of step time, so they are sampled)")
+    ap.add_argument("--roofline-steps", type=int, default=30,
+                    help="after the timed steps, this many more steps (same rotation) in which "
+                         "every lm_head launch records its own start/end events; the roofline's "
+                         "duration is their average")
     ap.add_argument("--small-m-profile", action="store_true",
                     help="only run the small-M products (Q4_K 14336x4096, Q6_K 4096x14336; "
                          "both variants at every M of SMALL_M_LIST), 20 calls each, for "
@@ -263,14 +267,26 @@ def main():
     ms_per_step = max(gpu_ms, wall_ms) / K
     value = step_wbytes / (ms_per_step * 1e-3) / 1e9
     # the lm_head kernel's own start/end events (qgemv_time_next_launch), and
-    # the bracket recorded on the stream around the same launch
-    head_us = [e.elapsed_ms(1) * 1e3 for e in evs if e is not None]
-    bracket_us = [e.elapsed_ms(0) * 1e3 for e in evs if e is not None]
+    # the bracket recorded on the stream around the same launch: sampled
+    # inside the timed steps ...
+    loop_us = [e.elapsed_ms(1) * 1e3 for e in evs if e is not None]
+    # ... and on every lm_head launch of a window of further steps (the same
+    # rotation continued), which the roofline's duration is read from
+    RW = max(5, args.roofline_steps)
+    evw = [HipTimer() for _ in range(RW)]
+    for i in range(RW):
+        step(K + i, evw[i])
+    torch.cuda.synchronize()
+    head_us = [e.elapsed_ms(1) * 1e3 for e in evw]
+    bracket_us = [e.elapsed_ms(0) * 1e3 for e in evw]
     head_avg_us = float(np.mean(head_us))
     bracket_avg_us = float(np.mean(bracket_us))
     log(f"[bench] step {ms_per_step * 1e3:.1f} us (events {gpu_ms / K * 1e3:.1f}, wall "
         f"{wall_ms / K * 1e3:.1f}); lm_head kernel avg {head_avg_us:.2f} us over "
-        f"{len(head_us)} timed launches (stream bracket {bracket_avg_us:.2f} us)")
+        f"{len(head_us)} event-timed launches after the timed steps (stream bracket "
+        f"{bracket_avg_us:.2f} us; {float(np.mean(loop_us)):.2f} us over {len(loop_us)} "
+        f"launches sampled inside them)")
+    read = read_kernel_rate(qg, torch, np, dev)
 
     # dominant kernel roofline: algorithmic bytes per launch of the lm_head GEMV
     # = N rows x (row weight bytes + 4 B output) + one activation row (codes,
@@ -278,22 +294,33 @@ def main():
     act_bytes = Kh + 2 * (Kh // 32) + 4 * (Kh // 32)
     head_alg = Nh * (synth.row_bytes("q6_k", Kh) + 4) + act_bytes + (0 if sep_quant else 4 * Kh)
     achieved = head_alg / (head_avg_us * 1e-6) / 1e9
-    traffic = None
+    traffic, traffic_src = None, None
     if os.path.exists(TRAFFIC_FILE):
         tr = json.load(open(TRAFFIC_FILE))
-        if tr.get("kernel_fingerprint") == kernel_fingerprint():
+        fp = kernel_fingerprint()
+        if tr.get("kernel_fingerprint") == fp:
             traffic = tr.get("bytes_per_launch")
+            traffic_src = (f"stored profile profiles/{os.path.basename(TRAFFIC_FILE)} "
+                           f"(rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE passes of an earlier "
+                           f"run, scaled by a 1 GiB copy; kernel source fingerprint {fp}), "
+                           f"not measured in this run")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                 "kernel": (("qgemv_q6_k lm_head 128256x4096" if args.native_q6k else
                             "qgemv_q6_k_r8 lm_head 128256x4096 (repacked Q6_K)") +
                            ("" if sep_quant else ", activation quantized in the launch "
                             "(qgemv_quantize_gemv)")),
+                "traffic_source": traffic_src,
                 "avg_us": round(head_avg_us, 2),
                 "timed_launches": len(head_us),
-                "timing": "kernel start/end events (qgemv_time_next_launch)",
+                "timing": ("kernel start/end events (qgemv_time_next_launch) on every lm_head "
+                           "launch of %d steps run right after the timed steps" % len(head_us)),
+                "in_loop_sampled_avg_us": round(float(np.mean(loop_us)), 2),
+                "in_loop_sampled_launches": len(loop_us),
                 "stream_bracket_avg_us": round(bracket_avg_us, 2),
-                "alg_bytes_per_launch": head_alg}
+                "alg_bytes_per_launch": head_alg,
+                "achievable_read_GBps": read["GBps"],
+                "frac_of_achievable_read": round(achieved / read["GBps"], 4)}
 
     extra = {}
     if not args.no_extra:
@@ -328,12 +355,49 @@ def main():
                    "weight_bytes_per_step": step_wbytes, "weight_copies_rotated": R,
                    "steps_per_s": round(1e3 / ms_per_step, 1)},
         "hbm_peak_frac": round(value / HBM_PEAK_GBPS, 4),
+        "read_kernel": read,
+        "read_kernel_frac": round(value / read["GBps"], 4),
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
     if extra:
         out["extra"] = extra
     print(json.dumps(out), flush=True)
+
+
+def read_kernel_rate(qg, torch, np, dev, gib=1, reps=5):
+    """The achievable HBM read rate on this device: qgemv_stream_read (plain
+    16-byte streaming loads, non-temporal and ordinary, 2 or 4 workgroups per
+    compute unit) over `gib` GiB, timed with events around each read after
+    two warm-up reads; the best configuration's median."""
+    nbytes = gib << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    buf.random_(0, 256)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    res = {}
+    for nt in (1, 0):
+        for wpc in (2, 4):
+            for _ in range(2):
+                qg.qgemv_stream_read(buf, nbytes, nt, sink, wpc)
+            per = []
+            for _ in range(reps):
+                a = torch.cuda.Event(enable_timing=True)
+                b = torch.cuda.Event(enable_timing=True)
+                a.record()
+                qg.qgemv_stream_read(buf, nbytes, nt, sink, wpc)
+                b.record()
+                torch.cuda.synchronize()
+                per.append(a.elapsed_time(b) * 1e-3)
+            res[(nt, wpc)] = nbytes / float(np.median(per)) / 1e9
+    del buf
+    best = max(res, key=res.get)
+    out = {"GBps": round(res[best], 1), "bytes": nbytes,
+           "config": {"nontemporal": bool(best[0]), "wg_per_cu": best[1]},
+           "all_GBps": {f"{'nt' if k[0] else 'plain'}_wg{k[1]}": round(v, 1)
+                        for k, v in res.items()},
+           "kernel": "qgemv_stream_read: 16-byte loads, 8 per thread in flight, grid-stride"}
+    log(f"[bench] read kernel {out['GBps']} GB/s ({out['all_GBps']})")
+    return out
 
 
 def small_m_profile(qg, torch, np, synth, dev):
@@ -860,10 +924,12 @@ def oracle_parallel(np, c2, c3, step_wbytes, seconds=3.0):
     import oracle
     from concurrent.futures import ThreadPoolExecutor
     try:
-        T = len(os.sched_getaffinity(0))
+        avail = len(os.sched_getaffinity(0))
     except AttributeError:
-        T = os.cpu_count() or 1
-    T = max(1, min(16, T))
+        avail = os.cpu_count() or 1
+    # at most 16 threads: the host CPU share that goes with one GPU on the
+    # machines this runs on, whatever the affinity mask shows
+    T = max(1, min(16, avail))
     Ngu, Kgu, Nd, Kd = c2["N_gu"], c2["K_gu"], c2["N_down"], c2["K_down"]
     Nh, Kh = c3["N"], c3["K"]
 
@@ -890,9 +956,11 @@ def oracle_parallel(np, c2, c3, step_wbytes, seconds=3.0):
                 break
     per = float(np.median(times))
     return {"value": round(step_wbytes / per / 1e9, 4), "unit": "GB/s", "cores": T,
+            "cores_in_affinity_mask": avail,
             "ms_per_step": round(per * 1e3, 1),
-            "sample": f"{len(times)} whole steps, each GEMV's rows split over {T} threads, "
-                      f"median step time"}
+            "sample": f"{len(times)} whole steps, each GEMV's rows split over {T} threads "
+                      f"(capped at 16, the host CPU share of one GPU; {avail} in the affinity "
+                      f"mask), median step time"}
 
 
 def oracle_rates(np, synth, c2, c3, seconds=0.3):

@@ -41,7 +41,7 @@ QGEMV_M_MAX = 64
 # Every extern "C" symbol that include/qgemv.h declares.
 EXPORTS = [
     "qgemv_abi_version", "qgemv_status_str", "qgemv_build_info", "qgemv_last_error",
-    "qgemv_time_next_launch",
+    "qgemv_time_next_launch", "qgemv_stream_read",
     "qgemv_quantize_act", "qgemv_q4_0", "qgemv_q4_k", "qgemv_q6_k", "qgemv_q8_0",
     "qgemv_q6_k_repack", "qgemv_q6_k_r8",
     "qgemm_q4_k_small_m", "qgemm_q6_k_small_m", "qgemm_q4_0_small_m",
@@ -158,6 +158,16 @@ def qgemv_time_next_launch(start=None, stop=None):
     """start, stop: hipEvent_t handles (int or ctypes.c_void_p) or None."""
     return _check(_lib.qgemv_time_next_launch(_handle(start), _handle(stop)),
                   "qgemv_time_next_launch")
+
+
+_lib.qgemv_stream_read.restype = _I
+_lib.qgemv_stream_read.argtypes = [_P, _I64, _I, _P, _I, _P]
+
+
+def qgemv_stream_read(buf, nbytes, nontemporal, sink, wg_per_cu=4, stream=None):
+    """Measurement aid: one streaming read of nbytes of buf (see the header)."""
+    return _check(_lib.qgemv_stream_read(_ptr(buf), nbytes, int(nontemporal), _ptr(sink),
+                                         wg_per_cu, _stream(stream)), "qgemv_stream_read")
 
 
 def qgemv_quantize_act(x, M, K, ldx, q, d, s, stream=None):

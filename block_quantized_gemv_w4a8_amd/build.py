@@ -22,11 +22,13 @@ CSRC = os.path.join(HERE, "csrc")
 LIB_DIR = os.path.join(HERE, "_lib")
 LIB = os.path.join(LIB_DIR, "libqgemv.so")
 
-SOURCES = ["qgemv_api.cpp", "k_quantize.hip", "k_gemv.hip", "k_small_m.hip"]
+SOURCES = ["qgemv_api.cpp", "k_quantize.hip", "k_gemv.hip", "k_gemv_q4_0.hip", "k_gemv_q4_k.hip",
+           "k_gemv_q6_k.hip", "k_gemv_q6_k_r8.hip", "k_gemv_q8_0.hip", "k_small_m.hip",
+           "k_measure.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-fno-fast-math", "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
@@ -37,24 +39,46 @@ FLAGS = [
 ]
 
 
-def build(force: bool = True, verbose: bool = False) -> str:
-    if not force and os.path.exists(LIB):
-        return LIB
-    os.makedirs(LIB_DIR, exist_ok=True)
-    tmp = LIB + ".tmp%d" % os.getpid()
-    srcs = []
-    for s in SOURCES:
-        p = os.path.join(CSRC, s)
-        # .cpp files include the HIP runtime: compile them as HIP as well
-        srcs += (["-x", "hip", p, "-x", "none"] if s.endswith(".cpp") else [p])
-    cmd = [HIPCC, *FLAGS, "-o", tmp, *srcs]
+def _compile(src: str, obj: str, verbose: bool) -> None:
+    # .cpp files include the HIP runtime: compile them as HIP as well
+    lang = ["-x", "hip"] if src.endswith(".cpp") else []
+    cmd = [HIPCC, *FLAGS, "-c", *lang, src, "-o", obj]
     if verbose:
         print(" ".join(cmd), file=sys.stderr)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
-        raise RuntimeError("hipcc failed building libqgemv.so")
-    os.replace(tmp, LIB)
+        raise RuntimeError(f"hipcc failed on {os.path.basename(src)}")
+
+
+def build(force: bool = True, verbose: bool = False) -> str:
+    """Compile every source to an object (in parallel), then link the library."""
+    if not force and os.path.exists(LIB):
+        return LIB
+    from concurrent.futures import ThreadPoolExecutor
+    obj_dir = os.path.join(LIB_DIR, "obj")
+    os.makedirs(obj_dir, exist_ok=True)
+    tag = "%d" % os.getpid()
+    objs = [os.path.join(obj_dir, os.path.splitext(s)[0] + "." + tag + ".o") for s in SOURCES]
+    try:
+        with ThreadPoolExecutor(len(SOURCES)) as pool:
+            futs = [pool.submit(_compile, os.path.join(CSRC, s), o, verbose)
+                    for s, o in zip(SOURCES, objs)]
+            for f in futs:
+                f.result()
+        tmp = LIB + ".tmp" + tag
+        cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
+        if verbose:
+            print(" ".join(cmd), file=sys.stderr)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            sys.stderr.write(r.stdout + r.stderr)
+            raise RuntimeError("hipcc failed linking libqgemv.so")
+        os.replace(tmp, LIB)
+    finally:
+        for o in objs:
+            if os.path.exists(o):
+                os.remove(o)
     return LIB
 
 

@@ -275,6 +275,24 @@ qgemv_status qgemv_time_next_launch(void* start, void* stop) {
     return QGEMV_OK;
 }
 
+qgemv_status qgemv_stream_read(const void* buf, int64_t bytes, int nontemporal, uint32_t* sink,
+                               int wg_per_cu, qgemv_stream_t stream) {
+    const char* name = "qgemv_stream_read";
+    if (!buf || !sink) return fail(QGEMV_E_NULL, "%s: NULL pointer argument", name);
+    if (bytes < 16 || bytes % 16 != 0)
+        return fail(QGEMV_E_SHAPE, "%s: bytes = %lld must be a positive multiple of 16", name,
+                    (long long)bytes);
+    if (wg_per_cu < 1 || wg_per_cu > 32)
+        return fail(QGEMV_E_UNSUPPORTED, "%s: wg_per_cu = %d outside 1..32", name, wg_per_cu);
+    if (!aligned(buf, 16)) return fail(QGEMV_E_ALIGN, "%s: buf must be 16-byte aligned", name);
+    if (!aligned(sink, 4)) return fail(QGEMV_E_ALIGN, "%s: sink must be 4-byte aligned", name);
+    qgemv_status st = check_device();
+    if (st != QGEMV_OK) return st;
+    return launched(qgemv::launch_stream_read(buf, bytes, nontemporal, sink, wg_per_cu,
+                                              (hipStream_t)stream),
+                    name);
+}
+
 qgemv_status qgemv_quantize_act(const float* x, int64_t M, int64_t K, int64_t ldx, int8_t* q,
                                 uint16_t* d, int32_t* s, qgemv_stream_t stream) {
     if (M < 0) return fail(QGEMV_E_SHAPE, "qgemv_quantize_act: M = %lld is negative", (long long)M);

@@ -106,4 +106,10 @@ hipError_t launch_small_m(int fmt, const void* w, int64_t N, int64_t K, int64_t 
                           const int8_t* q, const uint16_t* d, const int32_t* s, float* y,
                           int variant, hipStream_t st);
 
+// Measurement aid: a plain streaming read of `bytes` (a multiple of 16) at
+// buf with 16-byte loads (non-temporal if asked), wg_per_cu workgroups per
+// compute unit.
+hipError_t launch_stream_read(const void* buf, int64_t bytes, int nontemporal, uint32_t* sink,
+                              int wg_per_cu, hipStream_t st);
+
 }  // namespace qgemv

@@ -227,3 +227,18 @@ def test_device_gate_without_gpu():
     assert qg.qgemv_last_error()
     with pytest.raises(qg.QgemvError):
         qg.qgemv_q6_k(A, 10, 256, A, A, A, A, stream=0)
+
+
+def test_gates_stream_read():
+    """The streaming-read measurement aid: NULL, size, limit and alignment
+    gates, before any device work."""
+    qg = _lib()
+    R = "qgemv_stream_read"   # buf, bytes, nontemporal, sink, wg_per_cu, stream
+    assert _status(R, None, 1 << 20, 1, A, 4, 0) == qg.QGEMV_E_NULL
+    assert _status(R, A, 1 << 20, 1, None, 4, 0) == qg.QGEMV_E_NULL
+    assert _status(R, A, 0, 1, A, 4, 0) == qg.QGEMV_E_SHAPE
+    assert _status(R, A, 24, 1, A, 4, 0) == qg.QGEMV_E_SHAPE
+    assert _status(R, A, 1 << 20, 1, A, 0, 0) == qg.QGEMV_E_UNSUPPORTED
+    assert _status(R, A, 1 << 20, 1, A, 33, 0) == qg.QGEMV_E_UNSUPPORTED
+    assert _status(R, A + 8, 1 << 20, 1, A, 4, 0) == qg.QGEMV_E_ALIGN
+    assert _status(R, A, 1 << 20, 1, A + 2, 4, 0) == qg.QGEMV_E_ALIGN

@@ -63,6 +63,9 @@ def run_multi(qg, fmt, ns, K, seed, quantize_in_launch=False):
     ("q4_k", [3, 5, 7, 11, 13, 17, 19, 23], 512),   # QGEMV_MULTI_MAX matrices
     ("q4_k", [300, 200], 4096),              # long rows: one launch per matrix
     ("q6_k", [64, 65], 14336),
+    ("q4_k", [0, 300], 4096),                # long rows, empty first matrix
+    ("q6_k", [0, 64], 14336),
+    ("q4_0", [0, 0, 40], 2048),              # short rows, empty first matrices
 ])
 @pytest.mark.parametrize("xq", [False, True])
 def test_multi(qg, fmt, ns, K, xq):

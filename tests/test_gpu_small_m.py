@@ -61,7 +61,7 @@ def test_small_m_shapes(qg, fmt, M, N, K):
 # or 32 weight rows, one per bucket of M; every output against the oracle.
 WIDE = [("q4_k", 8, 1024), ("q4_k", 20, 1024), ("q4_k", 40, 1024), ("q4_k", 64, 1024),
         ("q6_k", 8, 1024), ("q6_k", 24, 1024), ("q6_k", 33, 1024), ("q6_k", 64, 1024),
-        ("q4_0", 17, 1056), ("q4_0", 64, 1056)]
+        ("q4_0", 8, 1056), ("q4_0", 17, 1056), ("q4_0", 40, 1056), ("q4_0", 64, 1056)]
 
 
 @pytest.mark.parametrize("fmt,M,K", WIDE)
