@@ -94,7 +94,19 @@ enum {
     QGEMV_FMT_Q8_0 = 3,
     QGEMV_FMT_Q6_K_R8 = 4
 };
-enum { QGEMV_VARIANT_AUTO = 0, QGEMV_VARIANT_DOT4 = 1, QGEMV_VARIANT_MFMA = 2 };
+/* Small-M variants.  QGEMV_VARIANT_MFMA runs the int8 matrix cores with the
+ * faster of two kernels for the format, shape and bucket of M (measured);
+ * QGEMV_VARIANT_MFMA_STAGED forces the kernel that stages every K step of
+ * weights and activation through LDS, QGEMV_VARIANT_MFMA_STREAM the one in
+ * which every wave streams its own weight rows into registers and only the
+ * activation is shared through LDS.  All compute the same products. */
+enum {
+    QGEMV_VARIANT_AUTO = 0,
+    QGEMV_VARIANT_DOT4 = 1,
+    QGEMV_VARIANT_MFMA = 2,
+    QGEMV_VARIANT_MFMA_STAGED = 3,
+    QGEMV_VARIANT_MFMA_STREAM = 4
+};
 
 /* Returns QGEMV_ABI_VERSION of the loaded library.  A caller built against a
  * different generation must refuse the library as a whole rather than bind

@@ -28,7 +28,8 @@ def small_m(qg, fmt, wd, N, K, act, M, variant):
 
 
 def variants(qg):
-    return [qg.QGEMV_VARIANT_DOT4, qg.QGEMV_VARIANT_MFMA, qg.QGEMV_VARIANT_AUTO]
+    return [qg.QGEMV_VARIANT_DOT4, qg.QGEMV_VARIANT_MFMA, qg.QGEMV_VARIANT_AUTO,
+            qg.QGEMV_VARIANT_MFMA_STAGED, qg.QGEMV_VARIANT_MFMA_STREAM]
 
 
 SHAPES = [(1, 100, 256), (2, 65, 896), (3, 257, 4096), (5, 64, 4864), (8, 300, 4096),
@@ -74,7 +75,8 @@ def test_small_m_wide_matrices(qg, fmt, M, K):
     q, d, s = act_host(*act)
     wd = dev(w)
     Y_ref, TT = oracle.gemm(fmt, w, N, K, q, d, s)
-    for v in (qg.QGEMV_VARIANT_MFMA, qg.QGEMV_VARIANT_AUTO):
+    for v in (qg.QGEMV_VARIANT_MFMA, qg.QGEMV_VARIANT_AUTO, qg.QGEMV_VARIANT_MFMA_STAGED,
+              qg.QGEMV_VARIANT_MFMA_STREAM):
         say("small_m wide", fmt, M, N, K, "variant", v)
         Y = small_m(qg, fmt, wd, N, K, act, M, v)
         check_y(Y.reshape(-1), Y_ref.reshape(-1), TT.reshape(-1),
@@ -147,7 +149,8 @@ def test_row_independence(qg, fmt):
     x, _ = synth.activation(g, M, K)
     wd = dev(w)
     q, d, s = quantize(qg, x)
-    for v in (qg.QGEMV_VARIANT_DOT4, qg.QGEMV_VARIANT_MFMA):
+    for v in (qg.QGEMV_VARIANT_DOT4, qg.QGEMV_VARIANT_MFMA, qg.QGEMV_VARIANT_MFMA_STAGED,
+              qg.QGEMV_VARIANT_MFMA_STREAM):
         Y = small_m(qg, fmt, wd, N, K, (q, d, s), M, v)
         for m in (0, 3, 7):
             Ym = small_m(qg, fmt, wd, N, K, (q[m:m + 1], d[m:m + 1], s[m:m + 1]), 1, v)
@@ -193,3 +196,48 @@ def test_wide_shapes(qg, fmt, M, N, K):
     say("small_m wide", fmt, M, N, K)
     Y = small_m(qg, fmt, dev(w), N, K, act, M, qg.QGEMV_VARIANT_MFMA)
     check_y(Y[:, rows].reshape(-1), Y_ref.reshape(-1), TT.reshape(-1), f"wide {fmt} M={M} N={N} K={K}")
+
+
+# Every bucket edge of M on both matrix widths, with ragged tiles (N not a
+# multiple of 64) and, for Q4_0, K not a multiple of 256 (a partial last unit).
+EDGE_M = [1, 2, 7, 8, 9, 16, 17, 32, 33, 48, 49, 64]
+
+
+@pytest.mark.parametrize("fmt", ["q4_k", "q6_k", "q4_0"])
+@pytest.mark.parametrize("wide", [False, True])
+def test_small_m_bucket_edges(qg, fmt, wide):
+    N = 8200 if wide else 600
+    K = 1056 if fmt == "q4_0" else 1280
+    g = np.random.default_rng(N + K + len(fmt))
+    w = WEIGHTS[fmt](g, N, K)
+    wd = dev(w)
+    x64, _ = synth.activation(g, 64, K)
+    windows = [(0, 96), (N // 2, 40), (N - 70, 70)]
+    for M in EDGE_M:
+        act = quantize(qg, x64[:M])
+        rows, Y_ref, TT = sampled(fmt, w, N, K, act_host(*act), windows)
+        say("small_m edges", fmt, "wide" if wide else "narrow", M)
+        for v in (qg.QGEMV_VARIANT_MFMA_STREAM, qg.QGEMV_VARIANT_MFMA_STAGED):
+            Y = small_m(qg, fmt, wd, N, K, act, M, v)
+            assert np.all(np.isfinite(Y))
+            check_y(Y[:, rows].reshape(-1), Y_ref.reshape(-1), TT.reshape(-1),
+                    f"edges {fmt} wide={wide} M={M} v={v}")
+
+
+@pytest.mark.parametrize("fmt", ["q4_k", "q6_k", "q4_0"])
+def test_small_m_deterministic_and_row_independent(qg, fmt):
+    """Same inputs, same bits; row m of an M-row call equals a call on that
+    row alone within the same bucket of M."""
+    g = np.random.default_rng(77)
+    N, K = 8256, 2048
+    w = WEIGHTS[fmt](g, N, K)
+    wd = dev(w)
+    x, _ = synth.activation(g, 8, K)
+    q, d, s = quantize(qg, x)
+    for v in (qg.QGEMV_VARIANT_MFMA_STREAM, qg.QGEMV_VARIANT_MFMA):
+        Y1 = small_m(qg, fmt, wd, N, K, (q, d, s), 8, v)
+        Y2 = small_m(qg, fmt, wd, N, K, (q, d, s), 8, v)
+        assert np.array_equal(Y1.view(np.uint32), Y2.view(np.uint32))
+        for m in (0, 5, 7):
+            Ym = small_m(qg, fmt, wd, N, K, (q[m:m + 1], d[m:m + 1], s[m:m + 1]), 1, v)
+            assert np.array_equal(Y1[m].view(np.uint32), Ym[0].view(np.uint32)), (fmt, v, m)
