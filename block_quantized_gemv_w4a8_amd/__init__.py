@@ -48,7 +48,7 @@ EXPORTS = [
     "qgemm_q4_k_small_m", "qgemm_q6_k_small_m", "qgemm_q4_0_small_m",
     "qgemv_silu_mul_quantize", "qgemv_q4_k_swiglu_quantize",
     "qgemv_quantize_gemv", "qgemv_quantize_q4_k_swiglu", "qgemv_multi", "qgemv_quantize_multi",
-    "qgemv_block_dots",
+    "qgemv_block_dots", "qgemv_block_dots_staged",
 ]
 
 _P, _I64, _I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
@@ -84,6 +84,8 @@ _lib.qgemv_quantize_multi.restype = _I
 _lib.qgemv_quantize_multi.argtypes = [_I, _I, _P, _P, _I64, _P, _P, _P, _P, _P, _P]
 _lib.qgemv_block_dots.restype = _I
 _lib.qgemv_block_dots.argtypes = [_I, _P, _I64, _I64, _I64, _I64, _P, _P, _P]
+_lib.qgemv_block_dots_staged.restype = _I
+_lib.qgemv_block_dots_staged.argtypes = [_I, _P, _I64, _I64, _I64, _I64, _P, _P, _P, _I, _P, _P]
 
 if _lib.qgemv_abi_version() != 1:
     raise ImportError("libqgemv ABI generation mismatch (expected 1)")
@@ -288,6 +290,12 @@ def qgemv_quantize_multi(fmt, ws, ns, K, x, q, d, s, ys, stream=None):
 def qgemv_block_dots(fmt, w, N, K, row0, nrows, q, dots, stream=None):
     return _check(_lib.qgemv_block_dots(fmt, _ptr(w), N, K, row0, nrows, _ptr(q), _ptr(dots),
                                         _stream(stream)), "qgemv_block_dots")
+
+
+def qgemv_block_dots_staged(fmt, w, N, K, row0, nrows, q, d, s, wk, dots, stream=None):
+    return _check(_lib.qgemv_block_dots_staged(fmt, _ptr(w), N, K, row0, nrows, _ptr(q), _ptr(d),
+                                               _ptr(s), wk, _ptr(dots), _stream(stream)),
+                  "qgemv_block_dots_staged")
 
 
 GEMV = {"q4_0": qgemv_q4_0, "q4_k": qgemv_q4_k, "q6_k": qgemv_q6_k, "q8_0": qgemv_q8_0,

@@ -117,6 +117,175 @@ __global__ __launch_bounds__(WG) void k_block_dots(const uint8_t* __restrict__ w
     }
 }
 
+// The integer block dots of one unit from its loaded fields and its
+// activation registers: the dot functions that Unit<FMT>::term calls, with
+// the ints kept.  NB blocks per unit; blk(u, j) is the output column of
+// block j of unit u.
+template <int FMT>
+struct UnitDots;
+template <>
+struct UnitDots<QGEMV_FMT_Q4_K> {
+    static constexpr int NB = 2;
+    __device__ static void dots(const Q4K::W& w, const ActReg<QGEMV_FMT_Q4_K>& a, int D[4]) {
+        Q4K::dots(w, a.x, D);
+    }
+    __device__ static int blk(int u, int j) { return 2 * u + j; }
+};
+template <>
+struct UnitDots<QGEMV_FMT_Q6_K> {
+    static constexpr int NB = 4;
+    __device__ static void dots(const Q6K::W& w, const ActReg<QGEMV_FMT_Q6_K>& a, int D[4]) {
+        Q6K::dots(w, a.x, a.init, D);
+    }
+    __device__ static int blk(int u, int j) { return Q6K::act_offset(u, j) >> 4; }
+};
+template <>
+struct UnitDots<QGEMV_FMT_Q6_K_R8> : UnitDots<QGEMV_FMT_Q6_K> {};
+template <>
+struct UnitDots<QGEMV_FMT_Q4_0> {
+    static constexpr int NB = 2;
+    __device__ static void dots(const Q40::W& w, const ActReg<QGEMV_FMT_Q4_0>& a, int D[4]) {
+        Q40::dots(w, a.x, a.init, D);
+    }
+    __device__ static int blk(int u, int j) { return 2 * u + j; }
+};
+template <>
+struct UnitDots<QGEMV_FMT_Q8_0> {
+    static constexpr int NB = 2;
+    __device__ static void dots(const Q80::W& w, const ActReg<QGEMV_FMT_Q8_0>& a, int D[4]) {
+        Q80::dots(w, a.x, D);
+    }
+    __device__ static int blk(int u, int j) { return 2 * u + j; }
+};
+
+// Block-dots validation through the LDS-streaming path: one wave per (row,
+// split-K slice), the slice split, staged, parked in LDS and read back by the
+// same SliceStream and UnitLds code as k_gemv_lds and k_gemv_dyn (16-byte
+// chunk grid, shifted last chunk, misaligned-field readers, empty last
+// slice), the activation in the same registers; only the last step differs:
+// the unit's integer dots are stored instead of scaled.  Lanes past the
+// slice and blocks past K store nothing.
+template <int FMT, int UPL, int NL>
+__global__ __launch_bounds__(WG) void k_block_dots_staged(const uint8_t* __restrict__ w,
+                                                           int64_t row0, int64_t nrows, int U,
+                                                           int US, int WK, int nbw,
+                                                           int row_bytes, int buf_bytes, int nblk,
+                                                           const int8_t* __restrict__ q,
+                                                           const uint16_t* __restrict__ d,
+                                                           const int32_t* __restrict__ s,
+                                                           int32_t* __restrict__ dots) {
+    extern __shared__ __align__(16) uint8_t lds[];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t t = (int64_t)blockIdx.x * (WG / 64) + wave;
+    if (t >= nrows * WK) return;   // whole waves; no workgroup barrier follows
+    const int64_t rr = t / WK;
+    const int kq = (int)(t % WK);
+    SliceStream<FMT, UPL, NL, kStreamNT> ss(lane, U, US, kq, nbw, row_bytes);
+    ss.load_act(q, d, s);
+    u32x4 R[NL];
+    const int delta = ss.stage(R, w + (row0 + rr) * (int64_t)row_bytes);
+    uint8_t* buf = lds + wave * buf_bytes;
+    ss.commit(R, delta, buf);
+    int32_t* out = dots + rr * nblk;
+#pragma unroll
+    for (int i = 0; i < UPL; i++) {
+        typename Unit<FMT>::W wv;
+        UnitLds<FMT>::load(buf, delta, ss.ul[i], ss.has1[i], wv);
+        int D[4];
+        UnitDots<FMT>::dots(wv, ss.A[i], D);
+        const int u = ss.u_lo + ss.ul[i];
+        constexpr bool PAIR = FMT == QGEMV_FMT_Q4_0 || FMT == QGEMV_FMT_Q8_0;
+        if (ss.ok[i]) {
+#pragma unroll
+            for (int j = 0; j < UnitDots<FMT>::NB; j++)
+                if (!PAIR || j == 0 || ss.has1[i]) out[UnitDots<FMT>::blk(u, j)] = D[j];
+        }
+    }
+}
+
+template <int FMT>
+static int staged_nl(int64_t K, int WK, int& US, int& buf_bytes, int& upl) {
+    const int U = units_of(FMT, K);
+    const SliceGeom g = slice_geom<FMT>(K, U, WK);
+    US = g.US;
+    buf_bytes = 16 * g.nchunk + 16;
+    upl = (US + 63) / 64;
+    return (g.nchunk + 63) / 64;
+}
+
+template <int FMT>
+static bool staged_ok(int64_t K, int WK) {
+    int US, bb, upl;
+    const int nl = staged_nl<FMT>(K, WK, US, bb, upl);
+    return upl <= 2 && nl <= 8;
+}
+
+bool block_dots_staged_supported(int fmt, int64_t K, int wk) {
+    if (wk != 1 && wk != 2 && wk != 4) return false;
+    switch (fmt) {
+    case QGEMV_FMT_Q4_0: return staged_ok<QGEMV_FMT_Q4_0>(K, wk);
+    case QGEMV_FMT_Q4_K: return staged_ok<QGEMV_FMT_Q4_K>(K, wk);
+    case QGEMV_FMT_Q6_K: return staged_ok<QGEMV_FMT_Q6_K>(K, wk);
+    case QGEMV_FMT_Q6_K_R8: return staged_ok<QGEMV_FMT_Q6_K_R8>(K, wk);
+    default: return staged_ok<QGEMV_FMT_Q8_0>(K, wk);
+    }
+}
+
+template <int FMT, int UPL, int NL>
+static void launch_staged_cfg(const uint8_t* w, int64_t K, int64_t row0, int64_t nrows, int WK,
+                              int US, int buf_bytes, int nblk, const int8_t* q,
+                              const uint16_t* d, const int32_t* s, int32_t* dots,
+                              hipStream_t st) {
+    const int64_t grid = (nrows * WK + WG / 64 - 1) / (WG / 64);
+    launch_kernel(k_block_dots_staged<FMT, UPL, NL>, dim3((unsigned)grid), dim3(WG),
+                  (unsigned)(WG / 64 * buf_bytes), st, w, row0, nrows, units_of(FMT, K), US, WK,
+                  (int)(K / 32), row_bytes_of(FMT, K), buf_bytes, nblk, q, d, s, dots);
+}
+
+template <int FMT>
+static hipError_t launch_staged_fmt(const uint8_t* w, int64_t K, int64_t row0, int64_t nrows,
+                                    int WK, int nblk, const int8_t* q, const uint16_t* d,
+                                    const int32_t* s, int32_t* dots, hipStream_t st) {
+    int US, bb, upl;
+    const int nl = staged_nl<FMT>(K, WK, US, bb, upl);
+    if (upl > 2 || nl > 8) return hipErrorInvalidValue;
+    // more chunks per lane than a slice needs only repeat its last chunk
+    if (upl == 1 && nl <= 2)
+        launch_staged_cfg<FMT, 1, 2>(w, K, row0, nrows, WK, US, bb, nblk, q, d, s, dots, st);
+    else if (upl == 1 && nl <= 4)
+        launch_staged_cfg<FMT, 1, 4>(w, K, row0, nrows, WK, US, bb, nblk, q, d, s, dots, st);
+    else if (upl == 1)
+        launch_staged_cfg<FMT, 1, 8>(w, K, row0, nrows, WK, US, bb, nblk, q, d, s, dots, st);
+    else if (nl <= 4)
+        launch_staged_cfg<FMT, 2, 4>(w, K, row0, nrows, WK, US, bb, nblk, q, d, s, dots, st);
+    else
+        launch_staged_cfg<FMT, 2, 8>(w, K, row0, nrows, WK, US, bb, nblk, q, d, s, dots, st);
+    return hipGetLastError();
+}
+
+hipError_t launch_block_dots_staged(int fmt, const void* w, int64_t K, int64_t row0,
+                                    int64_t nrows, const int8_t* q, const uint16_t* d,
+                                    const int32_t* s, int wk, int32_t* dots, hipStream_t st) {
+    const int64_t Kp = (K + 255) / 256 * 256;
+    const int nblk = (fmt == QGEMV_FMT_Q6_K || fmt == QGEMV_FMT_Q6_K_R8)
+                         ? (int)(Kp / 16)
+                         : (fmt == QGEMV_FMT_Q4_K ? (int)(Kp / 32) : (int)(K / 32));
+    const uint8_t* wp = (const uint8_t*)w;
+    switch (fmt) {
+    case QGEMV_FMT_Q4_0:
+        return launch_staged_fmt<QGEMV_FMT_Q4_0>(wp, K, row0, nrows, wk, nblk, q, d, s, dots, st);
+    case QGEMV_FMT_Q4_K:
+        return launch_staged_fmt<QGEMV_FMT_Q4_K>(wp, K, row0, nrows, wk, nblk, q, d, s, dots, st);
+    case QGEMV_FMT_Q6_K:
+        return launch_staged_fmt<QGEMV_FMT_Q6_K>(wp, K, row0, nrows, wk, nblk, q, d, s, dots, st);
+    case QGEMV_FMT_Q6_K_R8:
+        return launch_staged_fmt<QGEMV_FMT_Q6_K_R8>(wp, K, row0, nrows, wk, nblk, q, d, s, dots,
+                                                    st);
+    default:
+        return launch_staged_fmt<QGEMV_FMT_Q8_0>(wp, K, row0, nrows, wk, nblk, q, d, s, dots, st);
+    }
+}
+
 // Q6_K -> Q6_K_R8: one thread per (row, tile slot); a slot past the row's
 // super-blocks (the rest of a partial last tile) is written as zeros.  The
 // native super-block is 2-byte aligned, so it is copied as 16-bit words.

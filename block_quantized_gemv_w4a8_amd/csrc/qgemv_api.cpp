@@ -478,4 +478,36 @@ qgemv_status qgemv_block_dots(int fmt, const void* w, int64_t N, int64_t K, int6
                     name);
 }
 
+qgemv_status qgemv_block_dots_staged(int fmt, const void* w, int64_t N, int64_t K,
+                                     int64_t row0, int64_t nrows, const int8_t* q,
+                                     const uint16_t* d, const int32_t* s, int wk,
+                                     int32_t* dots, qgemv_stream_t stream) {
+    const char* name = "qgemv_block_dots_staged";
+    if (N < 0 || row0 < 0 || nrows < 0 || row0 > N || nrows > N - row0)
+        return fail(QGEMV_E_SHAPE, "%s: rows [%lld, %lld) outside [0, %lld)", name,
+                    (long long)row0, (long long)(row0 + nrows), (long long)N);
+    if (nrows == 0) return ok();
+    if (!w || !q || !d || !s || !dots)
+        return fail(QGEMV_E_NULL, "%s: NULL pointer argument", name);
+    qgemv_status st = check_k(K);
+    if (st != QGEMV_OK) return st;
+    if (fmt < QGEMV_FMT_Q4_0 || fmt > QGEMV_FMT_Q6_K_R8)
+        return fail(QGEMV_E_UNSUPPORTED, "%s: unknown format %d", name, fmt);
+    if (K > QGEMV_K_MAX) return fail(QGEMV_E_UNSUPPORTED, "%s: K exceeds QGEMV_K_MAX", name);
+    if (nrows * 4 >= ((int64_t)1 << 31))
+        return fail(QGEMV_E_UNSUPPORTED, "%s: too many rows for one launch", name);
+    if (!qgemv::block_dots_staged_supported(fmt, K, wk))
+        return fail(QGEMV_E_UNSUPPORTED,
+                    "%s: split-K width %d with K = %lld has no staged configuration (wk in "
+                    "1, 2, 4; at most 128 units per slice)",
+                    name, wk, (long long)K);
+    if (!aligned(w, 16)) return fail(QGEMV_E_ALIGN, "%s: w must be 16-byte aligned", name);
+    if ((st = check_act_align(q, d, s)) != QGEMV_OK) return st;
+    if (!aligned(dots, 4)) return fail(QGEMV_E_ALIGN, "%s: dots must be 4-byte aligned", name);
+    if ((st = check_device()) != QGEMV_OK) return st;
+    return launched(qgemv::launch_block_dots_staged(fmt, w, K, row0, nrows, q, d, s, wk, dots,
+                                                    (hipStream_t)stream),
+                    name);
+}
+
 }  // extern "C"

@@ -97,6 +97,12 @@ hipError_t launch_quantize_q4k_swiglu(const GemvArgs& a, const SwigluOut& so, co
                                       hipStream_t st);
 hipError_t launch_block_dots(int fmt, const void* w, int64_t K, int64_t row0, int64_t nrows,
                              const int8_t* q, int32_t* dots, hipStream_t st);
+// The same through the LDS-streaming loaders with split-K width wk (1, 2,
+// 4); supported says whether (fmt, K, wk) has a configuration.
+bool block_dots_staged_supported(int fmt, int64_t K, int wk);
+hipError_t launch_block_dots_staged(int fmt, const void* w, int64_t K, int64_t row0,
+                                    int64_t nrows, const int8_t* q, const uint16_t* d,
+                                    const int32_t* s, int wk, int32_t* dots, hipStream_t st);
 hipError_t launch_quantize_act(const float* x, int64_t M, int64_t K, int64_t ldx, int8_t* q,
                                uint16_t* d, int32_t* s, hipStream_t st);
 hipError_t launch_silu_mul_quantize(const float* gu, int64_t N, int8_t* q, uint16_t* d,

@@ -340,6 +340,21 @@ qgemv_status qgemv_quantize_multi(int fmt, int count, const void* const* w,
 qgemv_status qgemv_block_dots(int fmt, const void* w, int64_t N, int64_t K,
                               int64_t row0, int64_t nrows, const int8_t* q,
                               int32_t* dots, qgemv_stream_t stream);
+/* Validation: the same block dots through the loaders the streaming GEMV
+ * kernels run (the same passage): each (row, split-K slice) is split into
+ * wk slices as those kernels split it, staged in 16-byte chunks, parked in
+ * LDS and read back field by field (including 2-byte-misaligned Q6_K, Q4_0
+ * and Q8_0 fields and an empty last slice), with the activation in the same
+ * registers; the dots are stored instead of scaled.  d, s: the activation's
+ * fp16 scale bits and code sums (qgemv_quantize_act), which those registers
+ * also hold.  wk: 1, 2 or 4; a (K, wk) whose slices exceed 128 units of 64
+ * weights returns QGEMV_E_UNSUPPORTED.  Entries of dots for blocks past K are
+ * not written.  Other arguments, layout, gates and errors as for
+ * qgemv_block_dots. */
+qgemv_status qgemv_block_dots_staged(int fmt, const void* w, int64_t N, int64_t K,
+                                     int64_t row0, int64_t nrows, const int8_t* q,
+                                     const uint16_t* d, const int32_t* s, int wk,
+                                     int32_t* dots, qgemv_stream_t stream);
 
 #ifdef __cplusplus
 }

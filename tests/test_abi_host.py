@@ -242,3 +242,26 @@ def test_gates_stream_read():
     assert _status(R, A, 1 << 20, 1, A, 33, 0) == qg.QGEMV_E_UNSUPPORTED
     assert _status(R, A + 8, 1 << 20, 1, A, 4, 0) == qg.QGEMV_E_ALIGN
     assert _status(R, A, 1 << 20, 1, A + 2, 4, 0) == qg.QGEMV_E_ALIGN
+
+
+def test_gates_block_dots_staged():
+    """The staged block-dots validation entry: NULL, shape, limits (split-K
+    width, slice length) and alignment, before any device work."""
+    qg = _lib()
+    B = "qgemv_block_dots_staged"   # fmt, w, N, K, row0, nrows, q, d, s, wk, dots, stream
+    Q4K, R8 = qg.QGEMV_FMT_Q4_K, qg.QGEMV_FMT_Q6_K_R8
+    assert _status(B, Q4K, None, 4, 256, 0, 0, None, None, None, 1, None, 0) == qg.QGEMV_OK
+    assert _status(B, Q4K, A, 4, 256, 3, 2, A, A, A, 1, A, 0) == qg.QGEMV_E_SHAPE
+    assert _status(B, Q4K, A, 4, 256, 0, 4, A, None, A, 1, A, 0) == qg.QGEMV_E_NULL
+    assert _status(B, Q4K, A, 4, 256, 0, 4, A, A, None, 1, A, 0) == qg.QGEMV_E_NULL
+    assert _status(B, Q4K, A, 4, 48, 0, 4, A, A, A, 1, A, 0) == qg.QGEMV_E_SHAPE
+    assert _status(B, 9, A, 4, 256, 0, 4, A, A, A, 1, A, 0) == qg.QGEMV_E_UNSUPPORTED
+    assert _status(B, Q4K, A, 4, 256, 0, 4, A, A, A, 3, A, 0) == qg.QGEMV_E_UNSUPPORTED
+    # 224 units in one slice: more than 128
+    assert _status(B, R8, A, 4, 14336, 0, 4, A, A, A, 1, A, 0) == qg.QGEMV_E_UNSUPPORTED
+    assert "split-K width" in qg.qgemv_last_error()
+    assert _status(B, Q4K, A + 8, 4, 256, 0, 4, A, A, A, 1, A, 0) == qg.QGEMV_E_ALIGN
+    assert _status(B, Q4K, A, 4, 256, 0, 4, A + 4, A, A, 1, A, 0) == qg.QGEMV_E_ALIGN
+    assert _status(B, Q4K, A, 4, 256, 0, 4, A, A, A, 1, A + 2, 0) == qg.QGEMV_E_ALIGN
+    if _no_gpu():
+        assert _status(B, R8, A, 4, 14336, 0, 4, A, A, A, 4, A, 0) == qg.QGEMV_E_DEVICE
