@@ -567,14 +567,17 @@ __host__ __device__ inline int unit_byte(int u) {
 // (lane i fetches chunks i, i + 64, ...; the last one shifted back to end at
 // the slice end, so no load leaves the row).  Lanes past the slice repeat its
 // last unit (every load unconditional and in bounds) and drop its term.
-template <int FMT, int UPL, int NL, bool NT>
+//
+// MR > 1: the lane holds the activation of MR rows (the small-M product of a
+// few tokens) and dots every unit it reads from LDS against each of them.
+template <int FMT, int UPL, int NL, bool NT, int MR = 1>
 struct SliceStream {
     using UnitT = Unit<FMT>;
     using WT = typename UnitT::W;
     using UL = UnitLds<FMT>;
     int lane, u_lo, u_hi, sbeg, slen, nbw;
     bool empty;   // a slice past the row's last unit (see the constructor)
-    ActReg<FMT> A[UPL];
+    ActReg<FMT> A[MR][UPL];
     int ul[UPL];
     bool ok[UPL], has1[UPL];
 
@@ -596,15 +599,22 @@ struct SliceStream {
         sbeg = unit_byte<FMT>(u_lo);
         slen = min(unit_byte<FMT>(u_hi), row_bytes) - sbeg;
     }
-    // the activation of the lane's units (from global memory or LDS)
+    // the activation of the lane's units (from global memory or LDS); MR > 1:
+    // activation row m at q + m * ldq (d, s + m * ldq / 32), rows m >= mc
+    // repeating row mc - 1
     __device__ __forceinline__ void load_act(const int8_t* q, const uint16_t* d,
-                                             const int32_t* s) {
+                                             const int32_t* s, int ldq = 0, int mc = 1) {
 #pragma unroll
         for (int i = 0; i < UPL; i++) {
             const int u = u_lo + lane + 64 * i;
             ok[i] = !empty && u < u_hi;
             const int uc = ok[i] ? u : u_hi - 1;
-            A[i].load(q, d, s, uc);
+#pragma unroll
+            for (int m = 0; m < MR; m++) {
+                const int mm = m < mc ? m : mc - 1;
+                A[m][i].load(q + (int64_t)mm * ldq, d + (int64_t)mm * (ldq / 32),
+                             s + (int64_t)mm * (ldq / 32), uc);
+            }
             ul[i] = uc - u_lo;
             has1[i] = 2 * uc + 1 < nbw;
         }
@@ -639,10 +649,29 @@ struct SliceStream {
         for (int i = 0; i < UPL; i++) {
             WT wv;
             UL::load(buf, delta, ul[i], has1[i], wv);
-            const float t = UnitT::term(wv, A[i], u_lo + ul[i], nbw);
+            const float t = UnitT::term(wv, A[0][i], u_lo + ul[i], nbw);
             acc += ok[i] ? t : 0.0f;
         }
         return group_sum<64>(acc);
+    }
+    // The slice's dots with the MR activation rows, each formed exactly as
+    // dot() forms it for its row (valid in lane 63).
+    __device__ __forceinline__ void dot_mr(const uint8_t* buf, int delta, float (&out)[MR]) const {
+        float acc[MR];
+#pragma unroll
+        for (int m = 0; m < MR; m++) acc[m] = 0.0f;
+#pragma unroll
+        for (int i = 0; i < UPL; i++) {
+            WT wv;
+            UL::load(buf, delta, ul[i], has1[i], wv);
+#pragma unroll
+            for (int m = 0; m < MR; m++) {
+                const float t = UnitT::term(wv, A[m][i], u_lo + ul[i], nbw);
+                acc[m] += ok[i] ? t : 0.0f;
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < MR; m++) out[m] = group_sum<64>(acc[m]);
     }
     // Two rows' dots (two independent chains for the scheduler to
     // interleave); each is formed exactly as dot() forms it.
@@ -654,8 +683,8 @@ struct SliceStream {
             WT w0, w1;
             UL::load(buf0, delta0, ul[i], has1[i], w0);
             UL::load(buf1, delta1, ul[i], has1[i], w1);
-            const float t0 = UnitT::term(w0, A[i], u_lo + ul[i], nbw);
-            const float t1 = UnitT::term(w1, A[i], u_lo + ul[i], nbw);
+            const float t0 = UnitT::term(w0, A[0][i], u_lo + ul[i], nbw);
+            const float t1 = UnitT::term(w1, A[0][i], u_lo + ul[i], nbw);
             acc0 += ok[i] ? t0 : 0.0f;
             acc1 += ok[i] ? t1 : 0.0f;
         }
@@ -889,21 +918,28 @@ constexpr int DWG = 64 * DW;    // its threads
 constexpr int DRG = 8;          // rows per row group of the static split
 static_assert(DRG % 2 == 0, "pairs of rows stay inside a row group");
 
-template <int FMT, int UPL, int WK, int NL, bool XQ, bool SW, bool PAIRS>
+//
+// MR > 1 (the small-M product of MR activation rows, row m at q + m * ldq,
+// output row m at y + m * N; rows m >= mc are computed on row mc - 1 and not
+// stored): every unit read from LDS is dotted against the MR rows, each dot
+// formed exactly as the batch-1 product forms it, so output row m has the
+// bits of the batch-1 product on activation row m with the same slices.
+template <int FMT, int UPL, int WK, int NL, bool XQ, bool SW, bool PAIRS, int MR = 1>
 __global__ __launch_bounds__(DWG) void k_gemv_dyn(const uint8_t* __restrict__ w, int N, int U,
                                                    int US, int nbw, int row_bytes, int buf_bytes,
                                                    const int8_t* __restrict__ q,
                                                    const uint16_t* __restrict__ d,
                                                    const int32_t* __restrict__ s,
                                                    float* __restrict__ y, const SwigluOut so,
-                                                   const ActIn ai) {
+                                                   const ActIn ai, int ldq, int mc) {
     static_assert(DW % WK == 0, "whole waves per slice");
+    static_assert(MR == 1 || (!XQ && !SW && !PAIRS), "several activation rows: plain rows");
     extern __shared__ __align__(16) uint8_t lds[];
     __shared__ int cnt[WK];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int kq = wave % WK;
-    SliceStream<FMT, UPL, NL, true> ss(lane, U, US, kq, nbw, row_bytes);
+    SliceStream<FMT, UPL, NL, true, MR> ss(lane, U, US, kq, nbw, row_bytes);
 
     // this workgroup's rows; indices past them (and rows past N) map to row
     // N - 1, whose bytes the prefetch then reads from cache
@@ -923,7 +959,7 @@ __global__ __launch_bounds__(DWG) void k_gemv_dyn(const uint8_t* __restrict__ w,
 
     if (threadIdx.x < WK) cnt[threadIdx.x] = 0;
     if (SW && b == 0) swiglu_zero_tail<DWG>(so);
-    if constexpr (!XQ) ss.load_act(q, d, s);
+    if constexpr (!XQ) ss.load_act(q, d, s, ldq, mc);
     const int Kp = (32 * nbw + 255) / 256 * 256;
     int8_t* const aq = reinterpret_cast<int8_t*>(lds + 2 * DW * buf_bytes);
     uint16_t* const ad = reinterpret_cast<uint16_t*>(lds + 2 * DW * buf_bytes + Kp);
@@ -954,6 +990,24 @@ __global__ __launch_bounds__(DWG) void k_gemv_dyn(const uint8_t* __restrict__ w,
         if (lane == 63 && i < pool_n && row_raw(i) < N) {
             if constexpr (WK == 1 && !SW) y[row_raw(i)] = acc;
             else part[i * WK + kq] = acc;
+        }
+    };
+    // a row's dot(s) with the activation row(s), stored or parked
+    auto row_done = [&](const uint8_t* buf, int delta, int i) {
+        if constexpr (MR == 1) {
+            finish_row(dot_row(buf, delta), i);
+        } else {
+            float v[MR];
+            ss.dot_mr(buf, delta, v);
+            if (lane == 63 && i < pool_n && row_raw(i) < N) {
+#pragma unroll
+                for (int m = 0; m < MR; m++) {
+                    if (m < mc) {
+                        if constexpr (WK == 1) y[(int64_t)m * N + row_raw(i)] = v[m];
+                        else part[(i * WK + kq) * MR + m] = v[m];
+                    }
+                }
+            }
         }
     };
 
@@ -1045,7 +1099,7 @@ __global__ __launch_bounds__(DWG) void k_gemv_dyn(const uint8_t* __restrict__ w,
         int tn = grab_issue();   // the index after ib, in flight
         // a wave's indices increase, so once one is past the pool all later are
         while (i0 < pool_n) {
-            finish_row(dot_row(buf0, d0), i0);
+            row_done(buf0, d0, i0);
             commit(Ra, da, buf1);
             d1 = da;
             const int i1 = ia;
@@ -1053,7 +1107,7 @@ __global__ __launch_bounds__(DWG) void k_gemv_dyn(const uint8_t* __restrict__ w,
             tn = grab_issue();
             da = stage(Ra, row_of(ia));
             __builtin_amdgcn_sched_barrier(0);
-            if (i1 < pool_n) finish_row(dot_row(buf1, d1), i1);
+            if (i1 < pool_n) row_done(buf1, d1, i1);
             commit(Rb, db, buf0);
             d0 = db;
             i0 = ib;
@@ -1068,12 +1122,13 @@ __global__ __launch_bounds__(DWG) void k_gemv_dyn(const uint8_t* __restrict__ w,
         swiglu_epilogue<DWG, WK>(part, hseg, nblk, b, G, so);
     } else if constexpr (WK > 1) {
         __syncthreads();
-        for (int i = threadIdx.x; i < pool_n; i += DWG) {
-            if (row_raw(i) < N) {
-                float v = part[i * WK];
+        for (int t = threadIdx.x; t < pool_n * MR; t += DWG) {
+            const int i = t / MR, m = t % MR;
+            if (row_raw(i) < N && m < mc) {
+                float v = part[i * WK * MR + m];
 #pragma unroll
-                for (int k = 1; k < WK; k++) v += part[i * WK + k];
-                y[row_raw(i)] = v;
+                for (int k = 1; k < WK; k++) v += part[(i * WK + k) * MR + m];
+                y[(int64_t)m * N + row_raw(i)] = v;
             }
         }
     }
@@ -1309,12 +1364,12 @@ static hipError_t launch_dyn_cfg(const GemvArgs& a, const SwigluOut& so, const A
         launch_kernel((k_gemv_dyn<FMT, UPL, WK, NL, XQ, SW, true>), dim3((unsigned)grid),
                       dim3(DWG), (unsigned)smem, st, (const uint8_t*)a.w, (int)a.N, U, US,
                       (int)(a.K / 32), row_bytes_of(FMT, a.K), buf_bytes, a.q, a.d, a.s, a.y,
-                      so, ai);
+                      so, ai, 0, 1);
     else
         launch_kernel((k_gemv_dyn<FMT, UPL, WK, NL, XQ, SW, false>), dim3((unsigned)grid),
                       dim3(DWG), (unsigned)smem, st, (const uint8_t*)a.w, (int)a.N, U, US,
                       (int)(a.K / 32), row_bytes_of(FMT, a.K), buf_bytes, a.q, a.d, a.s, a.y,
-                      so, ai);
+                      so, ai, 0, 1);
     return hipGetLastError();
 }
 

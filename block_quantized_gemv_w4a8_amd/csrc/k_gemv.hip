@@ -192,7 +192,7 @@ __global__ __launch_bounds__(WG) void k_block_dots_staged(const uint8_t* __restr
         typename Unit<FMT>::W wv;
         UnitLds<FMT>::load(buf, delta, ss.ul[i], ss.has1[i], wv);
         int D[4];
-        UnitDots<FMT>::dots(wv, ss.A[i], D);
+        UnitDots<FMT>::dots(wv, ss.A[0][i], D);
         const int u = ss.u_lo + ss.ul[i];
         constexpr bool PAIR = FMT == QGEMV_FMT_Q4_0 || FMT == QGEMV_FMT_Q8_0;
         if (ss.ok[i]) {

@@ -3,12 +3,14 @@
 // row m (colibri GPU backends, eligibility gates: C = A x B is
 // row-independent).
 //
-// DOT4 variant (Q4_K): the GEMV kernel's mapping (LPR lanes per weight row,
-// one 64-weight unit per lane step), except that each weight unit is loaded
-// and unpacked once and then dotted against MT activation rows staged in
-// LDS, so the weight stream is shared by the MT rows ("Backends and
-// hardware", section "CUDA": W4A8 inner product on 4 x int8 dots).  For Q6_K
-// and Q4_0 the DOT4 variant is the batch-1 GEMV launched on each row.
+// DOT4 variant: one activation row is the batch-1 GEMV; more go through the
+// batch-1 streaming kernel up to four at a time (k_small_m_rows.hip), each
+// weight unit read once per group and dotted against every row of it with
+// v_dot4 ("Backends and hardware", section "CUDA": W4A8 inner product on
+// 4 x int8 dots).  Rows longer than that kernel takes (more than 256 units)
+// fall back to k_small_m_dot4 below (Q4_K: the lanes-per-row mapping with
+// each unit dotted against MT activation rows staged in LDS) or to the
+// batch-1 GEMV on each row (Q6_K, Q4_0).
 //
 // MFMA variant (all three formats): where the work is a dense contraction
 // (many rows), the int8 matrix cores do it.  Each 32-wide K block gets its
@@ -742,8 +744,12 @@ static int dot4_tile_rows(int64_t K) {
     return mt >= 8 ? 8 : mt >= 4 ? 4 : mt >= 2 ? 2 : 1;
 }
 
-// AUTO: the MFMA variant from this many rows on (measured crossover).
-constexpr int kMfmaFromM = 3;
+// AUTO: the MFMA variant from this many rows on (measured crossover on
+// MI355X: Q4_K 14336 x 4096 takes 12.6 us at M = 3 through the streaming
+// rows and 13.1 us on MFMA, 13.4 against 13.2 us at M = 4; Q6_K 4096 x 14336
+// 17.0 against 25.0 us and Q4_0 14336 x 4096 13.0 against 18.1 us at M = 4,
+// while two passes of four rows lose to MFMA at M = 8).
+static int mfma_from_m(int fmt) { return fmt == QGEMV_FMT_Q4_K ? 4 : 5; }
 
 static hipError_t launch_dot4_q4k(const void* w, int64_t N, int64_t K, int64_t M,
                                   const int8_t* q, const uint16_t* d, const int32_t* s, float* y,
@@ -789,25 +795,25 @@ static bool use_stream_kernel(int fmt, int64_t N, int64_t M) {
 hipError_t launch_small_m(int fmt, const void* w, int64_t N, int64_t K, int64_t M,
                           const int8_t* q, const uint16_t* d, const int32_t* s, float* y,
                           int variant, hipStream_t st) {
+    const bool auto_mfma = variant == QGEMV_VARIANT_AUTO && M >= mfma_from_m(fmt);
     if (variant == QGEMV_VARIANT_MFMA_STREAM ||
-        ((variant == QGEMV_VARIANT_MFMA || (variant == QGEMV_VARIANT_AUTO && M >= kMfmaFromM)) &&
-         use_stream_kernel(fmt, N, M)))
+        ((variant == QGEMV_VARIANT_MFMA || auto_mfma) && use_stream_kernel(fmt, N, M)))
         return launch_small_m2(fmt, w, N, K, M, q, d, s, y, st);
-    const bool mfma = variant == QGEMV_VARIANT_MFMA || variant == QGEMV_VARIANT_MFMA_STAGED ||
-                      (variant == QGEMV_VARIANT_AUTO && M >= kMfmaFromM);
+    const bool mfma =
+        variant == QGEMV_VARIANT_MFMA || variant == QGEMV_VARIANT_MFMA_STAGED || auto_mfma;
+    if (!mfma) {
+        // one row: the batch-1 GEMV; more: up to four rows per pass of the
+        // batch-1 streaming kernel, else the GEMV on each row
+        if (M == 1) return launch_rows_gemv(fmt, w, N, K, M, q, d, s, y, st);
+        const hipError_t e = launch_small_m_rows(fmt, w, N, K, M, q, d, s, y, st);
+        if (e != hipErrorNotSupported) return e;
+        if (fmt == QGEMV_FMT_Q4_K) return launch_dot4_q4k(w, N, K, M, q, d, s, y, st);
+        return launch_rows_gemv(fmt, w, N, K, M, q, d, s, y, st);
+    }
     switch (fmt) {
-    case QGEMV_FMT_Q4_K:
-        // one row under AUTO: the batch-1 GEMV streams the matrix fastest
-        if (variant == QGEMV_VARIANT_AUTO && M == 1)
-            return launch_rows_gemv(fmt, w, N, K, M, q, d, s, y, st);
-        return mfma ? launch_mfma<QGEMV_FMT_Q4_K>(w, N, K, M, q, d, s, y, st)
-                    : launch_dot4_q4k(w, N, K, M, q, d, s, y, st);
-    case QGEMV_FMT_Q6_K:
-        return mfma ? launch_mfma<QGEMV_FMT_Q6_K>(w, N, K, M, q, d, s, y, st)
-                    : launch_rows_gemv(fmt, w, N, K, M, q, d, s, y, st);
-    default:
-        return mfma ? launch_mfma<QGEMV_FMT_Q4_0>(w, N, K, M, q, d, s, y, st)
-                    : launch_rows_gemv(fmt, w, N, K, M, q, d, s, y, st);
+    case QGEMV_FMT_Q4_K: return launch_mfma<QGEMV_FMT_Q4_K>(w, N, K, M, q, d, s, y, st);
+    case QGEMV_FMT_Q6_K: return launch_mfma<QGEMV_FMT_Q6_K>(w, N, K, M, q, d, s, y, st);
+    default: return launch_mfma<QGEMV_FMT_Q4_0>(w, N, K, M, q, d, s, y, st);
     }
 }
 

@@ -112,6 +112,15 @@ hipError_t launch_small_m(int fmt, const void* w, int64_t N, int64_t K, int64_t 
                           const int8_t* q, const uint16_t* d, const int32_t* s, float* y,
                           int variant, hipStream_t st);
 
+// The small-M product through the batch-1 dynamic-row streaming kernel with
+// up to four activation rows per pass over the weights (fmt: QGEMV_FMT_Q4_K,
+// QGEMV_FMT_Q6_K or QGEMV_FMT_Q4_0; M >= 2).  hipErrorNotSupported (nothing
+// launched) for rows of more than 256 units or slices too long for its
+// buffers.
+hipError_t launch_small_m_rows(int fmt, const void* w, int64_t N, int64_t K, int64_t M,
+                               const int8_t* q, const uint16_t* d, const int32_t* s, float* y,
+                               hipStream_t st);
+
 // The small-M product on int8 matrix cores with wave-private weight streams
 // (fmt: QGEMV_FMT_Q4_K, QGEMV_FMT_Q6_K or QGEMV_FMT_Q4_0; 1 <= M <= 64).
 hipError_t launch_small_m2(int fmt, const void* w, int64_t N, int64_t K, int64_t M,

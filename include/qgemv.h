@@ -203,9 +203,11 @@ qgemv_status qgemv_q8_0(const void* w, int64_t N, int64_t K, const int8_t* q,
  * equals qgemv_q4_k on activation row m (colibri GPU backends, eligibility
  * gates: C = A x B is row-independent).  q [M][Kp], d/s [M][Kp/32],
  * y fp32 [M][N] row-major, 1 <= M <= QGEMV_M_MAX.
- * variant: QGEMV_VARIANT_DOT4 (4 x int8 dots), QGEMV_VARIANT_MFMA (int8
- * matrix cores), or QGEMV_VARIANT_AUTO (chooses by M; M = 1 is qgemv_q4_k
- * itself). */
+ * variant: QGEMV_VARIANT_DOT4 (4 x int8 dots: M = 1 is qgemv_q4_k itself;
+ * more rows stream the weights once per group of up to four activation
+ * rows, each output row then having the bits of qgemv_q4_k on its row where
+ * that GEMV streams its rows, K > 2048), QGEMV_VARIANT_MFMA (int8 matrix
+ * cores), or QGEMV_VARIANT_AUTO (DOT4 up to M = 3, MFMA from M = 4). */
 qgemv_status qgemm_q4_k_small_m(const void* w, int64_t N, int64_t K, int64_t M,
                                 const int8_t* q, const uint16_t* d, const int32_t* s,
                                 float* y, int variant, qgemv_stream_t stream);
@@ -214,9 +216,11 @@ qgemv_status qgemm_q4_k_small_m(const void* w, int64_t N, int64_t K, int64_t M,
  * down projection and lm_head, which are Q6_K in a Q4_K_M model; "llambda.lisp"
  * README, Features & Architecture).  Arguments, layouts, limits and errors as
  * for qgemm_q4_k_small_m; K % 32 == 0 for Q4_0, any K <= QGEMV_K_MAX.
- * variant: QGEMV_VARIANT_MFMA (int8 matrix cores), QGEMV_VARIANT_DOT4 (the
- * batch-1 GEMV of this library on each activation row, one launch per row),
- * or QGEMV_VARIANT_AUTO (chooses by M). */
+ * variant: QGEMV_VARIANT_MFMA (int8 matrix cores), QGEMV_VARIANT_DOT4 (as
+ * for Q4_K: the batch-1 GEMV at M = 1, else up to four activation rows per
+ * pass of its streaming kernel, with its bits where it streams the rows; rows
+ * of more than 16384 weights: the batch-1 GEMV on each row), or
+ * QGEMV_VARIANT_AUTO (DOT4 up to M = 4, MFMA from M = 5). */
 qgemv_status qgemm_q6_k_small_m(const void* w, int64_t N, int64_t K, int64_t M,
                                 const int8_t* q, const uint16_t* d, const int32_t* s,
                                 float* y, int variant, qgemv_stream_t stream);

@@ -241,3 +241,31 @@ def test_small_m_deterministic_and_row_independent(qg, fmt):
         for m in (0, 5, 7):
             Ym = small_m(qg, fmt, wd, N, K, (q[m:m + 1], d[m:m + 1], s[m:m + 1]), 1, v)
             assert np.array_equal(Y1[m].view(np.uint32), Ym[0].view(np.uint32)), (fmt, v, m)
+
+
+# The DOT4 variant passes up to four activation rows at a time through the
+# batch-1 streaming kernel with the batch-1 slices: for rows of more than 32
+# units (the rows that kernel takes) each output row has the bits of the
+# batch-1 GEMV on its activation row.  Covers split-K widths 1, 2 and 4,
+# M = 2, 3 (a group of four with one repeated row), 4, 5 and 7 (two groups).
+ROWS_BITS = [("q4_k", 2, 700, 4096), ("q4_k", 3, 513, 8192), ("q4_k", 5, 130, 14336),
+             ("q6_k", 2, 301, 4096), ("q6_k", 4, 300, 14336), ("q6_k", 7, 64, 8192),
+             ("q4_0", 2, 333, 4096), ("q4_0", 4, 100, 4128), ("q4_0", 5, 64, 14336)]
+
+
+@pytest.mark.parametrize("fmt,M,N,K", ROWS_BITS)
+def test_small_m_dot4_rows_equal_gemv_bits(qg, fmt, M, N, K):
+    g = np.random.default_rng(M * 7 + N + K)
+    w = WEIGHTS[fmt](g, N, K)
+    x, _ = synth.activation(g, M, K)
+    q, d, s = quantize(qg, x)
+    wd = dev(w)
+    say("small_m dot4 rows vs gemv", fmt, M, N, K)
+    Y = small_m(qg, fmt, wd, N, K, (q, d, s), M, qg.QGEMV_VARIANT_DOT4)
+    for m in range(M):
+        y1 = torch.full((N,), float("nan"), dtype=torch.float32, device="cuda:0")
+        qg.GEMV[fmt](wd, N, K, q[m], d[m], s[m], y1)
+        assert np.array_equal(Y[m].view(np.uint32), host(y1).view(np.uint32)), (fmt, M, m)
+    qh, dh, sh = act_host(q, d, s)
+    Y_ref, TT = oracle.gemm(fmt, w, N, K, qh, dh, sh)
+    check_y(Y.reshape(-1), Y_ref.reshape(-1), TT.reshape(-1), f"dot4 rows {fmt} M={M}")
