@@ -243,6 +243,11 @@ def main():
         if ev is not None:
             ev.record(1, sh)
 
+    # the achievable read rate is measured right before the warm-up steps: its
+    # ~30 streaming reads of 1 GiB also bring the GPU out of the idle it sat
+    # in while the host generated the inputs, so a short warm-up (the
+    # driver's 5 steps) starts the timed steps on a busy device
+    read = read_kernel_rate(qg, torch, np, dev)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -286,7 +291,6 @@ def main():
         f"{len(head_us)} event-timed launches after the timed steps (stream bracket "
         f"{bracket_avg_us:.2f} us; {float(np.mean(loop_us)):.2f} us over {len(loop_us)} "
         f"launches sampled inside them)")
-    read = read_kernel_rate(qg, torch, np, dev)
 
     # dominant kernel roofline: algorithmic bytes per launch of the lm_head GEMV
     # = N rows x (row weight bytes + 4 B output) + one activation row (codes,
