@@ -34,7 +34,7 @@ QGEMV_E_LAUNCH = 6
 QGEMV_FMT_Q4_0, QGEMV_FMT_Q4_K, QGEMV_FMT_Q6_K, QGEMV_FMT_Q8_0 = 0, 1, 2, 3
 QGEMV_FMT_Q6_K_R8 = 4
 QGEMV_VARIANT_AUTO, QGEMV_VARIANT_DOT4, QGEMV_VARIANT_MFMA = 0, 1, 2
-QGEMV_VARIANT_MFMA_STAGED, QGEMV_VARIANT_MFMA_STREAM = 3, 4
+QGEMV_VARIANT_MFMA_STAGED, QGEMV_VARIANT_MFMA_STREAM, QGEMV_VARIANT_MFMA_RESIDENT = 3, 4, 5
 QGEMV_K_MAX = 32768
 QGEMV_MULTI_MAX = 8
 QGEMV_M_MAX = 64

@@ -24,7 +24,7 @@ LIB = os.path.join(LIB_DIR, "libqgemv.so")
 
 SOURCES = ["qgemv_api.cpp", "k_quantize.hip", "k_gemv.hip", "k_gemv_q4_0.hip", "k_gemv_q4_k.hip",
            "k_gemv_q6_k.hip", "k_gemv_q6_k_r8.hip", "k_gemv_q8_0.hip", "k_small_m.hip",
-           "k_small_m2.hip", "k_small_m_rows.hip",
+           "k_small_m2.hip", "k_small_m_rows.hip", "k_small_m3.hip",
            "k_measure.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

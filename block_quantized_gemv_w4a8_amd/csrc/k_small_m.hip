@@ -786,6 +786,23 @@ static hipError_t launch_rows_gemv(int fmt, const void* w, int64_t N, int64_t K,
 // 17.9 us at M = 8, 33.8 against 36.0 us at M = 64; Q4_0: 19.1 against 51.6
 // us at M = 8).  A shape and a bucket of M fix the kernel, so the summation
 // order of a row stays fixed.
+// Which products the register-resident kernel (k_small_m3.hip) takes under
+// MFMA and AUTO: Q4_K with at most 16 rows on matrices of at least six
+// 16-row tiles per compute unit, where it measured faster (28672 x 4096 at
+// M = 8: 22.2 against 24.8 us staged; 14336 x 4096: 15.0 against 13.5 us,
+// so narrower matrices stay with the staged kernel).
+static bool use_resident_kernel(int fmt, int64_t N, int64_t K, int64_t M) {
+    if (!small_m3_supported(fmt, K, M)) return false;
+    int cus = 0, dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0) {
+        (void)hipGetLastError();
+        cus = 256;
+    }
+    return (N + 15) / 16 >= 6 * (int64_t)cus;
+}
+
 static bool use_stream_kernel(int fmt, int64_t N, int64_t M) {
     if (fmt != QGEMV_FMT_Q6_K) return false;
     const bool wide = (N + 15) / 16 >= kMfmaWideTiles;
@@ -796,6 +813,10 @@ hipError_t launch_small_m(int fmt, const void* w, int64_t N, int64_t K, int64_t 
                           const int8_t* q, const uint16_t* d, const int32_t* s, float* y,
                           int variant, hipStream_t st) {
     const bool auto_mfma = variant == QGEMV_VARIANT_AUTO && M >= mfma_from_m(fmt);
+    if ((variant == QGEMV_VARIANT_MFMA_RESIDENT && small_m3_supported(fmt, K, M)) ||
+        ((variant == QGEMV_VARIANT_MFMA || auto_mfma) && use_resident_kernel(fmt, N, K, M)))
+        return launch_small_m3(fmt, w, N, K, M, q, d, s, y, st);
+    if (variant == QGEMV_VARIANT_MFMA_RESIDENT) variant = QGEMV_VARIANT_MFMA;
     if (variant == QGEMV_VARIANT_MFMA_STREAM ||
         ((variant == QGEMV_VARIANT_MFMA || auto_mfma) && use_stream_kernel(fmt, N, M)))
         return launch_small_m2(fmt, w, N, K, M, q, d, s, y, st);

@@ -129,7 +129,7 @@ qgemv_status small_m_common(int fmt, const char* name, const void* w, int64_t N,
                     (long long)M, QGEMV_M_MAX);
     if (variant != QGEMV_VARIANT_AUTO && variant != QGEMV_VARIANT_DOT4 &&
         variant != QGEMV_VARIANT_MFMA && variant != QGEMV_VARIANT_MFMA_STAGED &&
-        variant != QGEMV_VARIANT_MFMA_STREAM)
+        variant != QGEMV_VARIANT_MFMA_STREAM && variant != QGEMV_VARIANT_MFMA_RESIDENT)
         return fail(QGEMV_E_UNSUPPORTED, "%s: unknown variant %d", name, variant);
     if (!aligned(w, 16)) return fail(QGEMV_E_ALIGN, "%s: w must be 16-byte aligned", name);
     if ((st = check_act_align(q, d, s)) != QGEMV_OK) return st;

@@ -121,6 +121,14 @@ hipError_t launch_small_m_rows(int fmt, const void* w, int64_t N, int64_t K, int
                                const int8_t* q, const uint16_t* d, const int32_t* s, float* y,
                                hipStream_t st);
 
+// The small-M product on int8 matrix cores with each wave's slice of the
+// activation resident in registers (Q4_K, 1 <= M <= 16, K <= 16384: where
+// small_m3_supported; else hipErrorNotSupported, nothing launched).
+bool small_m3_supported(int fmt, int64_t K, int64_t M);
+hipError_t launch_small_m3(int fmt, const void* w, int64_t N, int64_t K, int64_t M,
+                           const int8_t* q, const uint16_t* d, const int32_t* s, float* y,
+                           hipStream_t st);
+
 // The small-M product on int8 matrix cores with wave-private weight streams
 // (fmt: QGEMV_FMT_Q4_K, QGEMV_FMT_Q6_K or QGEMV_FMT_Q4_0; 1 <= M <= 64).
 hipError_t launch_small_m2(int fmt, const void* w, int64_t N, int64_t K, int64_t M,

@@ -99,13 +99,17 @@ enum {
  * QGEMV_VARIANT_MFMA_STAGED forces the kernel that stages every K step of
  * weights and activation through LDS, QGEMV_VARIANT_MFMA_STREAM the one in
  * which every wave streams its own weight rows into registers and only the
- * activation is shared through LDS.  All compute the same products. */
+ * activation is shared through LDS, QGEMV_VARIANT_MFMA_RESIDENT (Q4_K, M <=
+ * 16, K <= 16384; elsewhere the MFMA choice) the one in which each wave
+ * keeps the activation of its slice of K in registers and streams its own
+ * 16-row weight tiles.  All compute the same products. */
 enum {
     QGEMV_VARIANT_AUTO = 0,
     QGEMV_VARIANT_DOT4 = 1,
     QGEMV_VARIANT_MFMA = 2,
     QGEMV_VARIANT_MFMA_STAGED = 3,
-    QGEMV_VARIANT_MFMA_STREAM = 4
+    QGEMV_VARIANT_MFMA_STREAM = 4,
+    QGEMV_VARIANT_MFMA_RESIDENT = 5
 };
 
 /* Returns QGEMV_ABI_VERSION of the loaded library.  A caller built against a

@@ -29,7 +29,8 @@ def small_m(qg, fmt, wd, N, K, act, M, variant):
 
 def variants(qg):
     return [qg.QGEMV_VARIANT_DOT4, qg.QGEMV_VARIANT_MFMA, qg.QGEMV_VARIANT_AUTO,
-            qg.QGEMV_VARIANT_MFMA_STAGED, qg.QGEMV_VARIANT_MFMA_STREAM]
+            qg.QGEMV_VARIANT_MFMA_STAGED, qg.QGEMV_VARIANT_MFMA_STREAM,
+            qg.QGEMV_VARIANT_MFMA_RESIDENT]
 
 
 SHAPES = [(1, 100, 256), (2, 65, 896), (3, 257, 4096), (5, 64, 4864), (8, 300, 4096),
@@ -269,3 +270,25 @@ def test_small_m_dot4_rows_equal_gemv_bits(qg, fmt, M, N, K):
     qh, dh, sh = act_host(q, d, s)
     Y_ref, TT = oracle.gemm(fmt, w, N, K, qh, dh, sh)
     check_y(Y.reshape(-1), Y_ref.reshape(-1), TT.reshape(-1), f"dot4 rows {fmt} M={M}")
+
+
+@pytest.mark.parametrize("M", [4, 16])
+def test_small_m_very_wide_q4k_resident_route(qg, M):
+    """Q4_K matrices of at least six 16-row tiles per compute unit take the
+    register-resident kernel under MFMA and AUTO (N = 24600: 1538 tiles, the
+    last ragged); every output against the oracle, and the same bits as the
+    forced RESIDENT variant."""
+    N, K = 24600, 1024
+    g = np.random.default_rng(M + 99)
+    w = WEIGHTS["q4_k"](g, N, K)
+    x, _ = synth.activation(g, M, K)
+    act = quantize(qg, x)
+    q, d, s = act_host(*act)
+    wd = dev(w)
+    Y_ref, TT = oracle.gemm("q4_k", w, N, K, q, d, s)
+    say("small_m very wide q4_k", M)
+    Yr = small_m(qg, "q4_k", wd, N, K, act, M, qg.QGEMV_VARIANT_MFMA_RESIDENT)
+    check_y(Yr.reshape(-1), Y_ref.reshape(-1), TT.reshape(-1), f"resident M={M}")
+    for v in (qg.QGEMV_VARIANT_MFMA, qg.QGEMV_VARIANT_AUTO):
+        Y = small_m(qg, "q4_k", wd, N, K, act, M, v)
+        assert np.array_equal(Y.view(np.uint32), Yr.view(np.uint32)), v
