@@ -780,7 +780,8 @@ def extras(qg, torch, np, synth, dev, R, c2, c3, args):
         qm, dm, smm = qg.act_buffers(M, K6, dev)
         qg.qgemv_quantize_act(xm, M, K6, K6, qm, dm, smm)
         ym = torch.empty((M, N6), dtype=torch.float32, device=dev)
-        for vname, v in (("gemv_rows", qg.QGEMV_VARIANT_DOT4), ("mfma", qg.QGEMV_VARIANT_MFMA)):
+        for vname, v in (("dot4", qg.QGEMV_VARIANT_DOT4), ("mfma", qg.QGEMV_VARIANT_MFMA),
+                         ("auto", qg.QGEMV_VARIANT_AUTO)):
             us = time_kernel(torch, lambda c: qg.qgemm_q6_k_small_m(
                 w6[c], N6, K6, M, qm, dm, smm, ym, v), 50, 11)
             sm6[f"M{M}_{vname}_us"] = round(us, 2)
@@ -789,7 +790,7 @@ def extras(qg, torch, np, synth, dev, R, c2, c3, args):
         sm6[f"M{M}_mfma_weight_GBps"] = round(wb6 / sm6[f"M{M}_mfma_us"] / 1e3, 1)
         sm6[f"M{M}_mfma_int8_TOPS"] = round(2 * M * N6 * K6 / sm6[f"M{M}_mfma_us"] / 1e6, 1)
     sm6["crossover_M_mfma_faster_from"] = next(
-        (M for M in SMALL_M_LIST if sm6[f"M{M}_mfma_us"] < sm6[f"M{M}_gemv_rows_us"]), None)
+        (M for M in SMALL_M_LIST if sm6[f"M{M}_mfma_us"] < sm6[f"M{M}_dot4_us"]), None)
     ex["small_m_q6_k_4096x14336"] = sm6
     del w6
 
