@@ -48,7 +48,7 @@ EXPORTS = [
     "qgemm_q4_k_small_m", "qgemm_q6_k_small_m", "qgemm_q4_0_small_m",
     "qgemv_silu_mul_quantize", "qgemv_q4_k_swiglu_quantize",
     "qgemv_quantize_gemv", "qgemv_quantize_q4_k_swiglu", "qgemv_multi", "qgemv_quantize_multi",
-    "qgemv_block_dots", "qgemv_block_dots_staged",
+    "qgemv_block_dots", "qgemv_block_dots_staged", "qgemm_small_m_block_dots",
 ]
 
 _P, _I64, _I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
@@ -86,6 +86,8 @@ _lib.qgemv_block_dots.restype = _I
 _lib.qgemv_block_dots.argtypes = [_I, _P, _I64, _I64, _I64, _I64, _P, _P, _P]
 _lib.qgemv_block_dots_staged.restype = _I
 _lib.qgemv_block_dots_staged.argtypes = [_I, _P, _I64, _I64, _I64, _I64, _P, _P, _P, _I, _P, _P]
+_lib.qgemm_small_m_block_dots.restype = _I
+_lib.qgemm_small_m_block_dots.argtypes = [_I, _P, _I64, _I64, _I64, _P, _P, _P, _P, _I, _P, _P]
 
 if _lib.qgemv_abi_version() != 1:
     raise ImportError("libqgemv ABI generation mismatch (expected 1)")
@@ -296,6 +298,12 @@ def qgemv_block_dots_staged(fmt, w, N, K, row0, nrows, q, d, s, wk, dots, stream
     return _check(_lib.qgemv_block_dots_staged(fmt, _ptr(w), N, K, row0, nrows, _ptr(q), _ptr(d),
                                                _ptr(s), wk, _ptr(dots), _stream(stream)),
                   "qgemv_block_dots_staged")
+
+
+def qgemm_small_m_block_dots(fmt, w, N, K, M, q, d, s, y, variant, dots, stream=None):
+    return _check(_lib.qgemm_small_m_block_dots(fmt, _ptr(w), N, K, M, _ptr(q), _ptr(d), _ptr(s),
+                                                _ptr(y), variant, _ptr(dots), _stream(stream)),
+                  "qgemm_small_m_block_dots")
 
 
 GEMV = {"q4_0": qgemv_q4_0, "q4_k": qgemv_q4_k, "q6_k": qgemv_q6_k, "q8_0": qgemv_q8_0,

@@ -212,13 +212,19 @@ struct MfmaGeom {
 //   Q6_K  y += d*sc_g*dx*D  - (32*d*sc_g)(dx*sum16) (w = d*sc*(code - 32))
 // The second product of each line is a small dense product over the blocks
 // (groups) of a unit and goes to the fp32 MFMA.
-template <int FMT, int MT, int RT, int KS, int KP, int MS, int G, int R>
+//
+// DOTS (validation): every int32 MFMA tile is also stored to dots [M][N][nb]
+// (nb = Kp/32 blocks, Q4_0 K/32; Q6_K Kp/16 groups): the raw integer dots of
+// the unsigned codes (Q4_K and Q4_0: sum code*q per 32-block; Q6_K: per
+// 16-group) before any scale, offset or min is applied.
+template <int FMT, int MT, int RT, int KS, int KP, int MS, int G, int R, bool DOTS = false>
 __global__ __launch_bounds__(64 * RT * KS * KP * MS) void k_small_m_mfma(const uint8_t* __restrict__ w,
                                                                int N, int K, int Kp, int M,
                                                                const int8_t* __restrict__ q,
                                                                const uint16_t* __restrict__ d,
                                                                const int32_t* __restrict__ s,
-                                                               float* __restrict__ y) {
+                                                               float* __restrict__ y,
+                                                               int32_t* __restrict__ dots) {
     static_assert(KS == 1 || KS == 2 || KS == 4, "32-blocks split over 1, 2 or 4 waves");
     static_assert(G % KP == 0 && (KP > 1 || G <= 2), "units of a step split evenly over KP");
     static_assert(MT % MS == 0, "activation tiles split evenly over MS");
@@ -385,7 +391,10 @@ __global__ __launch_bounds__(64 * RT * KS * KP * MS) void k_small_m_mfma(const u
     auto compute_sb = [&](auto Pc, auto GAc, int g, int buf, int st, bool valid) {
         constexpr int P = decltype(Pc)::value;
         constexpr int ga = decltype(GAc)::value;   // accumulator set
-        constexpr bool PIN = BIG;
+        // (the dots mode drops the scheduling pins: its stores change the
+        // register allocation the pins were placed for; the integer tiles
+        // do not depend on the schedule)
+        constexpr bool PIN = BIG && !DOTS;
         int delta = 0;
         if (!U::ALIGNED) (void)span_base(my_row, st, delta);
         const int ow = buf * GM::BUF + (16 * rt + nl) * GM::WSTRIDE + GM::FRONT + delta + U::UB * g;
@@ -457,6 +466,23 @@ __global__ __launch_bounds__(64 * RT * KS * KP * MS) void k_small_m_mfma(const u
 #pragma unroll
                 for (int e = 0; e < ND; e++)
                     D[e][t] = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, B[e], zero, 0, 0, 0);
+            }
+            if constexpr (DOTS) {
+                // outputs of lane l: activation rows 16t + 4(l/16) + i of weight row n
+                const int blk = blk0 + j;
+                const bool okb = valid && n < N && (FMT != QGEMV_FMT_Q4_0 || blk < nbw);
+                const int ndb = FMT == QGEMV_FMT_Q6_K ? 2 * nb : (FMT == QGEMV_FMT_Q4_0 ? nbw : nb);
+#pragma unroll
+                for (int t = 0; t < TPW; t++)
+#pragma unroll
+                    for (int e = 0; e < ND; e++)
+#pragma unroll
+                        for (int i = 0; i < 4; i++) {
+                            const int m = 16 * (t0 + t) + 4 * kp + i;
+                            const int col = FMT == QGEMV_FMT_Q6_K ? 2 * blk + e : blk;
+                            if (okb && m < M)
+                                dots[((int64_t)m * N + n) * ndb + col] = D[e][t][i];
+                        }
             }
         };
         auto scale_block = [&](int jj, const i32x4 (&D)[ND][TPW]) {
@@ -621,15 +647,15 @@ __global__ __launch_bounds__(64 * RT * KS * KP * MS) void k_small_m_mfma(const u
 // RT: weight tiles per workgroup (the activation staged by a workgroup is
 // shared by 16*RT weight rows); KS, KP: waves sharing a tile's 32-blocks and
 // units; G: units per step; R: steps of global loads in flight.
-template <int FMT, int MT, int RT, int KS, int KP, int MS, int G, int R>
+template <int FMT, int MT, int RT, int KS, int KP, int MS, int G, int R, bool DOTS>
 static hipError_t launch_mfma_cfg(const void* w, int64_t N, int64_t K, int64_t M,
                                   const int8_t* q, const uint16_t* d, const int32_t* s, float* y,
-                                  hipStream_t st) {
+                                  int32_t* dots, hipStream_t st) {
     const int Kp = (int)((K + 255) / 256 * 256);
     const int64_t grid = (N + 16 * RT - 1) / (16 * RT);
-    launch_kernel((k_small_m_mfma<FMT, MT, RT, KS, KP, MS, G, R>), dim3((unsigned)grid),
+    launch_kernel((k_small_m_mfma<FMT, MT, RT, KS, KP, MS, G, R, DOTS>), dim3((unsigned)grid),
                   dim3(64 * RT * KS * KP * MS), 0, st, (const uint8_t*)w, (int)N, (int)K,
-                  Kp, (int)M, q, d, s, y);
+                  Kp, (int)M, q, d, s, y, dots);
     return hipGetLastError();
 }
 
@@ -639,9 +665,10 @@ constexpr int64_t kMfmaWideTiles = 512;
 // Row m of a product depends only on activation row m and on the bucket of
 // M (1-16, 17-32, 33-48, 49-64 rows) and the shape, which fix the
 // configuration and so the fp32 summation order.
-template <int FMT>
+template <int FMT, bool DOTS = false>
 static hipError_t launch_mfma(const void* w, int64_t N, int64_t K, int64_t M, const int8_t* q,
-                              const uint16_t* d, const int32_t* s, float* y, hipStream_t st) {
+                              const uint16_t* d, const int32_t* s, float* y, hipStream_t st,
+                              int32_t* dots = nullptr) {
     const int mt = (int)((M + 15) / 16);
     const bool wide = (N + 15) / 16 >= kMfmaWideTiles;
     // <FMT, MT, RT, KS, KP, MS, G, R>.  Wide matrices: 32 (MT = 1) or 64
@@ -664,45 +691,45 @@ static hipError_t launch_mfma(const void* w, int64_t N, int64_t K, int64_t M, co
             // against 14.1 us at M = 8 on 14336 x 4096 (same process); Q6_K
             // (12288 x 4096) runs 2.4 us slower that way
             if constexpr (FMT == QGEMV_FMT_Q4_K)
-                return launch_mfma_cfg<FMT, 1, 2, 2, 2, 1, 2, 2>(w, N, K, M, q, d, s, y, st);
+                return launch_mfma_cfg<FMT, 1, 2, 2, 2, 1, 2, 2, DOTS>(w, N, K, M, q, d, s, y, dots, st);
             else
-                return launch_mfma_cfg<FMT, 1, 2, 2, 1, 1, 2, 2>(w, N, K, M, q, d, s, y, st);
+                return launch_mfma_cfg<FMT, 1, 2, 2, 1, 1, 2, 2, DOTS>(w, N, K, M, q, d, s, y, dots, st);
         case 2:
             // Q4_K: the units of a step on 2 waves each: 19.7 against 21.8 us
             // at M = 24 on 14336 x 4096 (same process); Q6_K runs slower so
             if constexpr (FMT == QGEMV_FMT_Q4_K)
-                return launch_mfma_cfg<FMT, 2, 4, 2, 2, 1, 2, 2>(w, N, K, M, q, d, s, y, st);
+                return launch_mfma_cfg<FMT, 2, 4, 2, 2, 1, 2, 2, DOTS>(w, N, K, M, q, d, s, y, dots, st);
             else
-                return launch_mfma_cfg<FMT, 2, 4, 2, 1, 1, 2, 2>(w, N, K, M, q, d, s, y, st);
+                return launch_mfma_cfg<FMT, 2, 4, 2, 1, 1, 2, 2, DOTS>(w, N, K, M, q, d, s, y, dots, st);
         case 3:
             if constexpr (FMT == QGEMV_FMT_Q6_K)
-                return launch_mfma_cfg<FMT, 3, RT34, 2, 2, 1, 2, 2>(w, N, K, M, q, d, s, y, st);
+                return launch_mfma_cfg<FMT, 3, RT34, 2, 2, 1, 2, 2, DOTS>(w, N, K, M, q, d, s, y, dots, st);
             else
-                return launch_mfma_cfg<FMT, 3, RT34, 2, 1, 1, 2, 2>(w, N, K, M, q, d, s, y, st);
+                return launch_mfma_cfg<FMT, 3, RT34, 2, 1, 1, 2, 2, DOTS>(w, N, K, M, q, d, s, y, dots, st);
         default:
             // Q6_K: the units of a step on 2 waves each: 71 against 119 us at
             // M = 64 on 12288 x 4096 (same process); Q4_K runs slower so
             if constexpr (FMT == QGEMV_FMT_Q6_K)
-                return launch_mfma_cfg<FMT, 4, RT34, 2, 2, 1, 2, 2>(w, N, K, M, q, d, s, y, st);
+                return launch_mfma_cfg<FMT, 4, RT34, 2, 2, 1, 2, 2, DOTS>(w, N, K, M, q, d, s, y, dots, st);
             else
-                return launch_mfma_cfg<FMT, 4, RT34, 2, 1, 1, 2, 2>(w, N, K, M, q, d, s, y, st);
+                return launch_mfma_cfg<FMT, 4, RT34, 2, 1, 1, 2, 2, DOTS>(w, N, K, M, q, d, s, y, dots, st);
         }
     }
     switch (mt) {
-    case 1: return launch_mfma_cfg<FMT, 1, 1, 2, 4, 1, 4, 2>(w, N, K, M, q, d, s, y, st);
+    case 1: return launch_mfma_cfg<FMT, 1, 1, 2, 4, 1, 4, 2, DOTS>(w, N, K, M, q, d, s, y, dots, st);
     case 2:
         // Q4_K and Q4_0: each unit's 32-blocks halved over 2 waves: 25.4
         // against 29.1 us (Q4_K) and 33.8 against 37.7 us (Q4_0) at M = 24 on
         // 4096 x 14336 (same process); Q6_K no faster
         if constexpr (FMT != QGEMV_FMT_Q6_K)
-            return launch_mfma_cfg<FMT, 2, 1, 2, 2, 2, 2, 2>(w, N, K, M, q, d, s, y, st);
+            return launch_mfma_cfg<FMT, 2, 1, 2, 2, 2, 2, 2, DOTS>(w, N, K, M, q, d, s, y, dots, st);
         else
-            return launch_mfma_cfg<FMT, 2, 1, 1, 4, 2, 4, 2>(w, N, K, M, q, d, s, y, st);
+            return launch_mfma_cfg<FMT, 2, 1, 1, 4, 2, 4, 2, DOTS>(w, N, K, M, q, d, s, y, dots, st);
     case 3:
         // the same split for every format: at M = 48 on 4096 x 14336, Q6_K
         // 57 against 73 us, Q4_K 38 against 46 us, Q4_0 48 against 63 us
-        return launch_mfma_cfg<FMT, 3, 1, 2, 2, 3, 2, 2>(w, N, K, M, q, d, s, y, st);
-    default: return launch_mfma_cfg<FMT, 4, 1, 1, 2, 4, 2, 2>(w, N, K, M, q, d, s, y, st);
+        return launch_mfma_cfg<FMT, 3, 1, 2, 2, 3, 2, 2, DOTS>(w, N, K, M, q, d, s, y, dots, st);
+    default: return launch_mfma_cfg<FMT, 4, 1, 1, 2, 4, 2, 2, DOTS>(w, N, K, M, q, d, s, y, dots, st);
     }
 }
 
@@ -835,6 +862,35 @@ hipError_t launch_small_m(int fmt, const void* w, int64_t N, int64_t K, int64_t 
     case QGEMV_FMT_Q4_K: return launch_mfma<QGEMV_FMT_Q4_K>(w, N, K, M, q, d, s, y, st);
     case QGEMV_FMT_Q6_K: return launch_mfma<QGEMV_FMT_Q6_K>(w, N, K, M, q, d, s, y, st);
     default: return launch_mfma<QGEMV_FMT_Q4_0>(w, N, K, M, q, d, s, y, st);
+    }
+}
+
+// Whether the kernel variant selects for (fmt, N, K, M) has a dots mode (not
+// the wave-stream kernel).  Uses the device's compute-unit count where it
+// decides (256 without a device).
+bool small_m_dots_supported(int fmt, int64_t N, int64_t K, int64_t M, int variant) {
+    if (variant == QGEMV_VARIANT_MFMA_STAGED) return true;
+    if (variant == QGEMV_VARIANT_MFMA_RESIDENT && small_m3_supported(fmt, K, M)) return true;
+    if (variant == QGEMV_VARIANT_MFMA && use_resident_kernel(fmt, N, K, M)) return true;
+    return !use_stream_kernel(fmt, N, M);
+}
+
+hipError_t launch_small_m_dots(int fmt, const void* w, int64_t N, int64_t K, int64_t M,
+                               const int8_t* q, const uint16_t* d, const int32_t* s, float* y,
+                               int variant, int32_t* dots, hipStream_t st) {
+    if (variant != QGEMV_VARIANT_MFMA && variant != QGEMV_VARIANT_MFMA_STAGED &&
+        variant != QGEMV_VARIANT_MFMA_RESIDENT)
+        return hipErrorNotSupported;
+    // the kernel launch_small_m would run for this variant
+    if ((variant == QGEMV_VARIANT_MFMA_RESIDENT && small_m3_supported(fmt, K, M)) ||
+        (variant == QGEMV_VARIANT_MFMA && use_resident_kernel(fmt, N, K, M)))
+        return launch_small_m3_dots(fmt, w, N, K, M, q, d, s, y, dots, st);
+    if (variant != QGEMV_VARIANT_MFMA_STAGED && use_stream_kernel(fmt, N, M))
+        return hipErrorNotSupported;   // the wave-stream kernel has no dots mode
+    switch (fmt) {
+    case QGEMV_FMT_Q4_K: return launch_mfma<QGEMV_FMT_Q4_K, true>(w, N, K, M, q, d, s, y, st, dots);
+    case QGEMV_FMT_Q6_K: return launch_mfma<QGEMV_FMT_Q6_K, true>(w, N, K, M, q, d, s, y, st, dots);
+    default: return launch_mfma<QGEMV_FMT_Q4_0, true>(w, N, K, M, q, d, s, y, st, dots);
     }
 }
 

@@ -80,12 +80,14 @@ __device__ __forceinline__ void static_for(F&& f) {
 // NST: stages per wave slice (the slice holds at most NST * NSP
 // super-blocks).  LDS: the 8 stage buffers, dx and dx*s of every block and
 // row ([block][row], fp32), two tiles' partial-sum slots.
-template <int NST>
+// DOTS (validation): every int32 MFMA tile is also stored to dots [M][N][Kp/32],
+// the raw dots of the unsigned codes before any scale or min.
+template <int NST, bool DOTS = false>
 __global__ __launch_bounds__(NTH) void k_sm3_q4k(const uint8_t* __restrict__ w, int N, int Kp,
                                                  int M, const int8_t* __restrict__ q,
                                                  const uint16_t* __restrict__ d,
                                                  const int32_t* __restrict__ s,
-                                                 float* __restrict__ y) {
+                                                 float* __restrict__ y, int32_t* __restrict__ dots) {
     constexpr int NBMAX = NW * NST * NSP * 8;   // blocks of the longest row taken
     __shared__ __align__(16) uint8_t wbuf[NW * WBUF];
     __shared__ __align__(16) float dxl[NBMAX * 16];
@@ -188,6 +190,7 @@ __global__ __launch_bounds__(NTH) void k_sm3_q4k(const uint8_t* __restrict__ w, 
     f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
     const i32x4 zero = {0, 0, 0, 0};
 
+    int tile_now = 0;   // the tile whose stage compute() works on
     // the MFMAs and epilogue of stage st of the current tile (in mybuf)
     auto compute = [&](auto STc) {
         constexpr int st = decltype(STc)::value;
@@ -216,6 +219,15 @@ __global__ __launch_bounds__(NTH) void k_sm3_q4k(const uint8_t* __restrict__ w, 
                     const long Bo = (long)(((uint64_t)bv.y << 32) | bv.x);
                     const long Ao = (long)(((uint64_t)A[st][h][jj].y << 32) | A[st][h][jj].x);
                     const i32x4 D = __builtin_amdgcn_mfma_i32_16x16x32_i8(Ao, Bo, zero, 0, 0, 0);
+                    if constexpr (DOTS) {
+                        const int n = 16 * tile_now + n16;
+#pragma unroll
+                        for (int i = 0; i < 4; i++) {
+                            const int m = 4 * g + i;
+                            if (ok && m < M && n < N)
+                                dots[((int64_t)m * N + n) * nb + 8 * sbc + jj] = D[i];
+                        }
+                    }
                     const float ws =
                         fd * (float)((((jj < 4 ? slo : shi) >> (8 * (jj & 3))) & 0xFFu));
                     const f32x4 x4 = *reinterpret_cast<const f32x4*>(dxb + 16 * jj + 4 * g);
@@ -256,6 +268,7 @@ __global__ __launch_bounds__(NTH) void k_sm3_q4k(const uint8_t* __restrict__ w, 
             constexpr int st = decltype(STc)::value;
             constexpr int set = (PAR + st) % DEPTH;
             const int it = kt * NST + st;
+            tile_now = b + kt * G;
             commit(it, R[set]);
             load_item(it + DEPTH, R[set]);
             __builtin_amdgcn_sched_barrier(0);
@@ -285,9 +298,10 @@ __global__ __launch_bounds__(NTH) void k_sm3_q4k(const uint8_t* __restrict__ w, 
     }
 }
 
-template <int NST>
+template <int NST, bool DOTS>
 hipError_t launch_q4k(const void* w, int64_t N, int64_t K, int64_t M, const int8_t* q,
-                      const uint16_t* d, const int32_t* s, float* y, hipStream_t st) {
+                      const uint16_t* d, const int32_t* s, float* y, int32_t* dots,
+                      hipStream_t st) {
     const int Kp = (int)((K + 255) / 256 * 256);
     int cus = 0, dev = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
@@ -298,8 +312,8 @@ hipError_t launch_q4k(const void* w, int64_t N, int64_t K, int64_t M, const int8
     }
     const int64_t ntiles = (N + 15) / 16;
     const int64_t grid = ntiles < cus ? ntiles : cus;
-    launch_kernel(k_sm3_q4k<NST>, dim3((unsigned)grid), dim3(NTH), 0, st, (const uint8_t*)w,
-                  (int)N, Kp, (int)M, q, d, s, y);
+    launch_kernel(k_sm3_q4k<NST, DOTS>, dim3((unsigned)grid), dim3(NTH), 0, st,
+                  (const uint8_t*)w, (int)N, Kp, (int)M, q, d, s, y, dots);
     return hipGetLastError();
 }
 
@@ -312,18 +326,32 @@ bool small_m3_supported(int fmt, int64_t K, int64_t M) {
     return spw <= 8 * sm3::NSP;
 }
 
-hipError_t launch_small_m3(int fmt, const void* w, int64_t N, int64_t K, int64_t M,
-                           const int8_t* q, const uint16_t* d, const int32_t* s, float* y,
-                           hipStream_t st) {
-    if (!small_m3_supported(fmt, K, M)) return hipErrorNotSupported;
+template <bool DOTS>
+static hipError_t launch_m3(const void* w, int64_t N, int64_t K, int64_t M, const int8_t* q,
+                            const uint16_t* d, const int32_t* s, float* y, int32_t* dots,
+                            hipStream_t st) {
     const int64_t nsb = (K + 255) / 256;
     const int64_t spw = (nsb + sm3::NW - 1) / sm3::NW;
     const int64_t nst = (spw + sm3::NSP - 1) / sm3::NSP;
     // an even number of stages (a slice's stages past its super-blocks add
     // zeros)
-    if (nst <= 2) return sm3::launch_q4k<2>(w, N, K, M, q, d, s, y, st);
-    if (nst <= 4) return sm3::launch_q4k<4>(w, N, K, M, q, d, s, y, st);
-    return sm3::launch_q4k<8>(w, N, K, M, q, d, s, y, st);
+    if (nst <= 2) return sm3::launch_q4k<2, DOTS>(w, N, K, M, q, d, s, y, dots, st);
+    if (nst <= 4) return sm3::launch_q4k<4, DOTS>(w, N, K, M, q, d, s, y, dots, st);
+    return sm3::launch_q4k<8, DOTS>(w, N, K, M, q, d, s, y, dots, st);
+}
+
+hipError_t launch_small_m3(int fmt, const void* w, int64_t N, int64_t K, int64_t M,
+                           const int8_t* q, const uint16_t* d, const int32_t* s, float* y,
+                           hipStream_t st) {
+    if (!small_m3_supported(fmt, K, M)) return hipErrorNotSupported;
+    return launch_m3<false>(w, N, K, M, q, d, s, y, nullptr, st);
+}
+
+hipError_t launch_small_m3_dots(int fmt, const void* w, int64_t N, int64_t K, int64_t M,
+                                const int8_t* q, const uint16_t* d, const int32_t* s, float* y,
+                                int32_t* dots, hipStream_t st) {
+    if (!small_m3_supported(fmt, K, M)) return hipErrorNotSupported;
+    return launch_m3<true>(w, N, K, M, q, d, s, y, dots, st);
 }
 
 }  // namespace qgemv

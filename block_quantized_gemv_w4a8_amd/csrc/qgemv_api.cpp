@@ -406,6 +406,44 @@ qgemv_status qgemm_q4_0_small_m(const void* w, int64_t N, int64_t K, int64_t M, 
                           stream);
 }
 
+qgemv_status qgemm_small_m_block_dots(int fmt, const void* w, int64_t N, int64_t K, int64_t M,
+                                     const int8_t* q, const uint16_t* d, const int32_t* s,
+                                     float* y, int variant, int32_t* dots,
+                                     qgemv_stream_t stream) {
+    const char* name = "qgemm_small_m_block_dots";
+    if (N < 0 || M < 0) return fail(QGEMV_E_SHAPE, "%s: negative N or M", name);
+    if (N == 0 || M == 0) return ok();
+    if (!w || !q || !d || !s || !y || !dots)
+        return fail(QGEMV_E_NULL, "%s: NULL pointer argument", name);
+    qgemv_status st = check_k(K);
+    if (st != QGEMV_OK) return st;
+    if (N > INT32_MAX) return fail(QGEMV_E_SHAPE, "%s: N exceeds 2^31-1", name);
+    if (fmt != QGEMV_FMT_Q4_K && fmt != QGEMV_FMT_Q6_K && fmt != QGEMV_FMT_Q4_0)
+        return fail(QGEMV_E_UNSUPPORTED, "%s: format %d has no small-M product", name, fmt);
+    if (K > QGEMV_K_MAX)
+        return fail(QGEMV_E_UNSUPPORTED, "%s: K = %lld exceeds QGEMV_K_MAX", name, (long long)K);
+    if (M > QGEMV_M_MAX)
+        return fail(QGEMV_E_UNSUPPORTED, "%s: M = %lld exceeds QGEMV_M_MAX = %d", name,
+                    (long long)M, QGEMV_M_MAX);
+    if (variant != QGEMV_VARIANT_MFMA && variant != QGEMV_VARIANT_MFMA_STAGED &&
+        variant != QGEMV_VARIANT_MFMA_RESIDENT)
+        return fail(QGEMV_E_UNSUPPORTED,
+                    "%s: variant %d: only the MFMA, MFMA_STAGED and MFMA_RESIDENT variants "
+                    "have a dots mode", name, variant);
+    if (variant != QGEMV_VARIANT_MFMA_STAGED && !qgemv::small_m_dots_supported(fmt, N, K, M, variant))
+        return fail(QGEMV_E_UNSUPPORTED,
+                    "%s: the kernel variant %d selects for this shape (the wave-stream "
+                    "kernel) has no dots mode", name, variant);
+    if (!aligned(w, 16)) return fail(QGEMV_E_ALIGN, "%s: w must be 16-byte aligned", name);
+    if ((st = check_act_align(q, d, s)) != QGEMV_OK) return st;
+    if (!aligned(y, 4) || !aligned(dots, 4))
+        return fail(QGEMV_E_ALIGN, "%s: y and dots must be 4-byte aligned", name);
+    if ((st = check_device()) != QGEMV_OK) return st;
+    return launched(qgemv::launch_small_m_dots(fmt, w, N, K, M, q, d, s, y, variant, dots,
+                                               (hipStream_t)stream),
+                    name);
+}
+
 qgemv_status qgemv_silu_mul_quantize(const float* gu, int64_t N, int8_t* q, uint16_t* d,
                                      int32_t* s, float* h, qgemv_stream_t stream) {
     const char* name = "qgemv_silu_mul_quantize";

@@ -128,6 +128,18 @@ bool small_m3_supported(int fmt, int64_t K, int64_t M);
 hipError_t launch_small_m3(int fmt, const void* w, int64_t N, int64_t K, int64_t M,
                            const int8_t* q, const uint16_t* d, const int32_t* s, float* y,
                            hipStream_t st);
+// the same kernel also storing its raw int32 MFMA tiles to dots (validation)
+hipError_t launch_small_m3_dots(int fmt, const void* w, int64_t N, int64_t K, int64_t M,
+                                const int8_t* q, const uint16_t* d, const int32_t* s, float* y,
+                                int32_t* dots, hipStream_t st);
+// Validation: the small-M product of variant (MFMA, MFMA_STAGED or
+// MFMA_RESIDENT) run by the kernel that variant selects, storing every raw
+// int32 MFMA tile to dots [M][N][nb] as well as y; hipErrorNotSupported
+// (nothing launched) where that kernel has no such mode.
+bool small_m_dots_supported(int fmt, int64_t N, int64_t K, int64_t M, int variant);
+hipError_t launch_small_m_dots(int fmt, const void* w, int64_t N, int64_t K, int64_t M,
+                               const int8_t* q, const uint16_t* d, const int32_t* s, float* y,
+                               int variant, int32_t* dots, hipStream_t st);
 
 // The small-M product on int8 matrix cores with wave-private weight streams
 // (fmt: QGEMV_FMT_Q4_K, QGEMV_FMT_Q6_K or QGEMV_FMT_Q4_0; 1 <= M <= 64).

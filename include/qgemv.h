@@ -225,6 +225,25 @@ qgemv_status qgemm_q4_k_small_m(const void* w, int64_t N, int64_t K, int64_t M,
  * pass of its streaming kernel, with its bits where it streams the rows; rows
  * of more than 16384 weights: the batch-1 GEMV on each row), or
  * QGEMV_VARIANT_AUTO (DOT4 up to M = 4, MFMA from M = 5). */
+/* Validation: the small-M product of variant (QGEMV_VARIANT_MFMA,
+ * _MFMA_STAGED or _MFMA_RESIDENT) run by the kernel that variant selects for
+ * this format and shape, which also stores every raw int32 matrix-core tile
+ * to dots: int32 [M][N][nb], the dots of the unsigned codes before any
+ * scale, offset or min -- Q4_K: sum code*q per 32-block (nb = Kp/32);
+ * Q4_0: sum code*q with codes 0..15 per 32-block, i.e. the block dot of
+ * qgemv_block_dots plus 8 * s (nb = K/32); Q6_K: sum code*q with codes 0..63
+ * per 16-group, i.e. qgemv_block_dots' value plus 32 * (the group's code sum)
+ * (nb = Kp/16) ("Backends and hardware", section "CPU": the way to tell a
+ * SIMD bug from a block bug).  y [M][N] receives the product as from the
+ * small-M entry.  fmt: QGEMV_FMT_Q4_K, _Q6_K or _Q4_0.  Other variants, and
+ * shapes for which the variant selects the wave-stream kernel (Q6_K from
+ * M = 49 under MFMA), return QGEMV_E_UNSUPPORTED.  Other arguments, limits and
+ * errors as for qgemm_q4_k_small_m. */
+qgemv_status qgemm_small_m_block_dots(int fmt, const void* w, int64_t N, int64_t K,
+                                     int64_t M, const int8_t* q, const uint16_t* d,
+                                     const int32_t* s, float* y, int variant,
+                                     int32_t* dots, qgemv_stream_t stream);
+
 qgemv_status qgemm_q6_k_small_m(const void* w, int64_t N, int64_t K, int64_t M,
                                 const int8_t* q, const uint16_t* d, const int32_t* s,
                                 float* y, int variant, qgemv_stream_t stream);

@@ -265,3 +265,24 @@ def test_gates_block_dots_staged():
     assert _status(B, Q4K, A, 4, 256, 0, 4, A, A, A, 1, A + 2, 0) == qg.QGEMV_E_ALIGN
     if _no_gpu():
         assert _status(B, R8, A, 4, 14336, 0, 4, A, A, A, 4, A, 0) == qg.QGEMV_E_DEVICE
+
+
+def test_gates_small_m_block_dots():
+    qg = _lib()
+    B = "qgemm_small_m_block_dots"   # fmt, w, N, K, M, q, d, s, y, variant, dots, stream
+    Q4K, Q6K, MF = qg.QGEMV_FMT_Q4_K, qg.QGEMV_FMT_Q6_K, qg.QGEMV_VARIANT_MFMA
+    assert _status(B, Q4K, None, 0, 256, 4, None, None, None, None, MF, None, 0) == qg.QGEMV_OK
+    assert _status(B, Q4K, A, -1, 256, 4, A, A, A, A, MF, A, 0) == qg.QGEMV_E_SHAPE
+    assert _status(B, Q4K, A, 8, 256, 4, A, A, A, A, MF, None, 0) == qg.QGEMV_E_NULL
+    assert _status(B, Q4K, A, 8, 48, 4, A, A, A, A, MF, A, 0) == qg.QGEMV_E_SHAPE
+    assert _status(B, qg.QGEMV_FMT_Q8_0, A, 8, 256, 4, A, A, A, A, MF, A, 0) == qg.QGEMV_E_UNSUPPORTED
+    assert _status(B, Q4K, A, 8, 256, 65, A, A, A, A, MF, A, 0) == qg.QGEMV_E_UNSUPPORTED
+    assert _status(B, Q4K, A, 8, 256, 4, A, A, A, A, qg.QGEMV_VARIANT_DOT4, A, 0) == qg.QGEMV_E_UNSUPPORTED
+    assert _status(B, Q4K, A, 8, 256, 4, A, A, A, A, qg.QGEMV_VARIANT_MFMA_STREAM, A, 0) == qg.QGEMV_E_UNSUPPORTED
+    # Q6_K at M = 64 under MFMA takes the wave-stream kernel: no dots mode
+    assert _status(B, Q6K, A, 4096, 14336, 64, A, A, A, A, MF, A, 0) == qg.QGEMV_E_UNSUPPORTED
+    assert _status(B, Q4K, A + 8, 8, 256, 4, A, A, A, A, MF, A, 0) == qg.QGEMV_E_ALIGN
+    assert _status(B, Q4K, A, 8, 256, 4, A, A, A, A, MF, A + 2, 0) == qg.QGEMV_E_ALIGN
+    if _no_gpu():
+        assert _status(B, Q6K, A, 4096, 14336, 64, A, A, A, A, qg.QGEMV_VARIANT_MFMA_STAGED, A, 0) \
+            == qg.QGEMV_E_DEVICE
