@@ -42,8 +42,11 @@ WORKLOAD = ("llama3.1-8b decode step, batch 1: ffn gate|up q4_k 28672x4096 with 
             "(activation quantization inside the gate|up and lm_head launches; "
             "q6_k repacked at load into aligned 8-super-block tiles, same bytes)")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_q6k_lm_head.json")
-KERNEL_SOURCES = ["qgemv_device.h", "qgemv_quant.h", "k_gemv.h", "k_gemv.hip", "k_gemv_q6_k_r8.hip", "k_quantize.hip",
-                  "qgemv_api.cpp"]
+# the sources the lm_head kernel is built from (its unit code, quantiser,
+# kernel template and launcher); a stored traffic profile applies only while
+# they are unchanged
+KERNEL_SOURCES = ["qgemv_device.h", "qgemv_quant.h", "k_gemv.h", "k_gemv.hip",
+                  "k_gemv_q6_k_r8.hip"]
 
 
 def log(*a):
