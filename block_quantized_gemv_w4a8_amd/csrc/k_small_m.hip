@@ -217,7 +217,8 @@ struct MfmaGeom {
 // (nb = Kp/32 blocks, Q4_0 K/32; Q6_K Kp/16 groups): the raw integer dots of
 // the unsigned codes (Q4_K and Q4_0: sum code*q per 32-block; Q6_K: per
 // 16-group) before any scale, offset or min is applied.
-template <int FMT, int MT, int RT, int KS, int KP, int MS, int G, int R, bool DOTS = false>
+template <int FMT, int MT, int RT, int KS, int KP, int MS, int G, int R, bool DOTS = false,
+          bool TWO = false>
 __global__ __launch_bounds__(64 * RT * KS * KP * MS) void k_small_m_mfma(const uint8_t* __restrict__ w,
                                                                int N, int K, int Kp, int M,
                                                                const int8_t* __restrict__ q,
@@ -228,6 +229,8 @@ __global__ __launch_bounds__(64 * RT * KS * KP * MS) void k_small_m_mfma(const u
     static_assert(KS == 1 || KS == 2 || KS == 4, "32-blocks split over 1, 2 or 4 waves");
     static_assert(G % KP == 0 && (KP > 1 || G <= 2), "units of a step split evenly over KP");
     static_assert(MT % MS == 0, "activation tiles split evenly over MS");
+    static_assert(!TWO || (FMT == QGEMV_FMT_Q4_K && MT == 1 && KS <= 4),
+                  "two-block tiles: Q4_K, at most 8 activation rows, pairs of 32-blocks per wave");
     constexpr int TPW = MT / MS;                             // activation tiles per wave
     using GM = MfmaGeom<FMT, MT, RT, G>;
     using U = SmUnit<FMT>;
@@ -236,9 +239,10 @@ __global__ __launch_bounds__(64 * RT * KS * KP * MS) void k_small_m_mfma(const u
     constexpr int BPW = 8 / KS;                              // 32-blocks per wave and unit
     constexpr int WCH = ROWS * NCH;                          // 16-byte weight chunks per step
     constexpr int WPT = (WCH + NT - 1) / NT;
-    constexpr int ACH = G * MP * 16;                         // 16-byte code chunks per step
+    constexpr int MA = TWO ? 8 : MP;                         // activation rows staged
+    constexpr int ACH = G * MA * 16;                         // 16-byte code chunks per step
     constexpr int APT = (ACH + NT - 1) / NT;
-    constexpr int SCH = G * 8 * MP;                          // scale entries per step
+    constexpr int SCH = G * 8 * MA;                          // scale entries per step
     constexpr int SPT = (SCH + NT - 1) / NT;
     constexpr int NPART = KS * KP;                           // partial sums per tile
     constexpr int PART_BYTES = (NPART - 1) * RT * MT * 4 * 64 * 4;
@@ -304,7 +308,7 @@ __global__ __launch_bounds__(64 * RT * KS * KP * MS) void k_small_m_mfma(const u
 #pragma unroll
         for (int k = 0; k < APT; k++) {
             const int c = min(tid + NT * k, ACH - 1);
-            const int g = c / (MP * 16), rem = c - g * (MP * 16);
+            const int g = c / (MA * 16), rem = c - g * (MA * 16);
             const int m = min(rem >> 4, M - 1), cc = rem & 15;
             const int u = min(G * st + g, nunits - 1);
             r.ac[k] = *reinterpret_cast<const u32x4*>(q + (int64_t)m * Kp + 256 * u + 16 * cc);
@@ -312,8 +316,8 @@ __global__ __launch_bounds__(64 * RT * KS * KP * MS) void k_small_m_mfma(const u
 #pragma unroll
         for (int k = 0; k < SPT; k++) {
             const int c = min(tid + NT * k, SCH - 1);
-            const int g = c / (8 * MP), rem = c - g * (8 * MP);
-            const int j = rem / MP, m = min(rem - j * MP, M - 1);
+            const int g = c / (8 * MA), rem = c - g * (8 * MA);
+            const int j = rem / MA, m = min(rem - j * MA, M - 1);
             const int u = min(G * st + g, nunits - 1);
             const int64_t b = (int64_t)m * nb + 8 * u + j;
             r.dh[k] = d[b];
@@ -336,7 +340,7 @@ __global__ __launch_bounds__(64 * RT * KS * KP * MS) void k_small_m_mfma(const u
         for (int k = 0; k < APT; k++) {
             const int c = tid + NT * k;
             if (c < ACH) {
-                const int g = c / (MP * 16), rem = c - g * (MP * 16);
+                const int g = c / (MA * 16), rem = c - g * (MA * 16);
                 *reinterpret_cast<u32x4*>(act + g * GM::ASTAGE + (rem >> 4) * GM::ASTRIDE +
                                           16 * (rem & 15)) = r.ac[k];
                 if (U::S16) {
@@ -354,11 +358,12 @@ __global__ __launch_bounds__(64 * RT * KS * KP * MS) void k_small_m_mfma(const u
         for (int k = 0; k < SPT; k++) {
             const int c = tid + NT * k;
             if (c < SCH) {
-                const int g = c / (8 * MP), rem = c - g * (8 * MP);   // rem = j * MP + m
+                const int g = c / (8 * MA), rem = c - g * (8 * MA);   // rem = j * MA + m
+                const int j = rem / MA, i = j * MP + (rem - j * MA);  // [block][row] slot
                 float* dx = reinterpret_cast<float*>(act + g * GM::ASTAGE + GM::ACODES);
                 const float f = h2f(r.dh[k]);
-                dx[rem] = f;
-                dx[8 * MP + rem] = f * (float)r.sv[k];
+                dx[i] = f;
+                dx[8 * MP + i] = f * (float)r.sv[k];
             }
         }
     };
@@ -518,14 +523,67 @@ __global__ __launch_bounds__(64 * RT * KS * KP * MS) void k_small_m_mfma(const u
                 for (int t = 0; t < TPW; t++) asm volatile("" : "+v"(acc[ga][t]));
             }
         };
-        i32x4 D2[2][ND][TPW];
-        mfma_block(0, D2[0]);
+        // Two-block tiles (at most 8 activation rows): one
+        // v_mfma_i32_16x16x64_i8 per pair of 32-blocks (jp, jp + 1).  Tile
+        // rows 0-7 are activation rows 0-7 against block jp (K lanes 0-31, the
+        // quarters kp < 2; zeros in K lanes 32-63) and rows 8-15 the same
+        // activation rows against block jp + 1 (K lanes 32-63), so every
+        // output is one exact block dot and no tile row is padding.  Lane
+        // (nl, kp) holds rows 4*kp + i: block jp + (kp >= 2) of activation row
+        // 4*(kp & 1) + i; the two halves of a row meet at the end.
+        auto mfma_pair = [&](int pi, i32x4& E) {
+            const int jp = P * BPW + 2 * pi;              // even block of the pair
+            // weights: bytes 32*(jp/2) + 16*(kp&1) .. +15 of the unit's codes;
+            // low nibbles are block jp, high nibbles block jp + 1
+            const u32x4 v = *reinterpret_cast<const u32x4*>(smem + ow + 16 + 16 * jp + 16 * (kp & 1));
+            const int sh = kp < 2 ? 0 : 4;
+            const i32x4 B = {(int)((v.x >> sh) & LO4), (int)((v.y >> sh) & LO4),
+                             (int)((v.z >> sh) & LO4), (int)((v.w >> sh) & LO4)};
+            const int jb = jp + (kp >> 1);
+            const u32x4 a = *reinterpret_cast<const u32x4*>(
+                smem + oa + (nl & 7) * GM::ASTRIDE + 32 * jb + 16 * (kp & 1));
+            const bool mine = (nl < 8) == (kp < 2);
+            const i32x4 A = {mine ? (int)a.x : 0, mine ? (int)a.y : 0, mine ? (int)a.z : 0,
+                             mine ? (int)a.w : 0};
+            E = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, B, zero, 0, 0, 0);
+            if constexpr (DOTS) {
+                const int blk = blk0 + jb;
+                const bool okb = valid && n < N;
 #pragma unroll
-        for (int jj = 1; jj < BPW; jj++) {
-            mfma_block(jj, D2[jj & 1]);
-            scale_block(jj - 1, D2[(jj - 1) & 1]);
+                for (int i = 0; i < 4; i++) {
+                    const int m = 4 * (kp & 1) + i;
+                    if (okb && m < M) dots[((int64_t)m * N + n) * nb + blk] = E[i];
+                }
+            }
+        };
+        auto scale_pair = [&](int pi, const i32x4& E) {
+            const int jp = P * BPW + 2 * pi;
+            const int jb = jp + (kp >> 1);
+            const float ws = fd * (float)(((jb >= 4 ? shi : slo) >> (8 * (jb & 3))) & 0xFFu);
+            const f32x4 x4 = *reinterpret_cast<const f32x4*>(
+                smem + oa + GM::ACODES + 4 * (jb * MP + 4 * (kp & 1)));
+#pragma unroll
+            for (int i = 0; i < 4; i++) acc[ga][0][i] = fmaf((float)E[i], ws * x4[i], acc[ga][0][i]);
+        };
+        if constexpr (TWO) {
+            i32x4 E2[2];
+            mfma_pair(0, E2[0]);
+#pragma unroll
+            for (int pi = 1; pi < BPW / 2; pi++) {
+                mfma_pair(pi, E2[pi & 1]);
+                scale_pair(pi - 1, E2[(pi - 1) & 1]);
+            }
+            scale_pair(BPW / 2 - 1, E2[(BPW / 2 - 1) & 1]);
+        } else {
+            i32x4 D2[2][ND][TPW];
+            mfma_block(0, D2[0]);
+#pragma unroll
+            for (int jj = 1; jj < BPW; jj++) {
+                mfma_block(jj, D2[jj & 1]);
+                scale_block(jj - 1, D2[(jj - 1) & 1]);
+            }
+            scale_block(BPW - 1, D2[(BPW - 1) & 1]);
         }
-        scale_block(BPW - 1, D2[(BPW - 1) & 1]);
 
         // the second products: K lane kp of an fp32 MFMA carries one block
         // (Q4_K, Q4_0: block 4*kk + kp of the unit, lanes whose block belongs
@@ -560,7 +618,8 @@ __global__ __launch_bounds__(64 * RT * KS * KP * MS) void k_small_m_mfma(const u
                 }
 #pragma unroll
                 for (int t = 0; t < TPW; t++) {
-                    const float a = dxs[(jg + kp) * MP + 16 * (t0 + t) + nl];
+                    // (two-block tiles stage activation rows 0-7 only)
+                    const float a = TWO && nl >= 8 ? 0.0f : dxs[(jg + kp) * MP + 16 * (t0 + t) + nl];
                     acc2[ga][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc2[ga][t], 0, 0, 0);
                 }
             }
@@ -615,6 +674,17 @@ __global__ __launch_bounds__(64 * RT * KS * KP * MS) void k_small_m_mfma(const u
     // step's barrier); part 0 adds them in part order and stores
     float* pbuf = reinterpret_cast<float*>(smem);
     auto partial = [&](int t, int i) {
+        if constexpr (TWO) {
+            // lanes kp < 2 hold the even blocks of rows 4*kp + i, lanes 32
+            // above them the odd blocks of the same rows
+            float a = acc[0][t][i], m2 = acc2[0][t][i];
+#pragma unroll
+            for (int g = 1; g < AG; g++) {
+                a += acc[g][t][i];
+                m2 += acc2[g][t][i];
+            }
+            return (a + __shfl_xor(a, 32)) - m2;
+        }
         float v = acc[0][t][i] - acc2[0][t][i];
 #pragma unroll
         for (int g = 1; g < AG; g++) v += acc[g][t][i] - acc2[g][t][i];
@@ -623,11 +693,17 @@ __global__ __launch_bounds__(64 * RT * KS * KP * MS) void k_small_m_mfma(const u
     auto pidx = [&](int p, int t, int i) {   // t: this wave's tile index 0 .. TPW-1
         return (((p - 1) * RT + rt) * MT * 4 + 4 * (t0 + t) + i) * 64 + lane;
     };
+    // (formed by every lane of the wave: the two-block halves meet across lanes)
+    float pv[TPW][4];
+#pragma unroll
+    for (int t = 0; t < TPW; t++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) pv[t][i] = partial(t, i);
     if (NPART > 1 && part > 0) {
 #pragma unroll
         for (int t = 0; t < TPW; t++)
 #pragma unroll
-            for (int i = 0; i < 4; i++) pbuf[pidx(part, t, i)] = partial(t, i);
+            for (int i = 0; i < 4; i++) pbuf[pidx(part, t, i)] = pv[t][i];
     }
     if (NPART > 1) __syncthreads();
     if (part == 0 && n < N) {
@@ -635,7 +711,7 @@ __global__ __launch_bounds__(64 * RT * KS * KP * MS) void k_small_m_mfma(const u
         for (int t = 0; t < TPW; t++)
 #pragma unroll
             for (int i = 0; i < 4; i++) {
-                float v = partial(t, i);
+                float v = pv[t][i];
 #pragma unroll
                 for (int p = 1; p < NPART; p++) v += pbuf[pidx(p, t, i)];
                 const int m = 16 * (t0 + t) + 4 * kp + i;
@@ -647,13 +723,14 @@ __global__ __launch_bounds__(64 * RT * KS * KP * MS) void k_small_m_mfma(const u
 // RT: weight tiles per workgroup (the activation staged by a workgroup is
 // shared by 16*RT weight rows); KS, KP: waves sharing a tile's 32-blocks and
 // units; G: units per step; R: steps of global loads in flight.
-template <int FMT, int MT, int RT, int KS, int KP, int MS, int G, int R, bool DOTS>
+template <int FMT, int MT, int RT, int KS, int KP, int MS, int G, int R, bool DOTS,
+          bool TWO = false>
 static hipError_t launch_mfma_cfg(const void* w, int64_t N, int64_t K, int64_t M,
                                   const int8_t* q, const uint16_t* d, const int32_t* s, float* y,
                                   int32_t* dots, hipStream_t st) {
     const int Kp = (int)((K + 255) / 256 * 256);
     const int64_t grid = (N + 16 * RT - 1) / (16 * RT);
-    launch_kernel((k_small_m_mfma<FMT, MT, RT, KS, KP, MS, G, R, DOTS>), dim3((unsigned)grid),
+    launch_kernel((k_small_m_mfma<FMT, MT, RT, KS, KP, MS, G, R, DOTS, TWO>), dim3((unsigned)grid),
                   dim3(64 * RT * KS * KP * MS), 0, st, (const uint8_t*)w, (int)N, (int)K,
                   Kp, (int)M, q, d, s, y, dots);
     return hipGetLastError();
@@ -663,8 +740,9 @@ static hipError_t launch_mfma_cfg(const void* w, int64_t N, int64_t K, int64_t M
 constexpr int64_t kMfmaWideTiles = 512;
 
 // Row m of a product depends only on activation row m and on the bucket of
-// M (1-16, 17-32, 33-48, 49-64 rows) and the shape, which fix the
-// configuration and so the fp32 summation order.
+// M (1-16, 17-32, 33-48, 49-64 rows; Q4_K splits the first into 1-8, two-block
+// tiles, and 9-16) and the shape, which fix the configuration and so the fp32
+// summation order.
 template <int FMT, bool DOTS = false>
 static hipError_t launch_mfma(const void* w, int64_t N, int64_t K, int64_t M, const int8_t* q,
                               const uint16_t* d, const int32_t* s, float* y, hipStream_t st,
@@ -690,10 +768,16 @@ static hipError_t launch_mfma(const void* w, int64_t N, int64_t K, int64_t M, co
             // Q4_K: the 2 units of a step on 2 waves each (8 waves): 13.2
             // against 14.1 us at M = 8 on 14336 x 4096 (same process); Q6_K
             // (12288 x 4096) runs 2.4 us slower that way
-            if constexpr (FMT == QGEMV_FMT_Q4_K)
+            // At most 8 activation rows (Q4_K): two-block tiles, two 32-blocks
+            // per i8 MFMA with no padding rows (13.8 against 14.1 us at M = 8
+            // and 9 on 14336 x 4096; 13.6 against 15.7 us on 4096 x 14336)
+            if constexpr (FMT == QGEMV_FMT_Q4_K) {
+                if (M <= 8)
+                    return launch_mfma_cfg<FMT, 1, 2, 2, 2, 1, 2, 2, DOTS, true>(w, N, K, M, q, d, s, y, dots, st);
                 return launch_mfma_cfg<FMT, 1, 2, 2, 2, 1, 2, 2, DOTS>(w, N, K, M, q, d, s, y, dots, st);
-            else
+            } else {
                 return launch_mfma_cfg<FMT, 1, 2, 2, 1, 1, 2, 2, DOTS>(w, N, K, M, q, d, s, y, dots, st);
+            }
         case 2:
             // Q4_K: the units of a step on 2 waves each: 19.7 against 21.8 us
             // at M = 24 on 14336 x 4096 (same process); Q6_K runs slower so
@@ -725,7 +809,10 @@ static hipError_t launch_mfma(const void* w, int64_t N, int64_t K, int64_t M, co
         }
     }
     switch (mt) {
-    case 1: return launch_mfma_cfg<FMT, 1, 1, 2, 4, 1, 4, 2, DOTS>(w, N, K, M, q, d, s, y, dots, st);
+    case 1:
+        if (FMT == QGEMV_FMT_Q4_K && M <= 8)
+            return launch_mfma_cfg<FMT, 1, 1, 2, 4, 1, 4, 2, DOTS, FMT == QGEMV_FMT_Q4_K>(w, N, K, M, q, d, s, y, dots, st);
+        return launch_mfma_cfg<FMT, 1, 1, 2, 4, 1, 4, 2, DOTS>(w, N, K, M, q, d, s, y, dots, st);
     case 2:
         // Q4_K and Q4_0: each unit's 32-blocks halved over 2 waves: 25.4
         // against 29.1 us (Q4_K) and 33.8 against 37.7 us (Q4_0) at M = 24 on
