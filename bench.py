@@ -678,6 +678,15 @@ def extras(qg, torch, np, synth, dev, R, c2, c3, args):
         qg.qgemv_quantize_act(x, 1, Kgu, Kgu, q, d, s)
     ex["host_us_per_call_python_binding"] = round((time.perf_counter() - t0) / 2000 * 1e6, 2)
     torch.cuda.synchronize()
+    # the same C-ABI call refused at its argument checks (NULL x: nothing is
+    # launched): the binding's and the library's own host cost; the rest of
+    # a call is the HIP runtime's kernel submission
+    ptr_args = (q.data_ptr(), d.data_ptr(), s.data_ptr())
+    t0 = time.perf_counter()
+    for _ in range(2000):
+        qg._lib.qgemv_quantize_act(None, 1, Kgu, Kgu, *ptr_args, None)
+    ex["host_us_per_call_refused_before_launch"] = round(
+        (time.perf_counter() - t0) / 2000 * 1e6, 2)
     ex["quantize_act_4096"] = kernel_stats(
         torch, lambda c: qg.qgemv_quantize_act(x, 1, Kgu, Kgu, q, d, s), 200, 1)
     gu = torch.randn(Ngu, device=dev)
