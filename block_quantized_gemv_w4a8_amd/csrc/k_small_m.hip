@@ -769,11 +769,14 @@ static hipError_t launch_mfma(const void* w, int64_t N, int64_t K, int64_t M, co
             // against 14.1 us at M = 8 on 14336 x 4096 (same process); Q6_K
             // (12288 x 4096) runs 2.4 us slower that way
             // At most 8 activation rows (Q4_K): two-block tiles, two 32-blocks
-            // per i8 MFMA with no padding rows (13.8 against 14.1 us at M = 8
-            // and 9 on 14336 x 4096; 13.6 against 15.7 us on 4096 x 14336)
+            // per i8 MFMA with no padding rows, each wave taking whole units
+            // (4 waves per workgroup of 32 rows): at M = 8, 12.2 against 12.7
+            // us with the 32-blocks halved over 2 waves and 13.5 us with 16-row
+            // tiles on 14336 x 4096, 19.6 against 23.4 and 24.9 us on 28672 x
+            // 4096 (same process)
             if constexpr (FMT == QGEMV_FMT_Q4_K) {
                 if (M <= 8)
-                    return launch_mfma_cfg<FMT, 1, 2, 2, 2, 1, 2, 2, DOTS, true>(w, N, K, M, q, d, s, y, dots, st);
+                    return launch_mfma_cfg<FMT, 1, 2, 1, 2, 1, 2, 2, DOTS, true>(w, N, K, M, q, d, s, y, dots, st);
                 return launch_mfma_cfg<FMT, 1, 2, 2, 2, 1, 2, 2, DOTS>(w, N, K, M, q, d, s, y, dots, st);
             } else {
                 return launch_mfma_cfg<FMT, 1, 2, 2, 1, 1, 2, 2, DOTS>(w, N, K, M, q, d, s, y, dots, st);
@@ -910,12 +913,15 @@ static hipError_t launch_rows_gemv(int fmt, const void* w, int64_t N, int64_t K,
 // us at M = 8).  A shape and a bucket of M fix the kernel, so the summation
 // order of a row stays fixed.
 // Which products the register-resident kernel (k_small_m3.hip) takes under
-// MFMA and AUTO: Q4_K with at most 16 rows on matrices of at least six
-// 16-row tiles per compute unit, where it measured faster (28672 x 4096 at
-// M = 8: 22.2 against 24.8 us staged; 14336 x 4096: 15.0 against 13.5 us,
-// so narrower matrices stay with the staged kernel).
+// MFMA and AUTO: Q4_K with 9 to 16 rows on matrices of at least six 16-row
+// tiles per compute unit, where it measured faster than the 16-row tiles
+// (28672 x 4096 at M = 8: 22.2 against 24.8 us staged; 14336 x 4096: 15.0
+// against 13.5 us, so narrower matrices stay with the staged kernel).  Up to
+// 8 rows the staged kernel's two-block tiles beat both (19.6 us at M = 8 on
+// 28672 x 4096).
 static bool use_resident_kernel(int fmt, int64_t N, int64_t K, int64_t M) {
-    if (!small_m3_supported(fmt, K, M)) return false;
+    // (at most 8 rows the staged kernel's two-block tiles are faster there too)
+    if (M <= 8 || !small_m3_supported(fmt, K, M)) return false;
     int cus = 0, dev = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||

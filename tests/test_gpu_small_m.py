@@ -272,12 +272,13 @@ def test_small_m_dot4_rows_equal_gemv_bits(qg, fmt, M, N, K):
     check_y(Y.reshape(-1), Y_ref.reshape(-1), TT.reshape(-1), f"dot4 rows {fmt} M={M}")
 
 
-@pytest.mark.parametrize("M", [4, 16])
+@pytest.mark.parametrize("M", [4, 12, 16])
 def test_small_m_very_wide_q4k_resident_route(qg, M):
     """Q4_K matrices of at least six 16-row tiles per compute unit take the
-    register-resident kernel under MFMA and AUTO (N = 24600: 1538 tiles, the
+    register-resident kernel under MFMA and AUTO from 9 to 16 rows, and the
+    staged kernel's two-block tiles up to 8 rows (N = 24600: 1538 tiles, the
     last ragged); every output against the oracle, and the same bits as the
-    forced RESIDENT variant."""
+    forced RESIDENT or STAGED variant."""
     N, K = 24600, 1024
     g = np.random.default_rng(M + 99)
     w = WEIGHTS["q4_k"](g, N, K)
@@ -289,6 +290,9 @@ def test_small_m_very_wide_q4k_resident_route(qg, M):
     say("small_m very wide q4_k", M)
     Yr = small_m(qg, "q4_k", wd, N, K, act, M, qg.QGEMV_VARIANT_MFMA_RESIDENT)
     check_y(Yr.reshape(-1), Y_ref.reshape(-1), TT.reshape(-1), f"resident M={M}")
+    Ys = small_m(qg, "q4_k", wd, N, K, act, M, qg.QGEMV_VARIANT_MFMA_STAGED)
+    check_y(Ys.reshape(-1), Y_ref.reshape(-1), TT.reshape(-1), f"staged M={M}")
+    routed = Yr if M > 8 else Ys
     for v in (qg.QGEMV_VARIANT_MFMA, qg.QGEMV_VARIANT_AUTO):
         Y = small_m(qg, "q4_k", wd, N, K, act, M, v)
-        assert np.array_equal(Y.view(np.uint32), Yr.view(np.uint32)), v
+        assert np.array_equal(Y.view(np.uint32), routed.view(np.uint32)), v

@@ -20,10 +20,12 @@ WEIGHTS = {"q4_k": synth.q4_k_weights, "q6_k": synth.q6_k_weights, "q4_0": synth
 FMT = {"q4_k": 1, "q6_k": 2, "q4_0": 0}
 
 # wide matrices (at least 512 tiles of 16 rows) and narrow ones, M in each
-# bucket of 16; N = 24600 takes the register-resident kernel under MFMA (Q4_K)
+# bucket of 16 (and for Q4_K both halves of the first: two-block tiles up to
+# M = 8); N = 24600 takes the register-resident kernel under MFMA (Q4_K)
 CASES = [("q4_k", 8, 8200, 1024), ("q4_k", 20, 8200, 1024), ("q4_k", 40, 8200, 1024),
          ("q4_k", 64, 8200, 1024), ("q4_k", 8, 600, 4096), ("q4_k", 24, 300, 4096),
          ("q4_k", 48, 200, 2048), ("q4_k", 64, 130, 4096), ("q4_k", 5, 24600, 1024),
+         ("q4_k", 1, 8200, 1024), ("q4_k", 3, 600, 4096),
          ("q6_k", 8, 8200, 1024), ("q6_k", 24, 8200, 1024), ("q6_k", 40, 8200, 1024),
          ("q6_k", 8, 600, 4096), ("q6_k", 24, 300, 4096), ("q6_k", 48, 200, 2048),
          ("q6_k", 64, 130, 4096), ("q4_0", 8, 8200, 1056), ("q4_0", 40, 8200, 1056),
