@@ -765,22 +765,21 @@ static hipError_t launch_mfma(const void* w, int64_t N, int64_t K, int64_t M, co
     if (wide) {
         switch (mt) {
         case 1:
-            // Q4_K: the 2 units of a step on 2 waves each (8 waves): 13.2
-            // against 14.1 us at M = 8 on 14336 x 4096 (same process); Q6_K
-            // (12288 x 4096) runs 2.4 us slower that way
-            // At most 8 activation rows (Q4_K): two-block tiles, two 32-blocks
-            // per i8 MFMA with no padding rows, each wave taking whole units
-            // (4 waves per workgroup of 32 rows): at M = 8, 12.2 against 12.7
-            // us with the 32-blocks halved over 2 waves and 13.5 us with 16-row
-            // tiles on 14336 x 4096, 19.6 against 23.4 and 24.9 us on 28672 x
-            // 4096 (same process)
+            // Every format: each wave takes whole units, the 2 units of a step
+            // on 2 waves (4 waves per workgroup of 32 rows), measured faster
+            // than halving each unit's 32-blocks over 2 more waves (same
+            // process): Q4_K 14336 x 4096 at M = 16 14.1 against 14.9 us,
+            // Q6_K 12288 x 4096 at M = 8 23.2 against 24.5 us, Q4_0 14336 x
+            // 4096 at M = 8 18.2 against 18.9 us.  At most 8 activation rows
+            // (Q4_K): two-block tiles, two 32-blocks per i8 MFMA with no
+            // padding rows: 12.2 against 12.7 us (halved units) and 13.5 us
+            // (16-row tiles) on 14336 x 4096, 19.6 against 23.4 and 24.9 us on
+            // 28672 x 4096 at M = 8
             if constexpr (FMT == QGEMV_FMT_Q4_K) {
                 if (M <= 8)
                     return launch_mfma_cfg<FMT, 1, 2, 1, 2, 1, 2, 2, DOTS, true>(w, N, K, M, q, d, s, y, dots, st);
-                return launch_mfma_cfg<FMT, 1, 2, 2, 2, 1, 2, 2, DOTS>(w, N, K, M, q, d, s, y, dots, st);
-            } else {
-                return launch_mfma_cfg<FMT, 1, 2, 2, 1, 1, 2, 2, DOTS>(w, N, K, M, q, d, s, y, dots, st);
             }
+            return launch_mfma_cfg<FMT, 1, 2, 1, 2, 1, 2, 2, DOTS>(w, N, K, M, q, d, s, y, dots, st);
         case 2:
             // Q4_K: the units of a step on 2 waves each: 19.7 against 21.8 us
             // at M = 24 on 14336 x 4096 (same process); Q6_K runs slower so
