@@ -782,32 +782,34 @@ static hipError_t launch_mfma(const void* w, int64_t N, int64_t K, int64_t M, co
             return launch_mfma_cfg<FMT, 1, 2, 1, 2, 1, 2, 2, DOTS>(w, N, K, M, q, d, s, y, dots, st);
         case 2:
             // Q4_K: the units of a step on 2 waves each: 19.7 against 21.8 us
-            // at M = 24 on 14336 x 4096 (same process); Q6_K runs slower so
+            // at M = 24 on 14336 x 4096 (same process); Q6_K runs slower so.
+            // Q4_0: whole units per wave, the 2 units of a step on 2 waves:
+            // 24.6 against 25.2 us at M = 24 (same process)
             if constexpr (FMT == QGEMV_FMT_Q4_K)
                 return launch_mfma_cfg<FMT, 2, 4, 2, 2, 1, 2, 2, DOTS>(w, N, K, M, q, d, s, y, dots, st);
+            else if constexpr (FMT == QGEMV_FMT_Q4_0)
+                return launch_mfma_cfg<FMT, 2, 4, 1, 2, 1, 2, 2, DOTS>(w, N, K, M, q, d, s, y, dots, st);
             else
                 return launch_mfma_cfg<FMT, 2, 4, 2, 1, 1, 2, 2, DOTS>(w, N, K, M, q, d, s, y, dots, st);
         case 3:
-            // Q4_K: each wave takes whole units (all 8 32-blocks), the 2
-            // units of a step on 2 waves: 26.9 against 27.9 us at M = 40 on
-            // 14336 x 4096 (same process)
+            // Q4_K and Q4_0: each wave takes whole units (all 8 32-blocks),
+            // the 2 units of a step on 2 waves: 26.9 against 27.9 us (Q4_K)
+            // and 32.2 against 32.9 us (Q4_0) at M = 40 on 14336 x 4096 (same
+            // process)
             if constexpr (FMT == QGEMV_FMT_Q6_K)
                 return launch_mfma_cfg<FMT, 3, RT34, 2, 2, 1, 2, 2, DOTS>(w, N, K, M, q, d, s, y, dots, st);
-            else if constexpr (FMT == QGEMV_FMT_Q4_K)
-                return launch_mfma_cfg<FMT, 3, RT34, 1, 2, 1, 2, 2, DOTS>(w, N, K, M, q, d, s, y, dots, st);
             else
-                return launch_mfma_cfg<FMT, 3, RT34, 2, 1, 1, 2, 2, DOTS>(w, N, K, M, q, d, s, y, dots, st);
+                return launch_mfma_cfg<FMT, 3, RT34, 1, 2, 1, 2, 2, DOTS>(w, N, K, M, q, d, s, y, dots, st);
         default:
             // Q6_K: the units of a step on 2 waves each: 71 against 119 us at
             // M = 64 on 12288 x 4096 (same process); Q4_K runs slower so, but
             // with whole units per wave (the 2 units of a step on 2 waves of 8
-            // 32-blocks each) 33.1 against 33.9 us at M = 64 on 14336 x 4096
+            // 32-blocks each) 33.1 against 33.9 us at M = 64 on 14336 x 4096,
+            // and Q4_0 39.1 against 39.9 us
             if constexpr (FMT == QGEMV_FMT_Q6_K)
                 return launch_mfma_cfg<FMT, 4, RT34, 2, 2, 1, 2, 2, DOTS>(w, N, K, M, q, d, s, y, dots, st);
-            else if constexpr (FMT == QGEMV_FMT_Q4_K)
-                return launch_mfma_cfg<FMT, 4, RT34, 1, 2, 1, 2, 2, DOTS>(w, N, K, M, q, d, s, y, dots, st);
             else
-                return launch_mfma_cfg<FMT, 4, RT34, 2, 1, 1, 2, 2, DOTS>(w, N, K, M, q, d, s, y, dots, st);
+                return launch_mfma_cfg<FMT, 4, RT34, 1, 2, 1, 2, 2, DOTS>(w, N, K, M, q, d, s, y, dots, st);
         }
     }
     switch (mt) {
