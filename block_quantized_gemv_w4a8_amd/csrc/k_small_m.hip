@@ -229,8 +229,8 @@ __global__ __launch_bounds__(64 * RT * KS * KP * MS) void k_small_m_mfma(const u
     static_assert(KS == 1 || KS == 2 || KS == 4, "32-blocks split over 1, 2 or 4 waves");
     static_assert(G % KP == 0 && (KP > 1 || G <= 2), "units of a step split evenly over KP");
     static_assert(MT % MS == 0, "activation tiles split evenly over MS");
-    static_assert(!TWO || (FMT == QGEMV_FMT_Q4_K && MT == 1 && KS <= 4),
-                  "two-block tiles: Q4_K, at most 8 activation rows, pairs of 32-blocks per wave");
+    static_assert(!TWO || (MT == 1 && KS <= 4),
+                  "two-block tiles: at most 8 activation rows, pairs of 32-blocks per wave");
     constexpr int TPW = MT / MS;                             // activation tiles per wave
     using GM = MfmaGeom<FMT, MT, RT, G>;
     using U = SmUnit<FMT>;
@@ -531,42 +531,93 @@ __global__ __launch_bounds__(64 * RT * KS * KP * MS) void k_small_m_mfma(const u
         // output is one exact block dot and no tile row is padding.  Lane
         // (nl, kp) holds rows 4*kp + i: block jp + (kp >= 2) of activation row
         // 4*(kp & 1) + i; the two halves of a row meet at the end.
-        auto mfma_pair = [&](int pi, i32x4& E) {
+        auto mfma_pair = [&](int pi, i32x4 (&E)[ND]) {
             const int jp = P * BPW + 2 * pi;              // even block of the pair
-            // weights: bytes 32*(jp/2) + 16*(kp&1) .. +15 of the unit's codes;
-            // low nibbles are block jp, high nibbles block jp + 1
-            const u32x4 v = *reinterpret_cast<const u32x4*>(smem + ow + 16 + 16 * jp + 16 * (kp & 1));
-            const int sh = kp < 2 ? 0 : 4;
-            const i32x4 B = {(int)((v.x >> sh) & LO4), (int)((v.y >> sh) & LO4),
-                             (int)((v.z >> sh) & LO4), (int)((v.w >> sh) & LO4)};
-            const int jb = jp + (kp >> 1);
+            const int jb = jp + (kp >> 1);                // this lane's block
+            // weights: 16 codes of block jb for K lanes 16*kp .. 16*kp + 15
+            // (elements 16*(kp & 1) .. of the block)
+            i32x4 B;
+            if constexpr (FMT == QGEMV_FMT_Q4_K) {
+                // bytes 32*(jp/2) + 16*(kp&1) .. +15 of the unit's codes: low
+                // nibbles are block jp, high nibbles block jp + 1
+                const u32x4 v = *reinterpret_cast<const u32x4*>(smem + ow + 16 + 16 * jp + 16 * (kp & 1));
+                const int sh = kp < 2 ? 0 : 4;
+                B = i32x4{(int)((v.x >> sh) & LO4), (int)((v.y >> sh) & LO4),
+                          (int)((v.z >> sh) & LO4), (int)((v.w >> sh) & LO4)};
+            } else if constexpr (FMT == QGEMV_FMT_Q4_0) {
+                // block jb's 16 bytes: elements 0-15 are the low nibbles,
+                // 16-31 the high nibbles
+                const u32x4 v = lds16_a2(smem, ow + 18 * jb + 2);
+                const int sh = 4 * (kp & 1);
+                B = i32x4{(int)((v.x >> sh) & LO4), (int)((v.y >> sh) & LO4),
+                          (int)((v.z >> sh) & LO4), (int)((v.w >> sh) & LO4)};
+            } else {
+                // block jb = 4h + t: element l = low (t < 2) or high nibble of
+                // ql[64h + 32(t&1) + l], plus bits 2t..2t+1 of qh[32h + l]
+                const int h = jb >> 2, tt = jb & 3;
+                const u32x4 ql = lds16_a2(smem, ow + 64 * h + 32 * (tt & 1) + 16 * (kp & 1));
+                const u32x4 qh = lds16_a2(smem, ow + 128 + 32 * h + 16 * (kp & 1));
+                const int s1 = 4 * (tt >> 1), s2 = 2 * tt;
+                B = i32x4{(int)(((ql.x >> s1) & LO4) | (((qh.x >> s2) & 0x03030303u) << 4)),
+                          (int)(((ql.y >> s1) & LO4) | (((qh.y >> s2) & 0x03030303u) << 4)),
+                          (int)(((ql.z >> s1) & LO4) | (((qh.z >> s2) & 0x03030303u) << 4)),
+                          (int)(((ql.w >> s1) & LO4) | (((qh.w >> s2) & 0x03030303u) << 4))};
+            }
             const u32x4 a = *reinterpret_cast<const u32x4*>(
                 smem + oa + (nl & 7) * GM::ASTRIDE + 32 * jb + 16 * (kp & 1));
             const bool mine = (nl < 8) == (kp < 2);
             const i32x4 A = {mine ? (int)a.x : 0, mine ? (int)a.y : 0, mine ? (int)a.z : 0,
                              mine ? (int)a.w : 0};
-            E = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, B, zero, 0, 0, 0);
+            if constexpr (ND == 1) {
+                E[0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, B, zero, 0, 0, 0);
+            } else {
+                // Q6_K: a lane's K values are one 16-group (2*jb + (kp & 1));
+                // the first MFMA keeps the first group of each block, the
+                // second the other
+                const bool g1 = (kp & 1) != 0;
+                const i32x4 B0 = g1 ? zero : B, B1 = g1 ? B : zero;
+                E[0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, B0, zero, 0, 0, 0);
+                E[1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, B1, zero, 0, 0, 0);
+            }
             if constexpr (DOTS) {
                 const int blk = blk0 + jb;
-                const bool okb = valid && n < N;
+                const bool okb = valid && n < N && (FMT != QGEMV_FMT_Q4_0 || blk < nbw);
+                const int ndb = FMT == QGEMV_FMT_Q6_K ? 2 * nb : (FMT == QGEMV_FMT_Q4_0 ? nbw : nb);
+#pragma unroll
+                for (int e = 0; e < ND; e++)
+#pragma unroll
+                    for (int i = 0; i < 4; i++) {
+                        const int m = 4 * (kp & 1) + i;
+                        const int col = FMT == QGEMV_FMT_Q6_K ? 2 * blk + e : blk;
+                        if (okb && m < M) dots[((int64_t)m * N + n) * ndb + col] = E[e][i];
+                    }
+            }
+        };
+        auto scale_pair = [&](int pi, const i32x4 (&E)[ND]) {
+            const int jp = P * BPW + 2 * pi;
+            const int jb = jp + (kp >> 1);
+            const f32x4 x4 = *reinterpret_cast<const f32x4*>(
+                smem + oa + GM::ACODES + 4 * (jb * MP + 4 * (kp & 1)));
+            if constexpr (ND == 1) {
+                float ws;
+                if constexpr (FMT == QGEMV_FMT_Q4_K)
+                    ws = fd * (float)(((jb >= 4 ? shi : slo) >> (8 * (jb & 3))) & 0xFFu);
+                else
+                    ws = q40_scale(jb);
+#pragma unroll
+                for (int i = 0; i < 4; i++) acc[ga][0][i] = fmaf((float)E[0][i], ws * x4[i], acc[ga][0][i]);
+            } else {
+                const uint32_t sc = lds2(smem, ow + 192 + 2 * jb);   // int8 scales of 2jb, 2jb+1
+                const float ws0 = fd * (float)sbyte(sc, 0), ws1 = fd * (float)sbyte(sc, 1);
 #pragma unroll
                 for (int i = 0; i < 4; i++) {
-                    const int m = 4 * (kp & 1) + i;
-                    if (okb && m < M) dots[((int64_t)m * N + n) * nb + blk] = E[i];
+                    const float v = fmaf((float)E[1][i], ws1, (float)E[0][i] * ws0);
+                    acc[ga][0][i] = fmaf(v, x4[i], acc[ga][0][i]);
                 }
             }
         };
-        auto scale_pair = [&](int pi, const i32x4& E) {
-            const int jp = P * BPW + 2 * pi;
-            const int jb = jp + (kp >> 1);
-            const float ws = fd * (float)(((jb >= 4 ? shi : slo) >> (8 * (jb & 3))) & 0xFFu);
-            const f32x4 x4 = *reinterpret_cast<const f32x4*>(
-                smem + oa + GM::ACODES + 4 * (jb * MP + 4 * (kp & 1)));
-#pragma unroll
-            for (int i = 0; i < 4; i++) acc[ga][0][i] = fmaf((float)E[i], ws * x4[i], acc[ga][0][i]);
-        };
         if constexpr (TWO) {
-            i32x4 E2[2];
+            i32x4 E2[2][ND];
             mfma_pair(0, E2[0]);
 #pragma unroll
             for (int pi = 1; pi < BPW / 2; pi++) {
@@ -599,7 +650,8 @@ __global__ __launch_bounds__(64 * RT * KS * KP * MS) void k_small_m_mfma(const u
 #pragma unroll
                 for (int t = 0; t < TPW; t++) {
                     const int m = 16 * (t0 + t) + nl;
-                    const float a = dx[(gi >> 1) * MP + m] * (float)s16[gi * MP + m];
+                    // (two-block tiles stage activation rows 0-7 only)
+                    const float a = TWO && nl >= 8 ? 0.0f : dx[(gi >> 1) * MP + m] * (float)s16[gi * MP + m];
                     acc2[ga][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc2[ga][t], 0, 0, 0);
                 }
             }
@@ -740,9 +792,8 @@ static hipError_t launch_mfma_cfg(const void* w, int64_t N, int64_t K, int64_t M
 constexpr int64_t kMfmaWideTiles = 512;
 
 // Row m of a product depends only on activation row m and on the bucket of
-// M (1-16, 17-32, 33-48, 49-64 rows; Q4_K splits the first into 1-8, two-block
-// tiles, and 9-16) and the shape, which fix the configuration and so the fp32
-// summation order.
+// M (1-8: two-block tiles; 9-16, 17-32, 33-48, 49-64 rows) and the shape,
+// which fix the configuration and so the fp32 summation order.
 template <int FMT, bool DOTS = false>
 static hipError_t launch_mfma(const void* w, int64_t N, int64_t K, int64_t M, const int8_t* q,
                               const uint16_t* d, const int32_t* s, float* y, hipStream_t st,
@@ -770,15 +821,13 @@ static hipError_t launch_mfma(const void* w, int64_t N, int64_t K, int64_t M, co
             // than halving each unit's 32-blocks over 2 more waves (same
             // process): Q4_K 14336 x 4096 at M = 16 14.1 against 14.9 us,
             // Q6_K 12288 x 4096 at M = 8 23.2 against 24.5 us, Q4_0 14336 x
-            // 4096 at M = 8 18.2 against 18.9 us.  At most 8 activation rows
-            // (Q4_K): two-block tiles, two 32-blocks per i8 MFMA with no
-            // padding rows: 12.2 against 12.7 us (halved units) and 13.5 us
-            // (16-row tiles) on 14336 x 4096, 19.6 against 23.4 and 24.9 us on
-            // 28672 x 4096 at M = 8
-            if constexpr (FMT == QGEMV_FMT_Q4_K) {
-                if (M <= 8)
-                    return launch_mfma_cfg<FMT, 1, 2, 1, 2, 1, 2, 2, DOTS, true>(w, N, K, M, q, d, s, y, dots, st);
-            }
+            // 4096 at M = 8 18.2 against 18.9 us.  At most 8 activation rows:
+            // two-block tiles, two 32-blocks per i8 MFMA with no padding rows
+            // (M = 8 against M = 9: Q4_K 12.3 against 13.9 us, Q6_K 12288 x
+            // 4096 22.1 against 23.1 us, Q4_0 15.8 against 18.2 us; Q4_K
+            // 28672 x 4096 19.6 against 24.9 us)
+            if (M <= 8)
+                return launch_mfma_cfg<FMT, 1, 2, 1, 2, 1, 2, 2, DOTS, true>(w, N, K, M, q, d, s, y, dots, st);
             return launch_mfma_cfg<FMT, 1, 2, 1, 2, 1, 2, 2, DOTS>(w, N, K, M, q, d, s, y, dots, st);
         case 2:
             // Q4_K: the units of a step on 2 waves each: 19.7 against 21.8 us
@@ -814,8 +863,11 @@ static hipError_t launch_mfma(const void* w, int64_t N, int64_t K, int64_t M, co
     }
     switch (mt) {
     case 1:
-        if (FMT == QGEMV_FMT_Q4_K && M <= 8)
-            return launch_mfma_cfg<FMT, 1, 1, 2, 4, 1, 4, 2, DOTS, FMT == QGEMV_FMT_Q4_K>(w, N, K, M, q, d, s, y, dots, st);
+        // at most 8 rows: two-block tiles (M = 8 against M = 9 on 4096 x
+        // 14336: Q4_K 13.4 against 15.7 us, Q6_K 22.8 against 25.1 us, Q4_0
+        // 17.1 against 20.5 us)
+        if (M <= 8)
+            return launch_mfma_cfg<FMT, 1, 1, 2, 4, 1, 4, 2, DOTS, true>(w, N, K, M, q, d, s, y, dots, st);
         return launch_mfma_cfg<FMT, 1, 1, 2, 4, 1, 4, 2, DOTS>(w, N, K, M, q, d, s, y, dots, st);
     case 2:
         // Q4_K and Q4_0: each unit's 32-blocks halved over 2 waves: 25.4
