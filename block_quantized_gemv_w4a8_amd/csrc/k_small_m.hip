@@ -923,12 +923,17 @@ static int dot4_tile_rows(int64_t K) {
     return mt >= 8 ? 8 : mt >= 4 ? 4 : mt >= 2 ? 2 : 1;
 }
 
-// AUTO: the MFMA variant from this many rows on (measured crossover on
-// MI355X: Q4_K 14336 x 4096 takes 12.6 us at M = 3 through the streaming
-// rows and 13.1 us on MFMA, 13.4 against 13.2 us at M = 4; Q6_K 4096 x 14336
-// 17.0 against 25.0 us and Q4_0 14336 x 4096 13.0 against 18.1 us at M = 4,
-// while two passes of four rows lose to MFMA at M = 8).
-static int mfma_from_m(int fmt) { return fmt == QGEMV_FMT_Q4_K ? 4 : 5; }
+// AUTO: the MFMA variant from this many rows on (measured crossovers on
+// MI355X, same process: wide Q4_K takes 12.9 us at M = 3 through the
+// streaming rows and 12.1 us on MFMA's two-block tiles on 14336 x 4096, 20.0
+// against 18.8 us on 28672 x 4096; narrow Q4_K 4096 x 14336 12.6 against
+// 13.4 us at M = 4; Q6_K 4096 x 14336 16.6 against 22.6 us and Q4_0 14336 x
+// 4096 12.9 against 15.6 us at M = 4, while two passes of four rows lose to
+// MFMA from M = 5 everywhere).
+static int mfma_from_m(int fmt, int64_t N) {
+    if (fmt == QGEMV_FMT_Q4_K && (N + 15) / 16 >= kMfmaWideTiles) return 3;
+    return 5;
+}
 
 static hipError_t launch_dot4_q4k(const void* w, int64_t N, int64_t K, int64_t M,
                                   const int8_t* q, const uint16_t* d, const int32_t* s, float* y,
@@ -994,7 +999,7 @@ static bool use_stream_kernel(int fmt, int64_t N, int64_t M) {
 hipError_t launch_small_m(int fmt, const void* w, int64_t N, int64_t K, int64_t M,
                           const int8_t* q, const uint16_t* d, const int32_t* s, float* y,
                           int variant, hipStream_t st) {
-    const bool auto_mfma = variant == QGEMV_VARIANT_AUTO && M >= mfma_from_m(fmt);
+    const bool auto_mfma = variant == QGEMV_VARIANT_AUTO && M >= mfma_from_m(fmt, N);
     if ((variant == QGEMV_VARIANT_MFMA_RESIDENT && small_m3_supported(fmt, K, M)) ||
         ((variant == QGEMV_VARIANT_MFMA || auto_mfma) && use_resident_kernel(fmt, N, K, M)))
         return launch_small_m3(fmt, w, N, K, M, q, d, s, y, st);

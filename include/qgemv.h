@@ -211,7 +211,8 @@ qgemv_status qgemv_q8_0(const void* w, int64_t N, int64_t K, const int8_t* q,
  * more rows stream the weights once per group of up to four activation
  * rows, each output row then having the bits of qgemv_q4_k on its row where
  * that GEMV streams its rows, K > 2048), QGEMV_VARIANT_MFMA (int8 matrix
- * cores), or QGEMV_VARIANT_AUTO (DOT4 up to M = 3, MFMA from M = 4). */
+ * cores), or QGEMV_VARIANT_AUTO (MFMA from M = 3 where N >= 8192, i.e. at
+ * least 512 tiles of 16 rows, and from M = 5 below that; DOT4 under it). */
 qgemv_status qgemm_q4_k_small_m(const void* w, int64_t N, int64_t K, int64_t M,
                                 const int8_t* q, const uint16_t* d, const int32_t* s,
                                 float* y, int variant, qgemv_stream_t stream);
