@@ -1040,8 +1040,14 @@ __global__ __launch_bounds__(DWG) void k_gemv_dyn(const uint8_t* __restrict__ w,
             if (XQ) xq_prologue<DWG>(ss, ai, nbw, Kp, xv, aq, ad, as);
         }
         int tn = grab2_issue();   // the pair after j1, in flight
-        // a wave's indices increase, so once one is past the pool all later are
-        while (j0 < pool_n) {
+        // A wave's indices increase (j0 < j1 at the loop head), so once one is
+        // past the pool all later are.  The loop runs while both pairs in
+        // flight are rows of the pool and has no other exit: with an exit
+        // between its halves the two ways out met the back edge in one block,
+        // with the register sets in opposite load order, and the compiler's
+        // wait counts drained every load at the loop head (one pair in flight
+        // instead of two).  The last pair, if any, is finished after it.
+        while (j1 < pool_n) {
             commit(A0, dA0, buf0);
             commit(B0, dB0, buf1);
             const int c0 = j0, e0 = dA0, f0 = dB0;
@@ -1056,7 +1062,6 @@ __global__ __launch_bounds__(DWG) void k_gemv_dyn(const uint8_t* __restrict__ w,
                 finish_row(s0, c0);
                 finish_row(s1, c0 + 1);
             }
-            if (j1 >= pool_n) break;
             commit(A1, dA1, buf0);
             commit(B1, dB1, buf1);
             const int c1 = j1, e1 = dA1, f1 = dB1;
@@ -1071,6 +1076,14 @@ __global__ __launch_bounds__(DWG) void k_gemv_dyn(const uint8_t* __restrict__ w,
                 finish_row(s0, c1);
                 finish_row(s1, c1 + 1);
             }
+        }
+        if (j0 < pool_n) {
+            commit(A0, dA0, buf0);
+            commit(B0, dB0, buf1);
+            float s0, s1;
+            ss.dot2(buf0, dA0, buf1, dB0, s0, s1);
+            finish_row(s0, j0);
+            finish_row(s1, j0 + 1);
         }
     } else {
         u32x4 Ra[NL], Rb[NL];
