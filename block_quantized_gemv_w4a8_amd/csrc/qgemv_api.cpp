@@ -265,7 +265,8 @@ const char* qgemv_build_info(void) {
     return "libqgemv abi=1 arch=gfx950 formats=q4_0,q4_k,q6_k,q8_0,q6_k_r8(repacked) act=int8/32+fp16+int32sum "
            "gemv=v_dot4_i32_i8,lds-row-stream,lds-dynamic-rows(+row-pairs),direct-loads,lanes-per-row{4,8,16,32,64} "
            "small_m=q4_k{dot4,mfma_i8_16x16x32(staged,wave-stream,register-resident)},"
-           "q6_k/q4_0{dot4_multirow(2|4),mfma_i8_16x16x32(staged,wave-stream)} "
+           "q6_k/q4_0{dot4_multirow(2|4),mfma_i8_16x16x32(staged,wave-stream)},"
+           "two-block_tiles_mfma_i8_16x16x64(M<=8) "
            "block_dots=lds-rows,staged-stream,small_m_mfma_tiles "
            "fused=q4_k_swiglu_quantize,quantize_gemv,quantize_q4_k_swiglu multi=multi,quantize_multi(<=8) "
            "stream_read=calibration K_max=32768 M_max=64";
