@@ -22,7 +22,10 @@
 // fp32 MFMA (v_mfma_f32_16x16x4f32) instead of the vector ALUs.  Weights and
 // activation are staged through LDS with coalesced 16-byte loads; the waves
 // of a workgroup split the 32-blocks, the units of K and the activation tiles
-// as the matrix shape and M call for.
+// as the matrix shape and M call for.  Up to 8 activation rows a tile would
+// be half padding; there one v_mfma_i32_16x16x64_i8 takes a pair of 32-blocks
+// instead (tile rows 0-7 against the first block, 8-15 against the second,
+// the other block's K lanes zeroed): the two-block tiles.
 #include <type_traits>
 
 #include "qgemv_device.h"
