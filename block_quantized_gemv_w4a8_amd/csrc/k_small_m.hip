@@ -819,26 +819,44 @@ static hipError_t launch_mfma(const void* w, int64_t N, int64_t K, int64_t M, co
     if (wide) {
         switch (mt) {
         case 1:
-            // Every format: each wave takes whole units, the 2 units of a step
-            // on 2 waves (4 waves per workgroup of 32 rows), measured faster
-            // than halving each unit's 32-blocks over 2 more waves (same
-            // process): Q4_K 14336 x 4096 at M = 16 14.1 against 14.9 us,
-            // Q6_K 12288 x 4096 at M = 8 23.2 against 24.5 us, Q4_0 14336 x
-            // 4096 at M = 8 18.2 against 18.9 us.  At most 8 activation rows:
-            // two-block tiles, two 32-blocks per i8 MFMA with no padding rows
-            // (M = 8 against M = 9: Q4_K 12.3 against 13.9 us, Q6_K 12288 x
-            // 4096 22.1 against 23.1 us, Q4_0 15.8 against 18.2 us; Q4_K
-            // 28672 x 4096 19.6 against 24.9 us)
-            if (M <= 8)
-                return launch_mfma_cfg<FMT, 1, 2, 1, 2, 1, 2, 2, DOTS, true>(w, N, K, M, q, d, s, y, dots, st);
+            // Every format: each wave takes whole units (measured faster than
+            // halving each unit's 32-blocks over 2 more waves, same process:
+            // Q4_K 14336 x 4096 at M = 16 14.1 against 14.9 us, Q6_K 12288 x
+            // 4096 at M = 8 23.2 against 24.5 us, Q4_0 14336 x 4096 at M = 8
+            // 18.2 against 18.9 us).  Q4_K: 4 units per step on 4 waves (8
+            // per workgroup of 32 rows), one step of loads in flight: 11.0
+            // against 12.9 us at M = 8 and 13.4 against 15.2 us at M = 16 on
+            // 14336 x 4096, 20.3 against 21.7 us at M = 8 on 28672 x 4096;
+            // Q6_K and Q4_0 lose so (Q6_K 12288 x 4096 M = 8 24.7 against
+            // 22.7 us, Q4_0 14336 x 4096 M = 8 17.6 against 16.2 us).  Q4_0
+            // at M <= 8: the 2 units of a step on 2 waves with one step in
+            // flight, 15.3 against 16.2 us (two in flight stay faster for
+            // Q6_K: 153.7 against 156.8 us on 128256 x 4096).  At most 8
+            // activation rows: two-block tiles, two 32-blocks per i8 MFMA with
+            // no padding rows (M = 8 against M = 9 with the same split: Q4_K
+            // 12.3 against 13.9 us, Q6_K 12288 x 4096 22.1 against 23.1 us,
+            // Q4_0 15.8 against 18.2 us; Q4_K 28672 x 4096 19.6 against
+            // 24.9 us)
+            if constexpr (FMT == QGEMV_FMT_Q4_K) {
+                if (M <= 8)
+                    return launch_mfma_cfg<FMT, 1, 2, 1, 4, 1, 4, 1, DOTS, true>(w, N, K, M, q, d, s, y, dots, st);
+                return launch_mfma_cfg<FMT, 1, 2, 1, 4, 1, 4, 1, DOTS>(w, N, K, M, q, d, s, y, dots, st);
+            } else if constexpr (FMT == QGEMV_FMT_Q4_0) {
+                if (M <= 8)
+                    return launch_mfma_cfg<FMT, 1, 2, 1, 2, 1, 2, 1, DOTS, true>(w, N, K, M, q, d, s, y, dots, st);
+            } else {
+                if (M <= 8)
+                    return launch_mfma_cfg<FMT, 1, 2, 1, 2, 1, 2, 2, DOTS, true>(w, N, K, M, q, d, s, y, dots, st);
+            }
             return launch_mfma_cfg<FMT, 1, 2, 1, 2, 1, 2, 2, DOTS>(w, N, K, M, q, d, s, y, dots, st);
         case 2:
             // Q4_K: the units of a step on 2 waves each: 19.7 against 21.8 us
-            // at M = 24 on 14336 x 4096 (same process); Q6_K runs slower so.
+            // at M = 24 on 14336 x 4096 (same process), and with one step of
+            // loads in flight 17.6 against 19.0 us; Q6_K runs slower so.
             // Q4_0: whole units per wave, the 2 units of a step on 2 waves:
             // 24.6 against 25.2 us at M = 24 (same process)
             if constexpr (FMT == QGEMV_FMT_Q4_K)
-                return launch_mfma_cfg<FMT, 2, 4, 2, 2, 1, 2, 2, DOTS>(w, N, K, M, q, d, s, y, dots, st);
+                return launch_mfma_cfg<FMT, 2, 4, 2, 2, 1, 2, 1, DOTS>(w, N, K, M, q, d, s, y, dots, st);
             else if constexpr (FMT == QGEMV_FMT_Q4_0)
                 return launch_mfma_cfg<FMT, 2, 4, 1, 2, 1, 2, 2, DOTS>(w, N, K, M, q, d, s, y, dots, st);
             else
@@ -868,10 +886,18 @@ static hipError_t launch_mfma(const void* w, int64_t N, int64_t K, int64_t M, co
     case 1:
         // at most 8 rows: two-block tiles (M = 8 against M = 9 on 4096 x
         // 14336: Q4_K 13.4 against 15.7 us, Q6_K 22.8 against 25.1 us, Q4_0
-        // 17.1 against 20.5 us)
+        // 17.1 against 20.5 us), and 8 units per step over 8 waves (each
+        // unit's 32-blocks halved over 2 of 16 waves) with one step of loads
+        // in flight against 4 units and two steps: Q4_0 14.6 against 17.3
+        // us, Q6_K 20.9 against 22.7 us, Q4_K 13.6 against 13.8 us.  At 9-16
+        // rows the same for Q4_0 (19.1 against 21.1 us) and Q6_K (22.8
+        // against 26.4 us); Q4_K stays on 4 units (17.0 against 18.4 us).
         if (M <= 8)
-            return launch_mfma_cfg<FMT, 1, 1, 2, 4, 1, 4, 2, DOTS, true>(w, N, K, M, q, d, s, y, dots, st);
-        return launch_mfma_cfg<FMT, 1, 1, 2, 4, 1, 4, 2, DOTS>(w, N, K, M, q, d, s, y, dots, st);
+            return launch_mfma_cfg<FMT, 1, 1, 2, 8, 1, 8, 1, DOTS, true>(w, N, K, M, q, d, s, y, dots, st);
+        if constexpr (FMT != QGEMV_FMT_Q4_K)
+            return launch_mfma_cfg<FMT, 1, 1, 2, 8, 1, 8, 1, DOTS>(w, N, K, M, q, d, s, y, dots, st);
+        else
+            return launch_mfma_cfg<FMT, 1, 1, 2, 4, 1, 4, 2, DOTS>(w, N, K, M, q, d, s, y, dots, st);
     case 2:
         // Q4_K and Q4_0: each unit's 32-blocks halved over 2 waves: 25.4
         // against 29.1 us (Q4_K) and 33.8 against 37.7 us (Q4_0) at M = 24 on

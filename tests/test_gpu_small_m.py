@@ -61,9 +61,10 @@ def test_small_m_shapes(qg, fmt, M, N, K):
 # Wide matrices (at least 512 row tiles of 16: N = 8200 gives 513, the last
 # ragged) take the configurations that share each staged activation over 64
 # or 32 weight rows, one per bucket of M; every output against the oracle.
-WIDE = [("q4_k", 8, 1024), ("q4_k", 20, 1024), ("q4_k", 40, 1024), ("q4_k", 64, 1024),
+WIDE = [("q4_k", 8, 1024), ("q4_k", 12, 2304), ("q4_k", 16, 1024), ("q4_k", 20, 1024),
+        ("q4_k", 40, 1024), ("q4_k", 64, 1024),
         ("q6_k", 8, 1024), ("q6_k", 24, 1024), ("q6_k", 33, 1024), ("q6_k", 64, 1024),
-        ("q4_0", 8, 1056), ("q4_0", 17, 1056), ("q4_0", 40, 1056), ("q4_0", 64, 1056)]
+        ("q4_0", 5, 2336), ("q4_0", 8, 1056), ("q4_0", 17, 1056), ("q4_0", 40, 1056), ("q4_0", 64, 1056)]
 
 
 @pytest.mark.parametrize("fmt,M,K", WIDE)
