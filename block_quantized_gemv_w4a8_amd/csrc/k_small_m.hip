@@ -710,14 +710,17 @@ __global__ __launch_bounds__(64 * RT * KS * KP * MS) void k_small_m_mfma(const u
     // Software pipeline over steps, R deep: step st issues the global loads
     // of step st+R into register set st mod R, computes st from LDS buffer
     // st&1, and stores step st+1 (loaded R-1 steps earlier) into the other
-    // buffer.  It starts at st = -R with nothing loaded, and every step
-    // issues the same loads, so the compiler's wait counts stay exact.
+    // buffer.  It starts at st = -R with nothing loaded.  With R > 1 every
+    // step issues the same loads (the last ones again at the end), so the
+    // compiler's wait counts stay exact; with R = 1 the store waits for all
+    // of the step's loads anyway, and the last step issues none (a load
+    // left in flight there would hold up the epilogue by a full latency).
     Regs rg[R];
     for (int base = -R; base < nsteps; base += R) {
 #pragma unroll
         for (int r = 0; r < R; r++) {
             const int st = base + r;
-            load_step(min(st + R, nsteps - 1), rg[r]);
+            if (R > 1 || st + R < nsteps) load_step(min(st + R, nsteps - 1), rg[r]);
             __builtin_amdgcn_sched_barrier(0);
             if (st >= 0 && st < nsteps) compute_step(st & 1, st);
             if (st + 1 >= 0 && st + 1 < nsteps) store_step(rg[(r + 1) % R], (st + 1) & 1, st + 1);
