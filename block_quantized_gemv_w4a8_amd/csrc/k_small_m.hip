@@ -902,18 +902,27 @@ static hipError_t launch_mfma(const void* w, int64_t N, int64_t K, int64_t M, co
         else
             return launch_mfma_cfg<FMT, 1, 1, 2, 4, 1, 4, 2, DOTS>(w, N, K, M, q, d, s, y, dots, st);
     case 2:
-        // Q4_K and Q4_0: each unit's 32-blocks halved over 2 waves: 25.4
-        // against 29.1 us (Q4_K) and 33.8 against 37.7 us (Q4_0) at M = 24 on
-        // 4096 x 14336 (same process); Q6_K no faster
-        if constexpr (FMT != QGEMV_FMT_Q6_K)
+        // Q4_K: each unit's 32-blocks halved over 2 waves: 25.4 against 29.1
+        // us at M = 24 on 4096 x 14336 (same process).  Q6_K and Q4_0: 4
+        // units per step, each halved over 2 waves, one step of loads in
+        // flight: on 4096 x 14336 at M = 24 Q6_K 37.8 against 44.7 us (4
+        // whole units per step, two in flight) and Q4_0 28.3 against 33.3 us
+        // (the Q4_K split); Q4_K loses so (27.5 against 24.7 us)
+        if constexpr (FMT == QGEMV_FMT_Q4_K)
             return launch_mfma_cfg<FMT, 2, 1, 2, 2, 2, 2, 2, DOTS>(w, N, K, M, q, d, s, y, dots, st);
         else
-            return launch_mfma_cfg<FMT, 2, 1, 1, 4, 2, 4, 2, DOTS>(w, N, K, M, q, d, s, y, dots, st);
+            return launch_mfma_cfg<FMT, 2, 1, 2, 4, 2, 4, 1, DOTS>(w, N, K, M, q, d, s, y, dots, st);
     case 3:
         // the same split for every format: at M = 48 on 4096 x 14336, Q6_K
         // 57 against 73 us, Q4_K 38 against 46 us, Q4_0 48 against 63 us
         return launch_mfma_cfg<FMT, 3, 1, 2, 2, 3, 2, 2, DOTS>(w, N, K, M, q, d, s, y, dots, st);
-    default: return launch_mfma_cfg<FMT, 4, 1, 1, 2, 4, 2, 2, DOTS>(w, N, K, M, q, d, s, y, dots, st);
+    default:
+        // Q4_K: each unit's 32-blocks halved over 2 waves, 51.0 against 53.1
+        // us at M = 64 on 4096 x 14336 (Q4_0 loses so, 80.4 against 69.6 us)
+        if constexpr (FMT == QGEMV_FMT_Q4_K)
+            return launch_mfma_cfg<FMT, 4, 1, 2, 2, 4, 2, 2, DOTS>(w, N, K, M, q, d, s, y, dots, st);
+        else
+            return launch_mfma_cfg<FMT, 4, 1, 1, 2, 4, 2, 2, DOTS>(w, N, K, M, q, d, s, y, dots, st);
     }
 }
 
