@@ -260,6 +260,20 @@ __global__ __launch_bounds__(64 * RT * KS * KP * MS) void k_small_m_mfma(const u
     const int t0 = ms * TPW;                                  // first activation tile
     const int nl = lane & 15, kp = lane >> 4;
     const int row0 = blockIdx.x * ROWS;
+    // activation rows: MP of them from m0 = MP * blockIdx.y (a second grid
+    // dimension splits M between workgroups where whole tiles of weight rows
+    // alone would leave compute units idle); the launch has M > m0
+    {
+        const int m0 = MP * blockIdx.y, nbk = Kp / 32;
+        q += (int64_t)m0 * Kp;
+        d += (int64_t)m0 * nbk;
+        s += (int64_t)m0 * nbk;
+        y += (int64_t)m0 * N;
+        if constexpr (DOTS)
+            dots += (int64_t)m0 * N *
+                    (FMT == QGEMV_FMT_Q6_K ? 2 * nbk : (FMT == QGEMV_FMT_Q4_0 ? K / 32 : nbk));
+        M = min(M - m0, MP);
+    }
     const int n = row0 + 16 * rt + nl;
     const int nunits = Kp / 256, nb = Kp / 32;
     const int nbw = K / 32;                                  // weight blocks of a Q4_0 row
@@ -788,7 +802,9 @@ static hipError_t launch_mfma_cfg(const void* w, int64_t N, int64_t K, int64_t M
                                   int32_t* dots, hipStream_t st) {
     const int Kp = (int)((K + 255) / 256 * 256);
     const int64_t grid = (N + 16 * RT - 1) / (16 * RT);
-    launch_kernel((k_small_m_mfma<FMT, MT, RT, KS, KP, MS, G, R, DOTS, TWO>), dim3((unsigned)grid),
+    const int64_t mgroups = (M + 16 * MT - 1) / (16 * MT);   // activation row groups
+    launch_kernel((k_small_m_mfma<FMT, MT, RT, KS, KP, MS, G, R, DOTS, TWO>),
+                  dim3((unsigned)grid, (unsigned)mgroups),
                   dim3(64 * RT * KS * KP * MS), 0, st, (const uint8_t*)w, (int)N, (int)K,
                   Kp, (int)M, q, d, s, y, dots);
     return hipGetLastError();
@@ -800,6 +816,22 @@ constexpr int64_t kMfmaWideTiles = 512;
 // Row m of a product depends only on activation row m and on the bucket of
 // M (1-8: two-block tiles; 9-16, 17-32, 33-48, 49-64 rows) and the shape,
 // which fix the configuration and so the fp32 summation order.
+// Wide Q4_K matrices at M = 33-64: 32 activation rows per workgroup (a
+// second grid dimension takes the rest) against 64 weight rows, whole units
+// per wave, one step of loads in flight -- 8 waves of ~118 VGPRs, so two
+// workgroups share a unit, where 64 activation rows per workgroup (~194
+// VGPRs) left two waves per SIMD.  Measured against the 64-by-64 workgroups
+// (same process): 27.1 against 33.2 us at M = 64 on 14336 x 4096, 51.3
+// against 64.5 us on 28672 x 4096, 217 against 251 us on 128256 x 4096; 26.1
+// against 27.9 us at M = 48 and 26.2 against 27.5 us at M = 40.
+template <bool DOTS>
+static hipError_t launch_q4k_wide_split(const void* w, int64_t N, int64_t K, int64_t M,
+                                        const int8_t* q, const uint16_t* d, const int32_t* s,
+                                        float* y, int32_t* dots, hipStream_t st) {
+    return launch_mfma_cfg<QGEMV_FMT_Q4_K, 2, 4, 1, 2, 1, 2, 1, DOTS>(w, N, K, M, q, d, s, y,
+                                                                       dots, st);
+}
+
 template <int FMT, bool DOTS = false>
 static hipError_t launch_mfma(const void* w, int64_t N, int64_t K, int64_t M, const int8_t* q,
                               const uint16_t* d, const int32_t* s, float* y, hipStream_t st,
@@ -865,24 +897,28 @@ static hipError_t launch_mfma(const void* w, int64_t N, int64_t K, int64_t M, co
             else
                 return launch_mfma_cfg<FMT, 2, 4, 2, 1, 1, 2, 2, DOTS>(w, N, K, M, q, d, s, y, dots, st);
         case 3:
-            // Q4_K and Q4_0: each wave takes whole units (all 8 32-blocks),
-            // the 2 units of a step on 2 waves: 26.9 against 27.9 us (Q4_K)
-            // and 32.2 against 32.9 us (Q4_0) at M = 40 on 14336 x 4096 (same
-            // process)
+            // Q4_0: each wave takes whole units (all 8 32-blocks), the 2
+            // units of a step on 2 waves: 32.2 against 32.9 us at M = 40 on
+            // 14336 x 4096 (same process)
             if constexpr (FMT == QGEMV_FMT_Q6_K)
                 return launch_mfma_cfg<FMT, 3, RT34, 2, 2, 1, 2, 2, DOTS>(w, N, K, M, q, d, s, y, dots, st);
-            else
+            else if constexpr (FMT == QGEMV_FMT_Q4_0)
                 return launch_mfma_cfg<FMT, 3, RT34, 1, 2, 1, 2, 2, DOTS>(w, N, K, M, q, d, s, y, dots, st);
+            else
+                return launch_q4k_wide_split<DOTS>(w, N, K, M, q, d, s, y, dots, st);
         default:
             // Q6_K: the units of a step on 2 waves each: 71 against 119 us at
-            // M = 64 on 12288 x 4096 (same process); Q4_K runs slower so, but
-            // with whole units per wave (the 2 units of a step on 2 waves of 8
-            // 32-blocks each) 33.1 against 33.9 us at M = 64 on 14336 x 4096,
-            // and Q4_0 39.1 against 39.9 us
+            // M = 64 on 12288 x 4096 (same process).  Q4_0: 32 activation
+            // rows per workgroup (a second grid dimension takes the rest),
+            // 128 weight rows, whole units per wave and one step of loads in
+            // flight: 35.2 against 38.8 us at M = 64 on 14336 x 4096 with 64
+            // rows by 64
             if constexpr (FMT == QGEMV_FMT_Q6_K)
                 return launch_mfma_cfg<FMT, 4, RT34, 2, 2, 1, 2, 2, DOTS>(w, N, K, M, q, d, s, y, dots, st);
+            else if constexpr (FMT == QGEMV_FMT_Q4_0)
+                return launch_mfma_cfg<FMT, 2, 8, 1, 2, 1, 2, 1, DOTS>(w, N, K, M, q, d, s, y, dots, st);
             else
-                return launch_mfma_cfg<FMT, 4, RT34, 1, 2, 1, 2, 2, DOTS>(w, N, K, M, q, d, s, y, dots, st);
+                return launch_q4k_wide_split<DOTS>(w, N, K, M, q, d, s, y, dots, st);
         }
     }
     switch (mt) {
@@ -917,10 +953,15 @@ static hipError_t launch_mfma(const void* w, int64_t N, int64_t K, int64_t M, co
         // 57 against 73 us, Q4_K 38 against 46 us, Q4_0 48 against 63 us
         return launch_mfma_cfg<FMT, 3, 1, 2, 2, 3, 2, 2, DOTS>(w, N, K, M, q, d, s, y, dots, st);
     default:
-        // Q4_K: each unit's 32-blocks halved over 2 waves, 51.0 against 53.1
-        // us at M = 64 on 4096 x 14336 (Q4_0 loses so, 80.4 against 69.6 us)
+        // Q4_K and Q4_0: 32 activation rows per workgroup (a second grid
+        // dimension takes the rest) with the M = 17-32 splits, at M = 64 on
+        // 4096 x 14336 Q4_K 46.2 against 50.8 us and Q4_0 56.3 against 69.9
+        // us (64 rows per workgroup, each wave one tile of 16); Q6_K keeps
+        // that (and under AUTO takes the wave-stream kernel)
         if constexpr (FMT == QGEMV_FMT_Q4_K)
-            return launch_mfma_cfg<FMT, 4, 1, 2, 2, 4, 2, 2, DOTS>(w, N, K, M, q, d, s, y, dots, st);
+            return launch_mfma_cfg<FMT, 2, 1, 2, 2, 2, 2, 2, DOTS>(w, N, K, M, q, d, s, y, dots, st);
+        else if constexpr (FMT == QGEMV_FMT_Q4_0)
+            return launch_mfma_cfg<FMT, 2, 1, 2, 4, 2, 4, 1, DOTS>(w, N, K, M, q, d, s, y, dots, st);
         else
             return launch_mfma_cfg<FMT, 4, 1, 1, 2, 4, 2, 2, DOTS>(w, N, K, M, q, d, s, y, dots, st);
     }

@@ -35,7 +35,7 @@ def variants(qg):
 
 SHAPES = [(1, 100, 256), (2, 65, 896), (3, 257, 4096), (5, 64, 4864), (8, 300, 4096),
           (9, 129, 1024), (16, 64, 4096), (17, 33, 768), (33, 70, 512), (48, 130, 2048),
-          (64, 96, 4096), (64, 1000, 1024), (7, 20, 32768)]
+          (64, 96, 4096), (64, 1000, 1024), (50, 300, 2048), (7, 20, 32768)]
 # Q4_0 rows need not hold whole 256-weight units: K = 32, 96, 1056, 4128
 Q40_EXTRA = [(3, 40, 32), (17, 50, 96), (8, 90, 1056), (64, 70, 4128)]
 
@@ -62,9 +62,10 @@ def test_small_m_shapes(qg, fmt, M, N, K):
 # ragged) take the configurations that share each staged activation over 64
 # or 32 weight rows, one per bucket of M; every output against the oracle.
 WIDE = [("q4_k", 8, 1024), ("q4_k", 12, 2304), ("q4_k", 16, 1024), ("q4_k", 20, 1024),
-        ("q4_k", 40, 1024), ("q4_k", 64, 1024),
+        ("q4_k", 40, 1024), ("q4_k", 57, 1280), ("q4_k", 64, 1024),
         ("q6_k", 8, 1024), ("q6_k", 24, 1024), ("q6_k", 33, 1024), ("q6_k", 64, 1024),
-        ("q4_0", 5, 2336), ("q4_0", 8, 1056), ("q4_0", 17, 1056), ("q4_0", 40, 1056), ("q4_0", 64, 1056)]
+        ("q4_0", 5, 2336), ("q4_0", 8, 1056), ("q4_0", 17, 1056), ("q4_0", 40, 1056), ("q4_0", 50, 1056),
+        ("q4_0", 64, 1056)]
 
 
 @pytest.mark.parametrize("fmt,M,K", WIDE)

@@ -21,7 +21,9 @@ FMT = {"q4_k": 1, "q6_k": 2, "q4_0": 0}
 
 # wide matrices (at least 512 tiles of 16 rows) and narrow ones, M in each
 # bucket of 16 (and for Q4_K both halves of the first: two-block tiles up to
-# M = 8); N = 24600 takes the register-resident kernel under MFMA (Q4_K)
+# M = 8; above 32 some take 32 activation rows per workgroup, the rest on a
+# second grid dimension); N = 24600 takes the register-resident kernel under
+# MFMA (Q4_K)
 CASES = [("q4_k", 8, 8200, 1024), ("q4_k", 20, 8200, 1024), ("q4_k", 40, 8200, 1024),
          ("q4_k", 64, 8200, 1024), ("q4_k", 8, 600, 4096), ("q4_k", 24, 300, 4096),
          ("q4_k", 48, 200, 2048), ("q4_k", 64, 130, 4096), ("q4_k", 5, 24600, 1024),
@@ -29,7 +31,8 @@ CASES = [("q4_k", 8, 8200, 1024), ("q4_k", 20, 8200, 1024), ("q4_k", 40, 8200, 1
          ("q6_k", 8, 8200, 1024), ("q6_k", 24, 8200, 1024), ("q6_k", 40, 8200, 1024),
          ("q6_k", 8, 600, 4096), ("q6_k", 24, 300, 4096), ("q6_k", 48, 200, 2048),
          ("q6_k", 64, 130, 4096), ("q4_0", 8, 8200, 1056), ("q4_0", 40, 8200, 1056),
-         ("q4_0", 8, 600, 4128), ("q4_0", 24, 300, 4096), ("q4_0", 64, 130, 4096)]
+         ("q4_0", 8, 600, 4128), ("q4_0", 24, 300, 4096), ("q4_0", 64, 130, 4096),
+         ("q4_k", 50, 8200, 1024), ("q4_0", 64, 8200, 1056), ("q4_0", 50, 200, 2048)]
 
 
 def _expected(fmt, w, N, K, q, s, M):
