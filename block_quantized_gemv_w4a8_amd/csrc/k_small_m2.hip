@@ -9,7 +9,7 @@
 // the scales ("Backends and hardware", section "CUDA": the prefill kernel's
 // gap is staging the next weight tile behind the current multiply).
 //
-// Work split.  A workgroup of 8 waves owns NTW tiles of 16 weight rows.  The
+// Work split.  A workgroup of NW waves owns NTW tiles of 16 weight rows.  The
 // waves of a tile split its 256-weight units (KSB ways, interleaved) and the
 // four pairs of 32-blocks of every unit (KS ways).  Each wave streams its own
 // weight bytes straight from HBM into registers, in the operand layout of
@@ -54,8 +54,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) void glb_void;
 
-constexpr int NTH = 512;   // 8 waves
-constexpr int NWAVE = NTH / 64;
 
 // One 16-byte chunk per lane from global memory straight into LDS: lane i's
 // chunk lands at dst + 16 * i (dst is the same for the whole wave).
@@ -199,7 +197,6 @@ struct Chunk {
     static constexpr int CSTR = 16 * CSLOT;                   // bytes per code row
     static constexpr int NCODE = MP * CSLOT;                  // code slots written per chunk
     static constexpr int NSC = MP * KC;                       // scale groups (row, 8 blocks)
-    static_assert(NSC <= NTH, "one scale group per thread");
     static constexpr int O_CODE = 0;
     static constexpr int O_DX = 16 * MPC * CSLOT;             // fp32 dx [KC*8][MP]
     static constexpr int O_DXS = O_DX + 4 * KC * 8 * MP;      // fp32 dx*s [KC*8][MP]
@@ -209,14 +206,15 @@ struct Chunk {
 // FMT: weight format; MT: activation tiles of 16 rows; TWO: the two-block
 // tiles (MT = 1, M <= 8); NTW: weight tiles per workgroup; KSB, KS: waves per
 // tile over units and over block pairs; KC: units per activation chunk; D:
-// units of weights in flight per wave.
-template <int FMT, int MT, bool TWO, int NTW, int KSB, int KS, int KC, int D>
-__global__ __launch_bounds__(NTH) void k_small_m2(const uint8_t* __restrict__ w, int N, int K,
+// units of weights in flight per wave; NW: waves per workgroup.
+template <int FMT, int MT, bool TWO, int NTW, int KSB, int KS, int KC, int D, int NW>
+__global__ __launch_bounds__(64 * NW) void k_small_m2(const uint8_t* __restrict__ w, int N, int K,
                                                   int M, const int8_t* __restrict__ q,
                                                   const uint16_t* __restrict__ dact,
                                                   const int32_t* __restrict__ sact,
                                                   float* __restrict__ y) {
-    static_assert(NTW * KSB * KS == NWAVE, "8 waves");
+    constexpr int NTH = 64 * NW;
+    static_assert(NTW * KSB * KS == NW, "every wave has a tile, units and block pairs");
     static_assert(!TWO || MT == 1, "two-block tiles have one activation tile");
     static_assert(KC % KSB == 0, "every wave has units in every chunk");
     static_assert(KS == 1 || KS == 2 || KS == 4, "block pairs split evenly");
@@ -224,6 +222,7 @@ __global__ __launch_bounds__(NTH) void k_small_m2(const uint8_t* __restrict__ w,
     constexpr bool MIN = F::MIN;
     constexpr int MP = TWO ? 8 : 16 * MT;     // activation rows staged
     using C = Chunk<FMT, MP, TWO ? 16 : MP, KC>;
+    static_assert(C::NSC <= NTH, "one scale group per thread");
     constexpr int BPW = 4 / KS;               // block pairs per wave and unit
     constexpr int SPC = KC / KSB;             // units per wave and chunk
     constexpr int NPART = KSB * KS;
@@ -638,12 +637,12 @@ __global__ __launch_bounds__(NTH) void k_small_m2(const uint8_t* __restrict__ w,
     }
 }
 
-template <int FMT, int MT, bool TWO, int NTW, int KSB, int KS, int KC, int D>
+template <int FMT, int MT, bool TWO, int NTW, int KSB, int KS, int KC, int D, int NW = 8>
 static hipError_t launch_cfg(const void* w, int64_t N, int64_t K, int64_t M, const int8_t* q,
                              const uint16_t* d, const int32_t* s, float* y, hipStream_t st) {
     const int64_t grid = (N + 16 * NTW - 1) / (16 * NTW);
-    launch_kernel((k_small_m2<FMT, MT, TWO, NTW, KSB, KS, KC, D>), dim3((unsigned)grid),
-                  dim3(NTH), 0, st, (const uint8_t*)w, (int)N, (int)K, (int)M, q, d, s, y);
+    launch_kernel((k_small_m2<FMT, MT, TWO, NTW, KSB, KS, KC, D, NW>), dim3((unsigned)grid),
+                  dim3(64 * NW), 0, st, (const uint8_t*)w, (int)N, (int)K, (int)M, q, d, s, y);
     return hipGetLastError();
 }
 
@@ -667,6 +666,17 @@ static hipError_t launch_fmt(const void* w, int64_t N, int64_t K, int64_t M, con
         }
     }
     if (M <= 8) return launch_cfg<FMT, 1, true, 1, 2, 4, 8, 4>(w, N, K, M, q, d, s, y, st);
+    // Q6_K at M = 33-64: 16 waves per tile (units 4 ways, block pairs 4
+    // ways), one unit in flight per wave: with one workgroup per 16 rows a
+    // narrow matrix has a workgroup per unit, and 8 waves left two per SIMD.
+    // On 4096 x 14336: M = 64 54.1 against 63.5 us, M = 48 42.9 against
+    // 59.5 us, M = 40 42.7 against 57.6 us (same process; at M <= 32 the
+    // staged kernel stays faster, and the other formats' activation chunks
+    // do not fit twice in LDS at this width)
+    if constexpr (FMT == QGEMV_FMT_Q6_K) {
+        if (mt == 3) return launch_cfg<FMT, 3, false, 1, 4, 4, 4, 1, 16>(w, N, K, M, q, d, s, y, st);
+        if (mt >= 4) return launch_cfg<FMT, 4, false, 1, 4, 4, 4, 1, 16>(w, N, K, M, q, d, s, y, st);
+    }
     switch (mt) {
     case 1: return launch_cfg<FMT, 1, false, 1, 2, 4, 8, 4>(w, N, K, M, q, d, s, y, st);
     case 2: return launch_cfg<FMT, 2, false, 1, 2, 4, 4, 4>(w, N, K, M, q, d, s, y, st);
