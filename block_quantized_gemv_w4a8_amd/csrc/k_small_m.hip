@@ -1046,9 +1046,10 @@ static hipError_t launch_rows_gemv(int fmt, const void* w, int64_t N, int64_t K,
 
 // Which int8-MFMA kernel takes a product: the wave-stream kernel
 // (k_small_m2.hip) where it measured faster than the staged one -- Q6_K from
-// M = 33 (4096 x 14336: 54.1 against 82.8 us at M = 64 and 42.9 against 57.0
-// us at M = 48; 12288 x 4096: 49.3 against 72.4 us at M = 64, 44.6 against
-// 57.1 us at M = 48) -- the staged kernel elsewhere (Q4_K 14336 x 4096: 13.6 against
+// M = 17 (4096 x 14336: 48.3 against 82.8 us at M = 64, 42.7 against 57.0 us
+// at M = 48, 37.3 against 37.6 us at M = 17; 12288 x 4096: 49.3 against 72.4
+// us at M = 64, 36.2 against 57.1 us at M = 48, 31.9 against 34.5 us at M =
+// 17) -- the staged kernel elsewhere (Q4_K 14336 x 4096: 13.6 against
 // 17.9 us at M = 8, 33.8 against 36.0 us at M = 64; Q4_0: 19.1 against 51.6
 // us at M = 8).  A shape and a bucket of M fix the kernel, so the summation
 // order of a row stays fixed.
@@ -1074,7 +1075,7 @@ static bool use_resident_kernel(int fmt, int64_t N, int64_t K, int64_t M) {
 
 static bool use_stream_kernel(int fmt, int64_t N, int64_t M) {
     (void)N;
-    return fmt == QGEMV_FMT_Q6_K && M >= 33;
+    return fmt == QGEMV_FMT_Q6_K && M >= 17;
 }
 
 hipError_t launch_small_m(int fmt, const void* w, int64_t N, int64_t K, int64_t M,

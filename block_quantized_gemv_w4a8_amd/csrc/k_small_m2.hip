@@ -658,6 +658,15 @@ static hipError_t launch_fmt(const void* w, int64_t N, int64_t K, int64_t M, con
     // <FMT, MT, TWO, NTW, KSB, KS, KC, D>
     if (wide) {
         if (M <= 8) return launch_cfg<FMT, 1, true, 4, 2, 1, 8, 4>(w, N, K, M, q, d, s, y, st);
+        // Q6_K at M = 17-48: 2 tiles per workgroup of 16 waves, each tile's
+        // units split 4 ways and block pairs 2 ways, one unit in flight per
+        // wave (12288 x 4096: M = 48 36.2 against 44.4 us, M = 24 32.2
+        // against 35.0 us for the staged kernel; 128256 x 4096 at M = 48 277
+        // against 341 us)
+        if constexpr (FMT == QGEMV_FMT_Q6_K) {
+            if (mt == 2) return launch_cfg<FMT, 2, false, 2, 4, 2, 4, 1, 16>(w, N, K, M, q, d, s, y, st);
+            if (mt == 3) return launch_cfg<FMT, 3, false, 2, 4, 2, 4, 1, 16>(w, N, K, M, q, d, s, y, st);
+        }
         switch (mt) {
         case 1: return launch_cfg<FMT, 1, false, 4, 2, 1, 8, 4>(w, N, K, M, q, d, s, y, st);
         case 2: return launch_cfg<FMT, 2, false, 4, 2, 1, 4, 4>(w, N, K, M, q, d, s, y, st);
@@ -666,16 +675,16 @@ static hipError_t launch_fmt(const void* w, int64_t N, int64_t K, int64_t M, con
         }
     }
     if (M <= 8) return launch_cfg<FMT, 1, true, 1, 2, 4, 8, 4>(w, N, K, M, q, d, s, y, st);
-    // Q6_K at M = 33-64: 16 waves per tile (units 4 ways, block pairs 4
-    // ways), one unit in flight per wave: with one workgroup per 16 rows a
-    // narrow matrix has a workgroup per unit, and 8 waves left two per SIMD.
-    // On 4096 x 14336: M = 64 54.1 against 63.5 us, M = 48 42.9 against
-    // 59.5 us, M = 40 42.7 against 57.6 us (same process; at M <= 32 the
-    // staged kernel stays faster, and the other formats' activation chunks
-    // do not fit twice in LDS at this width)
+    // Q6_K at M = 17-64: a tile's units split 4 ways and its block pairs 2
+    // ways, 4 units per activation chunk, one unit in flight per wave.  On
+    // 4096 x 14336 (same process): M = 64 48.3 against 63.5 us (units 2
+    // ways, block pairs 4 ways, two units in flight) and against 54.2 us
+    // with 16 waves; M = 48 42.7 against 59.5 us; M = 24 37.3 against 38.3
+    // us for the staged kernel
     if constexpr (FMT == QGEMV_FMT_Q6_K) {
-        if (mt == 3) return launch_cfg<FMT, 3, false, 1, 4, 4, 4, 1, 16>(w, N, K, M, q, d, s, y, st);
-        if (mt >= 4) return launch_cfg<FMT, 4, false, 1, 4, 4, 4, 1, 16>(w, N, K, M, q, d, s, y, st);
+        if (mt == 2) return launch_cfg<FMT, 2, false, 1, 4, 2, 4, 1>(w, N, K, M, q, d, s, y, st);
+        if (mt == 3) return launch_cfg<FMT, 3, false, 1, 4, 2, 4, 1>(w, N, K, M, q, d, s, y, st);
+        if (mt >= 4) return launch_cfg<FMT, 4, false, 1, 4, 2, 4, 1>(w, N, K, M, q, d, s, y, st);
     }
     switch (mt) {
     case 1: return launch_cfg<FMT, 1, false, 1, 2, 4, 8, 4>(w, N, K, M, q, d, s, y, st);

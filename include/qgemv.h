@@ -238,7 +238,7 @@ qgemv_status qgemm_q4_k_small_m(const void* w, int64_t N, int64_t K, int64_t M,
  * SIMD bug from a block bug).  y [M][N] receives the product as from the
  * small-M entry.  fmt: QGEMV_FMT_Q4_K, _Q6_K or _Q4_0.  Other variants, and
  * shapes for which the variant selects the wave-stream kernel (Q6_K from
- * M = 33 under MFMA), return QGEMV_E_UNSUPPORTED.  Other arguments, limits and
+ * M = 17 under MFMA), return QGEMV_E_UNSUPPORTED.  Other arguments, limits and
  * errors as for qgemm_q4_k_small_m. */
 qgemv_status qgemm_small_m_block_dots(int fmt, const void* w, int64_t N, int64_t K,
                                      int64_t M, const int8_t* q, const uint16_t* d,

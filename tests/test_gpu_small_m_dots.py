@@ -70,9 +70,9 @@ def test_small_m_mfma_dots_equal_oracle(fmt, M, N, K):
         try:
             qg.qgemm_small_m_block_dots(FMT[fmt], wd, N, K, M, *act, y, v, dots)
         except qg.QgemvError as e:
-            # only the wave-stream kernel (Q6_K from M = 33 under MFMA) has
+            # only the wave-stream kernel (Q6_K from M = 17 under MFMA) has
             # no dots mode
-            assert e.status == qg.QGEMV_E_UNSUPPORTED and fmt == "q6_k" and M > 32, e
+            assert e.status == qg.QGEMV_E_UNSUPPORTED and fmt == "q6_k" and M > 16, e
             assert v == qg.QGEMV_VARIANT_MFMA
             continue
         got = host(dots)
