@@ -663,9 +663,13 @@ static hipError_t launch_fmt(const void* w, int64_t N, int64_t K, int64_t M, con
         // wave (12288 x 4096: M = 48 36.2 against 44.4 us, M = 24 32.2
         // against 35.0 us for the staged kernel; 128256 x 4096 at M = 48 277
         // against 341 us)
+        // and at M = 49-64 four tiles per 8-wave workgroup with one unit in
+        // flight per wave (46.2 against 48.9 us for two on 12288 x 4096, 355
+        // against 375 us on 128256 x 4096)
         if constexpr (FMT == QGEMV_FMT_Q6_K) {
             if (mt == 2) return launch_cfg<FMT, 2, false, 2, 4, 2, 4, 1, 16>(w, N, K, M, q, d, s, y, st);
             if (mt == 3) return launch_cfg<FMT, 3, false, 2, 4, 2, 4, 1, 16>(w, N, K, M, q, d, s, y, st);
+            if (mt >= 4) return launch_cfg<FMT, 4, false, 4, 2, 1, 2, 1>(w, N, K, M, q, d, s, y, st);
         }
         switch (mt) {
         case 1: return launch_cfg<FMT, 1, false, 4, 2, 1, 8, 4>(w, N, K, M, q, d, s, y, st);
