@@ -1327,8 +1327,16 @@ static hipError_t launch_lds_wk(const GemvArgs& a, int U, const SliceGeom& g, hi
     return launch_lds_cfg<FMT, UPL, WK, 8, SW, XQ>(a, so, ai, U, g.US, buf_bytes, st);
 }
 
-// Split-K of the LDS-streaming kernel: waves per row.
-static int lds_wk(int U) { return U > 128 ? 4 : (U > 64 ? 2 : 1); }
+// Split-K of the LDS-streaming kernel: waves per row, by the row's length in
+// 64-weight units of 36 bytes (a Q8_0 unit, 68 bytes, counts twice: 14336 x
+// 4096 ran 12.6 against 13.1 us with two waves per row).
+template <int FMT>
+static int wk_units(int U) { return FMT == QGEMV_FMT_Q8_0 ? 2 * U : U; }
+template <int FMT>
+static int lds_wk(int U) {
+    const int Uw = wk_units<FMT>(U);
+    return Uw > 128 ? 4 : (Uw > 64 ? 2 : 1);
+}
 
 // Compute units of the current device (cached per device).
 static int cu_count() {
@@ -1409,17 +1417,19 @@ static hipError_t launch_lds_fmt(const GemvArgs& a, int U, const SliceGeom& g, h
                                  const SwigluOut& so, const ActIn& ai) {
     // the fused gate|up product always tries the dynamic-row kernel (whole
     // output blocks per unit, shared by its 8 waves)
+    // (the split-K matches lds_wk: g was formed with it)
+    const int Uw = wk_units<FMT>(U);
     if (SW || a.N >= (int64_t)kDynRowsPerCu * cu_count()) {
         hipError_t e = hipErrorNotSupported;
         if (U > 256) e = launch_dyn_wk<FMT, 2, 4, XQ, SW>(a, U, g, st, so, ai);
-        else if (U > 128) e = launch_dyn_wk<FMT, 1, 4, XQ, SW>(a, U, g, st, so, ai);
-        else if (U > 64) e = launch_dyn_wk<FMT, 1, 2, XQ, SW>(a, U, g, st, so, ai);
+        else if (Uw > 128) e = launch_dyn_wk<FMT, 1, 4, XQ, SW>(a, U, g, st, so, ai);
+        else if (Uw > 64) e = launch_dyn_wk<FMT, 1, 2, XQ, SW>(a, U, g, st, so, ai);
         else e = launch_dyn_wk<FMT, 1, 1, XQ, SW>(a, U, g, st, so, ai);
         if (e != hipErrorNotSupported) return e;
     }
     if (U > 256) return launch_lds_wk<FMT, 2, 4, SW, XQ>(a, U, g, st, so, ai);
-    if (U > 128) return launch_lds_wk<FMT, 1, 4, SW, XQ>(a, U, g, st, so, ai);
-    if (U > 64) return launch_lds_wk<FMT, 1, 2, SW, XQ>(a, U, g, st, so, ai);
+    if (Uw > 128) return launch_lds_wk<FMT, 1, 4, SW, XQ>(a, U, g, st, so, ai);
+    if (Uw > 64) return launch_lds_wk<FMT, 1, 2, SW, XQ>(a, U, g, st, so, ai);
     return launch_lds_wk<FMT, 1, 1, SW, XQ>(a, U, g, st, so, ai);
 }
 
@@ -1439,7 +1449,7 @@ static hipError_t launch_gemv_fmt(const GemvArgs& a, hipStream_t st) {
         a.N < (int64_t)kDynRowsPerCu * cu_count())
         return launch_gemv_cfg<FMT, 64, 1, 4>(a, U, st);
     if (kLdsStream && U > 32) {
-        const SliceGeom g = slice_geom<FMT>(a.K, U, lds_wk(U));
+        const SliceGeom g = slice_geom<FMT>(a.K, U, lds_wk<FMT>(U));
         if (lds_slice_fits<FMT>(g)) return launch_lds_fmt<FMT, false, false>(a, U, g, st, {}, {});
     }
     if (U > 256) return launch_gemv_cfg<FMT, 64, 2, 4>(a, U, st);
@@ -1460,7 +1470,7 @@ static hipError_t launch_quantize_gemv_fmt(const GemvArgs& a, const ActIn& ai, h
     const int U = units_of(FMT, a.K);
     const int Kp = (int)((a.K + 255) / 256 * 256);
     if (kLdsStream && U > 32) {
-        const SliceGeom g = slice_geom<FMT>(a.K, U, lds_wk(U));
+        const SliceGeom g = slice_geom<FMT>(a.K, U, lds_wk<FMT>(U));
         if (lds_slice_fits<FMT>(g, act_lds_bytes(Kp)))
             return launch_lds_fmt<FMT, false, true>(a, U, g, st, {}, ai);
     } else if (U <= 32 && Kp <= kXqShortKp) {

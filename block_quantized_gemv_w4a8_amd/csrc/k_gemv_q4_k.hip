@@ -10,7 +10,7 @@ QGEMV_GEMV_FORMAT_ENTRIES(q4_k, QGEMV_FMT_Q4_K)
 hipError_t launch_q4k_swiglu(const GemvArgs& a, const SwigluOut& so, hipStream_t st) {
     constexpr int FMT = QGEMV_FMT_Q4_K;
     const int U = units_of(FMT, a.K);
-    const SliceGeom g = slice_geom<FMT>(a.K, U, lds_wk(U));
+    const SliceGeom g = slice_geom<FMT>(a.K, U, lds_wk<FMT>(U));
     if (!lds_slice_fits<FMT>(g)) return hipErrorInvalidValue;
     return launch_lds_fmt<FMT, true, false>(a, U, g, st, so, {});
 }
@@ -20,7 +20,7 @@ hipError_t launch_quantize_q4k_swiglu(const GemvArgs& a, const SwigluOut& so, co
     constexpr int FMT = QGEMV_FMT_Q4_K;
     const int U = units_of(FMT, a.K);
     const int Kp = (int)((a.K + 255) / 256 * 256);
-    const SliceGeom g = slice_geom<FMT>(a.K, U, lds_wk(U));
+    const SliceGeom g = slice_geom<FMT>(a.K, U, lds_wk<FMT>(U));
     if (!lds_slice_fits<FMT>(g, act_lds_bytes(Kp))) return hipErrorInvalidValue;
     return launch_lds_fmt<FMT, true, true>(a, U, g, st, so, ai);
 }
