@@ -283,11 +283,14 @@ __global__ __launch_bounds__(64 * RT * KS * KP * MS) void k_small_m_mfma(const u
 
     // 16-byte-aligned start of row r's span in step st, and the span's offset from it
     auto span_base = [&](const uint8_t* rowp, int st, int& delta) {
-        const uint8_t* a = rowp + (int64_t)GM::SPAN * st;
+        const uint8_t* a = rowp + __umul24((unsigned)GM::SPAN, (unsigned)st);
         delta = (int)((uintptr_t)a & 15);
         return a - delta;
     };
 
+    // (Offsets within a row or an activation buffer stay below 2^24 -- K is at
+    // most 32768 and M at most 64 -- so they use the full-rate 24-bit
+    // multiply.)
     // One step's global data in registers between load and LDS store.  Every
     // load is issued unconditionally with its address clamped into the
     // buffers (rows past N re-read row N-1, units past K re-read the last
@@ -300,13 +303,13 @@ __global__ __launch_bounds__(64 * RT * KS * KP * MS) void k_small_m_mfma(const u
         uint32_t dh[SPT];
         int32_t sv[SPT];
     };
-    auto chunk_ptr = [&](int st, int c, int& lds_off) {
+    // rowp: the start of the chunk's row (row c / NCH of the workgroup)
+    auto chunk_ptr = [&](int st, int c, int& lds_off, const uint8_t* rowp) {
         const int row = c / NCH, k = c - row * NCH;
-        const uint8_t* rowp = w + (int64_t)min(row0 + row, N - 1) * row_bytes;
         if (U::ALIGNED) {
             const int unit = min(G * st + k / 9, nunits - 1);
             lds_off = row * GM::WSTRIDE + 16 * k;
-            return rowp + U::UB * unit + 16 * (k % 9);
+            return rowp + __umul24((unsigned)U::UB, (unsigned)unit) + 16 * (k % 9);
         }
         int delta;
         const uint8_t* a0 = span_base(rowp, st, delta);
@@ -316,11 +319,16 @@ __global__ __launch_bounds__(64 * RT * KS * KP * MS) void k_small_m_mfma(const u
         lds_off = row * GM::WSTRIDE + GM::FRONT + (int)(p - a0);
         return p;
     };
+    // the rows of this thread's weight chunk slots, the same in every step
+    const uint8_t* wrow[WPT];
+#pragma unroll
+    for (int k = 0; k < WPT; k++)
+        wrow[k] = w + (int64_t)min(row0 + min(tid + NT * k, WCH - 1) / NCH, N - 1) * row_bytes;
     auto load_step = [&](int st, Regs& r) {
 #pragma unroll
         for (int k = 0; k < WPT; k++) {
             int lo;
-            r.wc[k] = ld16(chunk_ptr(st, min(tid + NT * k, WCH - 1), lo));
+            r.wc[k] = ld16(chunk_ptr(st, min(tid + NT * k, WCH - 1), lo, wrow[k]));
         }
 #pragma unroll
         for (int k = 0; k < APT; k++) {
@@ -328,7 +336,7 @@ __global__ __launch_bounds__(64 * RT * KS * KP * MS) void k_small_m_mfma(const u
             const int g = c / (MA * 16), rem = c - g * (MA * 16);
             const int m = min(rem >> 4, M - 1), cc = rem & 15;
             const int u = min(G * st + g, nunits - 1);
-            r.ac[k] = *reinterpret_cast<const u32x4*>(q + (int64_t)m * Kp + 256 * u + 16 * cc);
+            r.ac[k] = *reinterpret_cast<const u32x4*>(q + __umul24((unsigned)m, (unsigned)Kp) + 256 * u + 16 * cc);
         }
 #pragma unroll
         for (int k = 0; k < SPT; k++) {
@@ -336,7 +344,7 @@ __global__ __launch_bounds__(64 * RT * KS * KP * MS) void k_small_m_mfma(const u
             const int g = c / (8 * MA), rem = c - g * (8 * MA);
             const int j = rem / MA, m = min(rem - j * MA, M - 1);
             const int u = min(G * st + g, nunits - 1);
-            const int64_t b = (int64_t)m * nb + 8 * u + j;
+            const int64_t b = __umul24((unsigned)m, (unsigned)nb) + 8 * u + j;
             r.dh[k] = d[b];
             r.sv[k] = s[b];
         }
@@ -348,7 +356,7 @@ __global__ __launch_bounds__(64 * RT * KS * KP * MS) void k_small_m_mfma(const u
             const int c = tid + NT * k;
             if (c < WCH) {
                 int lo;
-                (void)chunk_ptr(st, c, lo);
+                (void)chunk_ptr(st, c, lo, wrow[k]);
                 *reinterpret_cast<u32x4*>(base + lo) = r.wc[k];
             }
         }
