@@ -250,7 +250,11 @@ __global__ __launch_bounds__(64 * RT * KS * KP * MS) void k_small_m_mfma(const u
     constexpr int NPART = KS * KP;                           // partial sums per tile
     constexpr int PART_BYTES = (NPART - 1) * RT * MT * 4 * 64 * 4;
     constexpr int SMEM = 2 * GM::BUF > PART_BYTES ? 2 * GM::BUF : PART_BYTES;
-    __shared__ __align__(16) uint8_t smem[SMEM];
+    // two-block tiles: 256 bytes of zeros after everything else, which the
+    // lanes whose A-operand quarter belongs to the other block (or, Q6_K, to
+    // the other MFMA's 16-group) read instead of masking their codes
+    constexpr int ZOFF = SMEM, ZBYTES = TWO ? 256 : 0;
+    __shared__ __align__(16) uint8_t smem[SMEM + ZBYTES];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -273,6 +277,10 @@ __global__ __launch_bounds__(64 * RT * KS * KP * MS) void k_small_m_mfma(const u
             dots += (int64_t)m0 * N *
                     (FMT == QGEMV_FMT_Q6_K ? 2 * nbk : (FMT == QGEMV_FMT_Q4_0 ? K / 32 : nbk));
         M = min(M - m0, MP);
+    }
+    if constexpr (TWO) {
+        // (written before the pipeline's first barrier, read after it)
+        if (tid < ZBYTES / 16) *reinterpret_cast<u32x4*>(smem + ZOFF + 16 * tid) = u32x4{0, 0, 0, 0};
     }
     const int n = row0 + 16 * rt + nl;
     const int nunits = Kp / 256, nb = Kp / 32;
@@ -588,21 +596,26 @@ __global__ __launch_bounds__(64 * RT * KS * KP * MS) void k_small_m_mfma(const u
                           (int)(((ql.z >> s1) & LO4) | (((qh.z >> s2) & 0x03030303u) << 4)),
                           (int)(((ql.w >> s1) & LO4) | (((qh.w >> s2) & 0x03030303u) << 4))};
             }
-            const u32x4 a = *reinterpret_cast<const u32x4*>(
-                smem + oa + (nl & 7) * GM::ASTRIDE + 32 * jb + 16 * (kp & 1));
+            // A operand: lane (nl, kp) carries activation row nl & 7 of block
+            // jb where tile row nl belongs to that block (mine), else zeros,
+            // read from the zero block (same offsets within it)
+            const int off = 32 * jb + 16 * (kp & 1);
             const bool mine = (nl < 8) == (kp < 2);
-            const i32x4 A = {mine ? (int)a.x : 0, mine ? (int)a.y : 0, mine ? (int)a.z : 0,
-                             mine ? (int)a.w : 0};
+            auto a_load = [&](bool real) {
+                const u32x4 a = *reinterpret_cast<const u32x4*>(
+                    smem + (real ? oa + (nl & 7) * GM::ASTRIDE : ZOFF) + off);
+                return i32x4{(int)a.x, (int)a.y, (int)a.z, (int)a.w};
+            };
             if constexpr (ND == 1) {
-                E[0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, B, zero, 0, 0, 0);
+                E[0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a_load(mine), B, zero, 0, 0, 0);
             } else {
                 // Q6_K: a lane's K values are one 16-group (2*jb + (kp & 1));
-                // the first MFMA keeps the first group of each block, the
-                // second the other
+                // the first MFMA takes the first group of each block (lanes
+                // with kp even supply codes, the others zeros), the second
+                // the other
                 const bool g1 = (kp & 1) != 0;
-                const i32x4 B0 = g1 ? zero : B, B1 = g1 ? B : zero;
-                E[0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, B0, zero, 0, 0, 0);
-                E[1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, B1, zero, 0, 0, 0);
+                E[0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a_load(mine && !g1), B, zero, 0, 0, 0);
+                E[1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a_load(mine && g1), B, zero, 0, 0, 0);
             }
             if constexpr (DOTS) {
                 const int blk = blk0 + jb;
