@@ -250,10 +250,14 @@ __global__ __launch_bounds__(64 * RT * KS * KP * MS) void k_small_m_mfma(const u
     constexpr int NPART = KS * KP;                           // partial sums per tile
     constexpr int PART_BYTES = (NPART - 1) * RT * MT * 4 * 64 * 4;
     constexpr int SMEM = 2 * GM::BUF > PART_BYTES ? 2 * GM::BUF : PART_BYTES;
-    // two-block tiles: 256 bytes of zeros after everything else, which the
-    // lanes whose A-operand quarter belongs to the other block (or, Q6_K, to
-    // the other MFMA's 16-group) read instead of masking their codes
-    constexpr int ZOFF = SMEM, ZBYTES = TWO ? 256 : 0;
+    // two-block tiles, and Q6_K with one activation tile and whole units per
+    // wave: 256 bytes of zeros after everything else, which the lanes whose
+    // A-operand quarter belongs to the other block or to the other MFMA's
+    // 16-group read instead of masking codes (Q6_K 12288 x 4096 at M = 16:
+    // 23.5 against 24.0 us; with halved units, 4096 x 14336, 23.8 against
+    // 23.3 us, so those keep the masks)
+    constexpr bool ZA = TWO || (FMT == QGEMV_FMT_Q6_K && TPW == 1 && KS == 1);
+    constexpr int ZOFF = SMEM, ZBYTES = ZA ? 256 : 0;
     __shared__ __align__(16) uint8_t smem[SMEM + ZBYTES];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -278,7 +282,7 @@ __global__ __launch_bounds__(64 * RT * KS * KP * MS) void k_small_m_mfma(const u
                     (FMT == QGEMV_FMT_Q6_K ? 2 * nbk : (FMT == QGEMV_FMT_Q4_0 ? K / 32 : nbk));
         M = min(M - m0, MP);
     }
-    if constexpr (TWO) {
+    if constexpr (ZA) {
         // (written before the pipeline's first barrier, read after it)
         if (tid < ZBYTES / 16) *reinterpret_cast<u32x4*>(smem + ZOFF + 16 * tid) = u32x4{0, 0, 0, 0};
     }
@@ -493,17 +497,29 @@ __global__ __launch_bounds__(64 * RT * KS * KP * MS) void k_small_m_mfma(const u
                 const uint32_t c0 = ((ql.x >> s1) & LO4) | (((qh.x >> s2) & 0x03030303u) << 4);
                 const uint32_t c1 = ((ql.y >> s1) & LO4) | (((qh.y >> s2) & 0x03030303u) << 4);
                 const long Bc = (long)(((uint64_t)c1 << 32) | c0);
-                // 16-group 2j is K lanes kp < 2, group 2j+1 kp >= 2
-                B[0] = kp < 2 ? Bc : 0;
-                B[1] = kp < 2 ? 0 : Bc;
+                // 16-group 2j is K lanes kp < 2, group 2j+1 kp >= 2 (with one
+                // activation tile the A operand is split instead, below)
+                B[0] = ZA || kp < 2 ? Bc : 0;
+                B[1] = ZA || kp >= 2 ? Bc : 0;
             }
+            if constexpr (FMT == QGEMV_FMT_Q6_K && ZA) {
+                // lanes kp < 2 supply their codes to the first MFMA and zeros
+                // (from the zero block) to the second, lanes kp >= 2 the
+                // other way round
+                const int oc = o2 + (16 * t0 + nl) * GM::ASTRIDE + 8 * kp;
+                const long A0 = *reinterpret_cast<const long*>(smem + (kp < 2 ? oc : ZOFF + 8 * kp));
+                const long A1 = *reinterpret_cast<const long*>(smem + (kp < 2 ? ZOFF + 8 * kp : oc));
+                D[0][0] = __builtin_amdgcn_mfma_i32_16x16x32_i8(A0, B[0], zero, 0, 0, 0);
+                D[1][0] = __builtin_amdgcn_mfma_i32_16x16x32_i8(A1, B[1], zero, 0, 0, 0);
+            } else {
 #pragma unroll
-            for (int t = 0; t < TPW; t++) {
-                const long A = *reinterpret_cast<const long*>(
-                    smem + o2 + (16 * (t0 + t) + nl) * GM::ASTRIDE + 8 * kp);
+                for (int t = 0; t < TPW; t++) {
+                    const long A = *reinterpret_cast<const long*>(
+                        smem + o2 + (16 * (t0 + t) + nl) * GM::ASTRIDE + 8 * kp);
 #pragma unroll
-                for (int e = 0; e < ND; e++)
-                    D[e][t] = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, B[e], zero, 0, 0, 0);
+                    for (int e = 0; e < ND; e++)
+                        D[e][t] = __builtin_amdgcn_mfma_i32_16x16x32_i8(A, B[e], zero, 0, 0, 0);
+                }
             }
             if constexpr (DOTS) {
                 // outputs of lane l: activation rows 16t + 4(l/16) + i of weight row n
