@@ -17,10 +17,11 @@
 // l / 16 of a block pair), D units ahead of the one it multiplies; no other
 // wave waits for them.  The activation (codes, and the fp16 scales and int32
 // sums as they are stored) is shared: it moves through LDS in chunks of KC
-// units with direct global->LDS loads, double-buffered, with one workgroup
-// barrier per chunk.  The thread that brought a row's scales in converts them
-// to fp32 (dx, and dx * s where the format has a min or offset term) in a
-// [block][row] layout, after waiting for its own loads only.
+// units, double-buffered, with one workgroup barrier per chunk.  Every thread
+// loads its share of the next chunk into registers while the current one is
+// computed and writes it to the other buffer before the barrier; the thread
+// that brought a row's scales in writes them as fp32 (dx, and dx * s where
+// the format has a min or offset term) in a [block][row] layout.
 //
 // Per 64-wide block pair a lane holds 16 weight codes; per activation tile of
 // 16 rows, one 16-byte LDS read gives the A operand:
@@ -51,22 +52,6 @@ namespace sm2 {
 
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) void glb_void;
-
-
-// One 16-byte chunk per lane from global memory straight into LDS: lane i's
-// chunk lands at dst + 16 * i (dst is the same for the whole wave).
-__device__ __forceinline__ void dma16(const void* src, void* dst_wave) {
-    __builtin_amdgcn_global_load_lds((glb_void*)src, (lds_void*)dst_wave, 16, 0, 0);
-}
-
-// s_waitcnt vmcnt(n) (n < 64), leaving the other counters alone.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
 
 // Keeps the compiler from moving code, memory accesses included, across this
 // point: the issue order of the loads is what the s_waitcnt counts assume,
