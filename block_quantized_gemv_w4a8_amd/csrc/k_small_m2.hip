@@ -212,9 +212,10 @@ __global__ __launch_bounds__(64 * NW) void k_small_m2(const uint8_t* __restrict_
     constexpr int SPC = KC / KSB;             // units per wave and chunk
     constexpr int NPART = KSB * KS;
     constexpr int NKK = BPW >= 2 ? BPW / 2 : 1;   // fp32-MFMA groups of 4 blocks per wave
-    // Q6_K tiles software-pipelined (below) where the registers allow: the
-    // second set of MFMA results spills at 16 waves and three tiles
-    constexpr bool PIPE = FMT == QGEMV_FMT_Q6_K && !TWO && NW * MT <= 32;
+    // Q6_K steps software-pipelined (below) where the registers allow: the
+    // second set of MFMA results and both pairs' B operands spill at 16
+    // waves (128 VGPRs)
+    constexpr bool PIPE = FMT == QGEMV_FMT_Q6_K && !TWO && NW <= 8;
     // chunks per unrolled step: even (buffer parity) and a multiple of the
     // ring period
     constexpr int CU = (SPC % D == 0) ? 2 : ((2 * SPC) % D == 0 ? 2 : 2 * D);
@@ -377,8 +378,82 @@ __global__ __launch_bounds__(64 * NW) void k_small_m2(const uint8_t* __restrict_
 #pragma unroll
             for (int t = 0; t < MT; t++) accs[t] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
+        if constexpr (PIPE) {
+            // The (block pair, activation tile) steps of the unit run as one
+            // software pipeline: step k's MFMAs and the LDS reads of its
+            // scales and of step k+1's codes issue before step k-1's
+            // epilogue, one MFMA between every few of its VALU instructions,
+            // so neither the LDS nor the MFMA latency is waited out (the
+            // register fence closing each epilogue would otherwise hold every
+            // later LDS read behind it).  Both pairs' B operands are unpacked
+            // first, so the pipeline runs through the pair boundary.  On 4096
+            // x 14336: 45.7 against 48.3 us at M = 64, 40.6 against 42.7 us
+            // at M = 48, 36.0 against 37.5 us at M = 32 for a pipeline within
+            // each pair (same process), and 44.6, 40.0 and 35.6 us through
+            // the pair boundary; 12288 x 4096 at M = 64 41.5 against 46.1
+            // us, 128256 x 4096 at M = 64 324 against 355 us.
+            i32x4 Bq[BPW][4];
+            int scq[BPW][4];
 #pragma unroll
-        for (int pi = 0; pi < BPW; pi++) {
+            for (int pi = 0; pi < BPW; pi++) {
+                const int p = pw + pi;
+                const u32x4 c = q6_codes(wr.ql[pi / 2], wr.qh[pi / 2], p & 1, 4 * (p & 1) + hsh6);
+#pragma unroll
+                for (int g = 0; g < 4; g++) {
+                    Bq[pi][g] = and4(c, kq == g ? 0xFFFFFFFFu : 0u);
+                    scq[pi][g] = sbyte(wr.sc[pi], g);
+                }
+            }
+            constexpr int NK = BPW * MT;
+            auto ld_a = [&](int k) {
+                const int pi = k / MT, t = k % MT;
+                const u32x4 av = *reinterpret_cast<const u32x4*>(codes + 16 * t * C::CSTR + 64 * pi);
+                return i32x4{(int)av.x, (int)av.y, (int)av.z, (int)av.w};
+            };
+            auto ld_x = [&](int k, int h) {
+                const int pi = k / MT, t = k % MT;
+                return *reinterpret_cast<const f32x4*>(dxT + 4 * ((2 * pi + h) * MP + 16 * t));
+            };
+            auto epi = [&](int k, const i32x4 (&Dv)[4], const f32x4& x0, const f32x4& x1) {
+                const int pi = k / MT, t = k % MT;
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const int v0 = __mul24(Dv[0][e], scq[pi][0]) + __mul24(Dv[1][e], scq[pi][1]);
+                    const int v1 = __mul24(Dv[2][e], scq[pi][2]) + __mul24(Dv[3][e], scq[pi][3]);
+                    const float a = fmaf((float)v0, x0[e], accs[t][e]);
+                    accs[t][e] = fmaf((float)v1, x1[e], a);
+                }
+                asm volatile("" : "+v"(accs[t]));
+            };
+            i32x4 A = ld_a(0);
+            i32x4 Dp[4];
+            f32x4 xp0, xp1;
+#pragma unroll
+            for (int k = 0; k < NK; k++) {
+                i32x4 Dc[4];
+#pragma unroll
+                for (int g = 0; g < 4; g++) Dc[g] = mfma64(A, Bq[k / MT][g]);
+                const f32x4 xc0 = ld_x(k, 0), xc1 = ld_x(k, 1);
+                if (k + 1 < NK) A = ld_a(k + 1);
+                if (k > 0) epi(k - 1, Dp, xp0, xp1);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+#pragma unroll
+                for (int g = 1; g < 4; g++) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int g = 0; g < 4; g++) Dp[g] = Dc[g];
+                xp0 = xc0;
+                xp1 = xc1;
+            }
+            epi(NK - 1, Dp, xp0, xp1);
+        }
+#pragma unroll
+        for (int pi = 0; pi < (PIPE ? 0 : BPW); pi++) {
             // block pairs one after another: interleaving them only raises
             // the register count (the waves of a SIMD hide the latencies)
             if (pi > 0) __builtin_amdgcn_sched_barrier(0);
@@ -442,63 +517,6 @@ __global__ __launch_bounds__(64 * NW) void k_small_m2(const uint8_t* __restrict_
 #pragma unroll
                     for (int g = 0; g < 4; g++) sc6[g] = sbyte(sw, g);
                 }
-            }
-            if constexpr (PIPE) {
-                // Activation tiles in a software pipeline: tile t's MFMAs and
-                // the LDS reads of its scales and of tile t+1's codes issue
-                // before tile t-1's epilogue, one MFMA between every few of
-                // its VALU instructions, so neither the LDS nor the MFMA
-                // latency is waited out (the register fence closing each
-                // epilogue would otherwise hold every later LDS read behind
-                // it).  On 4096 x 14336 (same process): 45.7 against 48.3 us
-                // at M = 64, 40.6 against 42.7 us at M = 48, 36.0 against
-                // 37.5 us at M = 32; 12288 x 4096 at M = 64 43.1 against 46.1
-                // us, 128256 x 4096 at M = 64 331 against 355 us.
-                auto ld_a = [&](int t) {
-                    const u32x4 av =
-                        *reinterpret_cast<const u32x4*>(codes + 16 * t * C::CSTR + 64 * pi);
-                    return i32x4{(int)av.x, (int)av.y, (int)av.z, (int)av.w};
-                };
-                auto ld_x = [&](int t, int h) {
-                    return *reinterpret_cast<const f32x4*>(dxT + 4 * ((2 * pi + h) * MP + 16 * t));
-                };
-                auto epi = [&](int t, const i32x4 (&Dv)[4], const f32x4& x0, const f32x4& x1) {
-#pragma unroll
-                    for (int e = 0; e < 4; e++) {
-                        const int v0 = __mul24(Dv[0][e], sc6[0]) + __mul24(Dv[1][e], sc6[1]);
-                        const int v1 = __mul24(Dv[2][e], sc6[2]) + __mul24(Dv[3][e], sc6[3]);
-                        const float a = fmaf((float)v0, x0[e], accs[t][e]);
-                        accs[t][e] = fmaf((float)v1, x1[e], a);
-                    }
-                    asm volatile("" : "+v"(accs[t]));
-                };
-                i32x4 A = ld_a(0);
-                i32x4 Dp[4];
-                f32x4 xp0, xp1;
-#pragma unroll
-                for (int t = 0; t < MT; t++) {
-                    i32x4 Dc[4];
-#pragma unroll
-                    for (int g = 0; g < 4; g++) Dc[g] = mfma64(A, Bop[g]);
-                    const f32x4 xc0 = ld_x(t, 0), xc1 = ld_x(t, 1);
-                    if (t + 1 < MT) A = ld_a(t + 1);
-                    if (t > 0) epi(t - 1, Dp, xp0, xp1);
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
-#pragma unroll
-                    for (int g = 1; g < 4; g++) {
-                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                    for (int g = 0; g < 4; g++) Dp[g] = Dc[g];
-                    xp0 = xc0;
-                    xp1 = xc1;
-                }
-                epi(MT - 1, Dp, xp0, xp1);
-                continue;
             }
 #pragma unroll
             for (int t = 0; t < MT; t++) {
