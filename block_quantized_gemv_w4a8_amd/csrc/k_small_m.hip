@@ -459,11 +459,13 @@ __global__ __launch_bounds__(64 * RT * KS * KP * MS) void k_small_m_mfma(const u
             mlo = hdr.z & 0x3F3F3F3Fu;
             mhi = ((hdr.w >> 4) & LO4) | ((hdr.z >> 2) & 0x30303030u);
         } else if constexpr (FMT == QGEMV_FMT_Q6_K) {
-            fd = valid ? h2f(lds2(smem, ow + 208)) : 0.0f;
+            // (the scale's bits masked rather than the read skipped: a
+            // branch around an LDS read waits for it on the spot)
+            fd = h2f(lds2(smem, ow + 208) & (valid ? 0xFFFFu : 0u));
         }
         // Q4_0: the scale of block j of the unit (zero past the row's blocks)
         auto q40_scale = [&](int j) {
-            return blk0 + j < nbw ? h2f(lds2(smem, ow + 18 * j)) : 0.0f;
+            return h2f(lds2(smem, ow + 18 * j) & (blk0 + j < nbw ? 0xFFFFu : 0u));
         };
 
         auto mfma_block = [&](int jj, i32x4 (&D)[ND][TPW]) {
