@@ -61,6 +61,19 @@ __device__ __forceinline__ void fence_code() {
     __builtin_amdgcn_sched_barrier(0);
 }
 
+// The same for loads through the given restrict-qualified pointers, which a
+// plain memory clobber does not hold: the compiler sank the activation-scale
+// load, used only by the threads that write the scales, past it into that
+// store at the end of the chunk, where its whole latency was then waited
+// out.  Naming the pointers in the asm keeps every load of the chunk at its
+// start (4096 x 14336, same process: 40.8 against 44.7 us at M = 64, 34.0
+// against 40.2 us at M = 48, 29.9 against 35.8 us at M = 32; 12288 x 4096 at
+// M = 64 37.5 against 41.7 us).
+__device__ __forceinline__ void fence_loads(const void* a, const void* b, const void* c) {
+    asm volatile("" ::"s"(a), "s"(b), "s"(c) : "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 __device__ __forceinline__ i32x4 mfma64(const i32x4& a, const i32x4& b) {
     return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, i32x4{0, 0, 0, 0}, 0, 0, 0);
 }
@@ -645,7 +658,7 @@ __global__ __launch_bounds__(64 * NW) void k_small_m2(const uint8_t* __restrict_
             uint8_t* nxt = (cc & 1) ? buf0 : buf1;
             ActRegs an;
             load_act(min(c + 1, nchunks - 1), an);
-            fence_code();
+            fence_loads(q, dact, sact);
 #pragma unroll
             for (int i = 0; i < SPC; i++) {
                 const int s = c * SPC + i;
@@ -721,17 +734,20 @@ static hipError_t launch_fmt(const void* w, int64_t N, int64_t K, int64_t M, con
     // <FMT, MT, TWO, NTW, KSB, KS, KC, D>
     if (wide) {
         if (M <= 8) return launch_cfg<FMT, 1, true, 4, 2, 1, 8, 4>(w, N, K, M, q, d, s, y, st);
-        // Q6_K at M = 17-48: 2 tiles per workgroup of 16 waves, each tile's
-        // units split 4 ways and block pairs 2 ways, one unit in flight per
-        // wave (12288 x 4096: M = 48 36.2 against 44.4 us, M = 24 32.2
-        // against 35.0 us for the staged kernel; 128256 x 4096 at M = 48 277
-        // against 341 us)
-        // and at M = 49-64 four tiles per 8-wave workgroup with one unit in
-        // flight per wave (46.2 against 48.9 us for two on 12288 x 4096, 355
-        // against 375 us on 128256 x 4096)
+        // Q6_K at M = 17-64: four tiles per 8-wave workgroup, each tile's
+        // units split 2 ways, whole units per wave, one unit in flight per
+        // wave, 4 units per activation chunk up to M = 48 and 2 at M = 49-64
+        // (4 spill there).  Against the earlier two tiles per 16-wave
+        // workgroup with units split 4 ways and block pairs 2 ways (same
+        // process): 12288 x 4096 at M = 24 27.1 against 32.9 us, at M = 32
+        // 27.4 against 33.2 us, at M = 48 32.2 against 37.8 us; 128256 x 4096
+        // at M = 32 206 against 255 us, at M = 48 238 against 289 us.  At M =
+        // 49-64: 46.2 against 48.9 us for two units in flight on 12288 x
+        // 4096, 355 against 375 us on 128256 x 4096 (before the pipelined
+        // steps)
         if constexpr (FMT == QGEMV_FMT_Q6_K) {
-            if (mt == 2) return launch_cfg<FMT, 2, false, 2, 4, 2, 4, 1, 16>(w, N, K, M, q, d, s, y, st);
-            if (mt == 3) return launch_cfg<FMT, 3, false, 2, 4, 2, 4, 1, 16>(w, N, K, M, q, d, s, y, st);
+            if (mt == 2) return launch_cfg<FMT, 2, false, 4, 2, 1, 4, 1>(w, N, K, M, q, d, s, y, st);
+            if (mt == 3) return launch_cfg<FMT, 3, false, 4, 2, 1, 4, 1>(w, N, K, M, q, d, s, y, st);
             if (mt >= 4) return launch_cfg<FMT, 4, false, 4, 2, 1, 2, 1>(w, N, K, M, q, d, s, y, st);
         }
         switch (mt) {
