@@ -449,6 +449,9 @@ __global__ __launch_bounds__(64 * NW) void k_small_m2(const uint8_t* __restrict_
                 const f32x4 xc0 = ld_x(k, 0), xc1 = ld_x(k, 1);
                 if (k + 1 < NK) A = ld_a(k + 1);
                 if (k > 0) epi(k - 1, Dp, xp0, xp1);
+                // issue order (scheduler group masks: 0x008 MFMA, 0x100 LDS
+                // read, 0x002 VALU): MFMA, the three LDS reads, six VALU,
+                // then each further MFMA followed by six VALU
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
                 __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
