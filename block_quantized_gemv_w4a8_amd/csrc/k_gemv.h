@@ -420,10 +420,16 @@ __global__ __launch_bounds__(WG) void k_gemv(const uint8_t* __restrict__ w, int 
 
     const int64_t npass_all = ngroups > (int64_t)blockIdx.x
                                   ? (ngroups - blockIdx.x + G - 1) / G : 0;
+    // The first row's loads go out before anything waits for the
+    // activation's, so the weight stream starts one load latency sooner; a
+    // segment's last pass loads the next segment's first row into wa (SEGP
+    // is even).
+    static_assert(SEGP % 2 == 0, "segments of whole row pairs");
+    WT wa[UPL], wb[UPL];
+    load_row(wa, row_of(0));
+    __builtin_amdgcn_sched_barrier(0);
     for (int64_t p0 = 0; p0 < npass_all; p0 += SEGP) {
         const int np = (int)min((int64_t)SEGP, npass_all - p0);
-        WT wa[UPL], wb[UPL];
-        load_row(wa, row_of(p0));
         if constexpr (XQ) {
             if (p0 == 0) {
                 // the first row's weights are on their way; quantise x
